@@ -1,0 +1,211 @@
+"""CPU oracle of the draft-tree verification step -- TEST INFRASTRUCTURE ONLY.
+
+Plain C loops in double precision (``ev_oracle.c``), built with gcc and called through
+ctypes.  Only the tests, the smoke check and the CPU-baseline leg of the benchmark may
+import this package; the GPU library and its Python binding never do, and the two share
+no code.  All arguments are host numpy arrays; bf16 data is passed as raw uint16 bits and
+widened exactly inside the C code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ev_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "libev_oracle.so")
+_lib = None
+
+BF16 = 0
+F32 = 1
+MAX_NODES = 1024
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle with gcc (OpenMP across independent rows/sequences)."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-std=c11", "-Wall",
+           "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load(path: str = None):
+    """Load the oracle library, building it first if it is missing or older than its source."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_D = ctypes.c_double
+
+
+def _bind(lib):
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_tree_errors.restype = _I32
+    lib.oracle_tree_errors.argtypes = [_P, _I32, _I32]
+    lib.oracle_ancestor_path.restype = _I32
+    lib.oracle_ancestor_path.argtypes = [_P, _I32, _P]
+    lib.oracle_tree_attention.restype = None
+    lib.oracle_tree_attention.argtypes = [_P, _P, _P, _I32, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32,
+                                          _I32, _D, _P, _P, _P]
+    lib.oracle_tree_attention_rows.restype = None
+    lib.oracle_tree_attention_rows.argtypes = [_P, _P, _P, _I32, _P, _P, _P, _P, _I32, _I32, _I64, _I32,
+                                               _I32, _I32, _D, _P, _I64, _P, _P]
+    lib.oracle_node_argmax.restype = None
+    lib.oracle_node_argmax.argtypes = [_P, _I32, _I64, _I32, _I32, _P, _P]
+    lib.oracle_greedy_accept.restype = None
+    lib.oracle_greedy_accept.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]
+    lib.oracle_compact_kv.restype = None
+    lib.oracle_compact_kv.argtypes = [_P, _P, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _I32, _I64,
+                                      _I32, _I32, _P, _P]
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arguments must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _dtype_of(x: np.ndarray) -> int:
+    if x.dtype == np.uint16:
+        return BF16
+    if x.dtype == np.float32:
+        return F32
+    raise TypeError(f"oracle expects bf16 bits (uint16) or float32, got {x.dtype}")
+
+
+def num_threads(lib=None) -> int:
+    return int((lib or load()).oracle_num_threads())
+
+
+def tree_errors(parent, max_nodes: int, lib=None) -> int:
+    parent = _i32(parent)
+    return int((lib or load()).oracle_tree_errors(_ptr(parent), len(parent), max_nodes))
+
+
+def ancestor_path(parent, i: int, lib=None) -> np.ndarray:
+    parent = _i32(parent)
+    out = np.zeros(max(len(parent), 1), dtype=np.int32)
+    n = (lib or load()).oracle_ancestor_path(_ptr(parent), int(i), _ptr(out))
+    return out[:n].copy()
+
+
+def tree_attention(q, k, v, node_start, parent, kv_start, prefix_len, *, num_q_heads: int,
+                   num_kv_heads: int, head_dim: int, sm_scale: float, total_slots: int,
+                   max_nodes: int = None, lib=None):
+    """Every row.  Returns (out [T, Hq, D] float64, lse [T, Hq] float64, seq_err [B] int32).
+    Rows of sequences with data errors hold NaN."""
+    lib = lib or load()
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    dt = _dtype_of(q)
+    assert _dtype_of(k) == dt and _dtype_of(v) == dt
+    node_start, parent, kv_start, prefix_len = map(_i32, (node_start, parent, kv_start, prefix_len))
+    B = len(prefix_len)
+    T = int(node_start[-1]) if len(node_start) else 0
+    if max_nodes is None:
+        max_nodes = int(np.diff(node_start).max()) if B else 1
+    assert max_nodes <= MAX_NODES
+    out = np.full((T, num_q_heads, head_dim), np.nan)
+    lse = np.full((T, num_q_heads), np.nan)
+    err = np.zeros(max(B, 1), dtype=np.int32)
+    lib.oracle_tree_attention(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(node_start), _ptr(parent), _ptr(kv_start),
+                              _ptr(prefix_len), B, max_nodes, int(total_slots), num_q_heads, num_kv_heads,
+                              head_dim, float(sm_scale), _ptr(out), _ptr(lse), _ptr(err))
+    return out, lse, err[:B]
+
+
+def tree_attention_rows(q, k, v, node_start, parent, kv_start, prefix_len, rows, *, num_q_heads: int,
+                        num_kv_heads: int, head_dim: int, sm_scale: float, total_slots: int,
+                        max_nodes: int = None, lib=None):
+    """Selected rows only: ``rows`` is an int array [R, 2] of (global node, q head).
+    Returns (out [R, D] float64, lse [R] float64)."""
+    lib = lib or load()
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    dt = _dtype_of(q)
+    node_start, parent, kv_start, prefix_len = map(_i32, (node_start, parent, kv_start, prefix_len))
+    rows = _i32(rows).reshape(-1, 2)
+    B = len(prefix_len)
+    if max_nodes is None:
+        max_nodes = int(np.diff(node_start).max()) if B else 1
+    R = rows.shape[0]
+    out = np.full((R, head_dim), np.nan)
+    lse = np.full(R, np.nan)
+    lib.oracle_tree_attention_rows(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(node_start), _ptr(parent),
+                                   _ptr(kv_start), _ptr(prefix_len), B, max_nodes, int(total_slots),
+                                   num_q_heads, num_kv_heads, head_dim, float(sm_scale), _ptr(rows), R,
+                                   _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def node_argmax(logits, vocab: int = None, row_stride: int = None, lib=None):
+    """Returns (target [R] int32, max_value [R] float64)."""
+    lib = lib or load()
+    logits = np.ascontiguousarray(logits)
+    dt = _dtype_of(logits)
+    R = logits.shape[0]
+    if vocab is None:
+        vocab = logits.shape[1]
+    if row_stride is None:
+        row_stride = logits.shape[1]
+    tgt = np.zeros(max(R, 1), dtype=np.int32)
+    mx = np.zeros(max(R, 1))
+    lib.oracle_node_argmax(_ptr(logits), dt, int(row_stride), R, int(vocab), _ptr(tgt), _ptr(mx))
+    return tgt[:R], mx[:R]
+
+
+def greedy_accept(node_start, parent, draft, target, max_nodes: int, vocab: int, lib=None):
+    """Returns dict of accept_len [B], accept_path [B, max_nodes], bonus [B], out_tokens [B, max_nodes],
+    seq_err [B]."""
+    lib = lib or load()
+    node_start, parent, draft, target = map(_i32, (node_start, parent, draft, target))
+    B = len(node_start) - 1
+    assert max_nodes <= MAX_NODES
+    acc = np.zeros(max(B, 1), np.int32)
+    path = np.zeros((max(B, 1), max_nodes), np.int32)
+    bonus = np.zeros(max(B, 1), np.int32)
+    outt = np.zeros((max(B, 1), max_nodes), np.int32)
+    err = np.zeros(max(B, 1), np.int32)
+    lib.oracle_greedy_accept(_ptr(node_start), _ptr(parent), _ptr(draft), _ptr(target), B, max_nodes,
+                             int(vocab), _ptr(acc), _ptr(path), _ptr(bonus), _ptr(outt), _ptr(err))
+    return {"accept_len": acc[:B], "accept_path": path[:B], "bonus": bonus[:B], "out_tokens": outt[:B],
+            "seq_err": err[:B]}
+
+
+def compact_kv(k, v, kv_start, prefix_len, accept_len, accept_path, *, num_layers: int, total_slots: int,
+               num_kv_heads: int, head_dim: int, lib=None):
+    """Out-of-place compaction of caches shaped [layers, total_slots, Hkv, D] (any element type).
+    Returns (k_out, v_out, new_len [B], seq_err [B])."""
+    lib = lib or load()
+    k, v = np.ascontiguousarray(k), np.ascontiguousarray(v)
+    kv_start, prefix_len, accept_len = map(_i32, (kv_start, prefix_len, accept_len))
+    accept_path = _i32(accept_path)
+    B = len(prefix_len)
+    max_nodes = accept_path.shape[1] if accept_path.ndim == 2 else 1
+    elem = k.dtype.itemsize
+    layer_stride = total_slots * num_kv_heads * head_dim * elem
+    assert k.nbytes == num_layers * layer_stride and v.nbytes == k.nbytes
+    k_out, v_out = np.empty_like(k), np.empty_like(v)
+    new_len = np.zeros(max(B, 1), np.int32)
+    err = np.zeros(max(B, 1), np.int32)
+    lib.oracle_compact_kv(_ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out), elem, num_layers, layer_stride,
+                          _ptr(kv_start), _ptr(prefix_len), _ptr(accept_len), _ptr(accept_path), B, max_nodes,
+                          int(total_slots), num_kv_heads, head_dim, _ptr(new_len), _ptr(err))
+    return k_out, v_out, new_len[:B], err[:B]

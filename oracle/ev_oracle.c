@@ -1,0 +1,296 @@
+/*
+ * ev_oracle.c -- CPU oracle of the draft-tree verification step (TEST INFRASTRUCTURE).
+ *
+ * Plain, slow loops in double precision.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark load this file's library; the GPU library never
+ * links it and shares no code or header with it.
+ *
+ * What is computed follows the descriptions of speculative decoding on the pages
+ * (kongchang.com EN article, "Technical Background": the target model checks all drafted
+ * tokens in one parallel forward pass, keeps the prefix that agrees with it and adds one
+ * token of its own after the first rejected position; EAGLE-2's dynamic draft tree lets one
+ * verification cover several candidate paths), at temperature 0 (aiposthub.com analysis,
+ * "paper Table 2", greedy T=0 results), plus the four-step decomposition named for this
+ * verification step: tree-masked GQA attention, per-node argmax, greedy longest-path
+ * acceptance, KV compaction.  Readings where the pages are silent:
+ *   - node 0 is the root (the previous round's decided token), always accepted;
+ *   - nodes are in topological order: parent[0] == -1 and 0 <= parent[i] < i;
+ *   - a node sees the whole prefix plus its ancestors INCLUDING itself;
+ *   - q head h reads KV head h / (Hq / Hkv);
+ *   - argmax ties go to the lowest index, +0 == -0, NaN ranks above everything
+ *     (first NaN wins);
+ *   - the accepted node is the deepest accepted node, lowest index on equal depth.
+ *
+ * Parity pins: every function here is checked in tests against an independent formulation
+ * (brute force / library routines / closed forms / hand-built cases); none is unpinned.
+ *
+ * Data-error bits (per sequence) mirror the GPU library's: 1 bad parent array,
+ * 2 node count outside [1, max_nodes], 4 token outside [0, vocab), 8 slot range outside the
+ * cache, 16 malformed accepted path.  A sequence with an error is skipped.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_BF16 = 0, OR_F32 = 1 };
+
+/* Element `idx` of a bf16 (raw bits) or fp32 array, widened exactly to double. */
+static double elem(const void *base, int dtype, size_t idx) {
+    if (dtype == OR_BF16) {
+        uint32_t u = (uint32_t)((const uint16_t *)base)[idx] << 16;
+        float f;
+        memcpy(&f, &u, 4);
+        return (double)f;
+    }
+    return (double)((const float *)base)[idx];
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Tree rule: parent[0] == -1 and 0 <= parent[i] < i; 1 <= n <= max_nodes. */
+int32_t oracle_tree_errors(const int32_t *parent, int32_t n, int32_t max_nodes) {
+    int32_t err = 0;
+    if (n < 1 || n > max_nodes) return 2;
+    if (parent[0] != -1) err |= 1;
+    for (int32_t i = 1; i < n; ++i)
+        if (parent[i] < 0 || parent[i] >= i) err |= 1;
+    return err;
+}
+
+/* Ancestors of node i including i itself, written root first (increasing depth).
+   Returns how many there are, i.e. depth(i) + 1. */
+int32_t oracle_ancestor_path(const int32_t *parent, int32_t i, int32_t *path) {
+    int32_t rev[1024];
+    int32_t n = 0;
+    for (int32_t j = i; j >= 0; j = parent[j]) rev[n++] = j;
+    for (int32_t t = 0; t < n; ++t) path[t] = rev[n - 1 - t];
+    return n;
+}
+
+static int32_t seq_layout_errors(const int32_t *kv_start, const int32_t *prefix_len, int32_t b,
+                                 int32_t n, int64_t total_slots) {
+    if (kv_start[b] < 0 || prefix_len[b] < 0) return 8;
+    if ((int64_t)kv_start[b] + prefix_len[b] + n > total_slots) return 8;
+    return 0;
+}
+
+/* Per-sequence validity for attention: tree rule and slot range. */
+void oracle_attention_errors(const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                             const int32_t *prefix_len, int32_t batch, int32_t max_nodes,
+                             int64_t total_slots, int32_t *seq_err) {
+    for (int32_t b = 0; b < batch; ++b) {
+        int32_t n = node_start[b + 1] - node_start[b];
+        int32_t e = oracle_tree_errors(parent + node_start[b], n, max_nodes);
+        if (!(e & 2)) e |= seq_layout_errors(kv_start, prefix_len, b, n, total_slots);
+        seq_err[b] = e;
+    }
+}
+
+/* Attention of one (sequence b, local node i, q head h) row.
+   Visible keys: prefix slots s0 + t for 0 <= t < L, then tree slots s0 + L + j for every j in
+   anc(i).  scores = sm_scale * <q, k>;  out = sum_t e^{s_t - m} v_t / sum_t e^{s_t - m};
+   lse = m + ln sum_t e^{s_t - m}. */
+static void attention_row(const void *q, const void *k, const void *v, int dtype, const int32_t *node_start,
+                          const int32_t *parent, const int32_t *kv_start, const int32_t *prefix_len,
+                          int32_t b, int32_t i, int32_t h, int32_t hq, int32_t hkv, int32_t d,
+                          double sm_scale, double *out, double *lse, double *scratch, int64_t *slots) {
+    const int32_t G = hq / hkv;
+    const int32_t g = h / G;
+    const int32_t L = prefix_len[b];
+    const int64_t s0 = kv_start[b];
+    const int32_t *par = parent + node_start[b];
+    int32_t path[1024];
+    int32_t np = oracle_ancestor_path(par, i, path);
+    int64_t nvis = 0;
+    for (int32_t t = 0; t < L; ++t) slots[nvis++] = s0 + t;
+    for (int32_t t = 0; t < np; ++t) slots[nvis++] = s0 + L + path[t];
+
+    const size_t qrow = ((size_t)(node_start[b] + i) * hq + h) * d;
+    double m = -INFINITY;
+    for (int64_t t = 0; t < nvis; ++t) {
+        const size_t krow = ((size_t)slots[t] * hkv + g) * d;
+        double dot = 0.0;
+        for (int32_t c = 0; c < d; ++c) dot += elem(q, dtype, qrow + c) * elem(k, dtype, krow + c);
+        scratch[t] = sm_scale * dot;
+        if (scratch[t] > m) m = scratch[t];
+    }
+    double sum = 0.0;
+    for (int64_t t = 0; t < nvis; ++t) {
+        scratch[t] = exp(scratch[t] - m);
+        sum += scratch[t];
+    }
+    for (int32_t c = 0; c < d; ++c) out[c] = 0.0;
+    for (int64_t t = 0; t < nvis; ++t) {
+        const size_t vrow = ((size_t)slots[t] * hkv + g) * d;
+        for (int32_t c = 0; c < d; ++c) out[c] += scratch[t] * elem(v, dtype, vrow + c);
+    }
+    for (int32_t c = 0; c < d; ++c) out[c] /= sum;
+    *lse = m + log(sum);
+}
+
+/* A list of rows: rows[2r] = global node index, rows[2r+1] = q head.  out [nrows, d], lse [nrows].
+   Rows of sequences with data errors are left untouched. */
+void oracle_tree_attention_rows(const void *q, const void *k, const void *v, int32_t dtype,
+                                const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                                const int32_t *prefix_len, int32_t batch, int32_t max_nodes,
+                                int64_t total_slots, int32_t hq, int32_t hkv, int32_t d, double sm_scale,
+                                const int32_t *rows, int64_t nrows, double *out, double *lse) {
+    int32_t *seq_err = (int32_t *)calloc(batch > 0 ? batch : 1, sizeof(int32_t));
+    oracle_attention_errors(node_start, parent, kv_start, prefix_len, batch, max_nodes, total_slots, seq_err);
+    int32_t maxvis = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        int32_t n = node_start[b + 1] - node_start[b];
+        if (prefix_len[b] + n > maxvis) maxvis = prefix_len[b] + n;
+    }
+#pragma omp parallel
+    {
+        double *scratch = (double *)malloc(sizeof(double) * (maxvis + 1));
+        int64_t *slots = (int64_t *)malloc(sizeof(int64_t) * (maxvis + 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int32_t node = rows[2 * r], h = rows[2 * r + 1];
+            int32_t b = 0;
+            while (b + 1 <= batch && node_start[b + 1] <= node) ++b;
+            if (seq_err[b]) continue;
+            attention_row(q, k, v, dtype, node_start, parent, kv_start, prefix_len, b, node - node_start[b], h,
+                          hq, hkv, d, sm_scale, out + (size_t)r * d, lse + r, scratch, slots);
+        }
+        free(scratch);
+        free(slots);
+    }
+    free(seq_err);
+}
+
+/* Every row: out [total_nodes, hq, d], lse [total_nodes, hq]. */
+void oracle_tree_attention(const void *q, const void *k, const void *v, int32_t dtype,
+                           const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                           const int32_t *prefix_len, int32_t batch, int32_t max_nodes, int64_t total_slots,
+                           int32_t hq, int32_t hkv, int32_t d, double sm_scale, double *out, double *lse,
+                           int32_t *seq_err) {
+    oracle_attention_errors(node_start, parent, kv_start, prefix_len, batch, max_nodes, total_slots, seq_err);
+    const int64_t total = (int64_t)node_start[batch] * hq;
+    int32_t *rows = (int32_t *)malloc(sizeof(int32_t) * 2 * (total > 0 ? total : 1));
+    for (int64_t r = 0; r < total; ++r) {
+        rows[2 * r] = (int32_t)(r / hq);
+        rows[2 * r + 1] = (int32_t)(r % hq);
+    }
+    oracle_tree_attention_rows(q, k, v, dtype, node_start, parent, kv_start, prefix_len, batch, max_nodes,
+                               total_slots, hq, hkv, d, sm_scale, rows, total, out, lse);
+    free(rows);
+}
+
+/* Greedy target token of every logits row: the lowest index holding the row maximum.
+   +0 and -0 are equal; a NaN ranks above every number, so the first NaN wins. */
+void oracle_node_argmax(const void *logits, int32_t dtype, int64_t row_stride, int32_t num_rows,
+                        int32_t vocab, int32_t *target, double *max_value) {
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int32_t r = 0; r < num_rows; ++r) {
+        const size_t base = (size_t)r * row_stride;
+        int32_t best = 0;
+        double bv = elem(logits, dtype, base);
+        if (!isnan(bv)) {
+            for (int32_t t = 1; t < vocab; ++t) {
+                double x = elem(logits, dtype, base + t);
+                if (isnan(x)) { best = t; bv = x; break; }
+                if (x > bv) { best = t; bv = x; }
+            }
+        }
+        target[r] = best;
+        if (max_value) max_value[r] = bv;
+    }
+}
+
+/* Greedy acceptance per sequence.
+   accepted(0) = true; for i >= 1 in index order accepted(i) = accepted(parent(i)) and
+   draft[i] == target[parent(i)].  The chosen node i* maximises (depth, -index) over accepted
+   nodes; the path is anc(i*) root first; len = depth(i*) + 1; bonus = target[i*];
+   out_tokens = draft of path[1..len-1] followed by the bonus.  Padding is -1. */
+void oracle_greedy_accept(const int32_t *node_start, const int32_t *parent, const int32_t *draft,
+                          const int32_t *target, int32_t batch, int32_t max_nodes, int32_t vocab,
+                          int32_t *accept_len, int32_t *accept_path, int32_t *bonus_token,
+                          int32_t *out_tokens, int32_t *seq_err) {
+    for (int32_t b = 0; b < batch; ++b) {
+        const int32_t s = node_start[b];
+        const int32_t n = node_start[b + 1] - s;
+        int32_t *path = accept_path + (size_t)b * max_nodes;
+        int32_t *outt = out_tokens + (size_t)b * max_nodes;
+        for (int32_t t = 0; t < max_nodes; ++t) path[t] = outt[t] = -1;
+        accept_len[b] = 0;
+        bonus_token[b] = -1;
+        int32_t err = oracle_tree_errors(parent + s, n, max_nodes);
+        if (!(err & 2)) {
+            for (int32_t i = 0; i < n; ++i) {
+                if (target[s + i] < 0 || target[s + i] >= vocab) err |= 4;
+                if (i > 0 && (draft[s + i] < 0 || draft[s + i] >= vocab)) err |= 4;
+            }
+        }
+        seq_err[b] = err;
+        if (err) continue;
+        char acc[1024];
+        int32_t depth[1024];
+        acc[0] = 1;
+        depth[0] = 0;
+        int32_t best = 0;
+        for (int32_t i = 1; i < n; ++i) {
+            const int32_t p = parent[s + i];
+            depth[i] = depth[p] + 1;
+            acc[i] = acc[p] && draft[s + i] == target[s + p];
+            if (acc[i] && depth[i] > depth[best]) best = i; /* equal depth keeps the lower index */
+        }
+        const int32_t len = oracle_ancestor_path(parent + s, best, path);
+        accept_len[b] = len;
+        bonus_token[b] = target[s + best];
+        for (int32_t t = 1; t < len; ++t) outt[t - 1] = draft[s + path[t]];
+        outt[len - 1] = bonus_token[b];
+    }
+}
+
+/* KV compaction, out of place: k_out/v_out start as copies of k_in/v_in; then for every layer,
+   KV head and 0 <= d < len, slot s0+L+d of the output takes slot s0+L+path[d] of the INPUT.
+   new_len = L + len.  A sequence with len <= 0 is left alone (new_len = L). */
+void oracle_compact_kv(const void *k_in, const void *v_in, void *k_out, void *v_out, int32_t elem_bytes,
+                       int32_t num_layers, int64_t layer_stride_bytes, const int32_t *kv_start,
+                       const int32_t *prefix_len, const int32_t *accept_len, const int32_t *accept_path,
+                       int32_t batch, int32_t max_nodes, int64_t total_slots, int32_t hkv, int32_t d,
+                       int32_t *new_len, int32_t *seq_err) {
+    const size_t bytes = (size_t)num_layers * (size_t)layer_stride_bytes;
+    memcpy(k_out, k_in, bytes);
+    memcpy(v_out, v_in, bytes);
+    const size_t row = (size_t)hkv * d * elem_bytes; /* one slot: all KV heads */
+    for (int32_t b = 0; b < batch; ++b) {
+        const int32_t len = accept_len[b];
+        const int32_t *path = accept_path + (size_t)b * max_nodes;
+        int32_t err = 0;
+        new_len[b] = prefix_len[b];
+        if (len <= 0) { seq_err[b] = 0; continue; }
+        if (len > max_nodes || path[0] != 0) err |= 16;
+        for (int32_t t = 1; t < len && !err; ++t)
+            if (path[t] <= path[t - 1]) err |= 16;
+        if (!err && (kv_start[b] < 0 || prefix_len[b] < 0 ||
+                     (int64_t)kv_start[b] + prefix_len[b] + path[len - 1] >= total_slots))
+            err |= 8;
+        seq_err[b] = err;
+        if (err) continue;
+        const int64_t base = (int64_t)kv_start[b] + prefix_len[b];
+        for (int32_t l = 0; l < num_layers; ++l) {
+            const size_t lo = (size_t)l * layer_stride_bytes;
+            for (int32_t t = 0; t < len; ++t) {
+                const size_t dst = lo + (size_t)(base + t) * row;
+                const size_t src = lo + (size_t)(base + path[t]) * row;
+                memcpy((char *)k_out + dst, (const char *)k_in + src, row);
+                memcpy((char *)v_out + dst, (const char *)v_in + src, row);
+            }
+        }
+        new_len[b] = prefix_len[b] + len;
+    }
+}

@@ -1,0 +1,277 @@
+"""Pins of the CPU oracle against things other than itself (test infrastructure).
+
+Each ``pin_*`` function runs one family of checks against an oracle library handle and raises
+AssertionError on the first mismatch.  The test suite runs them on the real oracle, and runs
+them again on deliberately broken copies of the oracle source to show that a plausible
+mistake (dropped term, wrong sign or index, swapped operand, wrong tie-break) fails a pin.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+import oracle
+from draft_tree_verification_amd import synth
+from draft_tree_verification_amd.synth import BF16, F32
+
+from . import bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _attn(w, lib, sm_scale=None):
+    return oracle.tree_attention(w.q, w.k, w.v, w.node_start, w.parent, w.kv_start, w.prefix_len,
+                                 num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                                 head_dim=w.head_dim, sm_scale=w.sm_scale if sm_scale is None else sm_scale,
+                                 total_slots=w.total_slots, max_nodes=max(w.max_nodes, 1), lib=lib)
+
+
+def _close(a, b, rtol=1e-9, atol=1e-12, what=""):
+    a, b = np.asarray(a), np.asarray(b)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    ok = np.abs(a - b) <= atol + rtol * np.abs(b)
+    assert ok.all(), f"{what}: max abs diff {np.nanmax(np.abs(a - b))}"
+
+
+def small_tree_workload(seed, dtype=F32, hq=6, hkv=2, d=16, prefix=(0, 1, 7, 37), nodes=(9, 16, 5, 12),
+                        trees=None, sm_scale=None, q_scale=1.0):
+    return synth.make_workload("pin", seed, prefix_lens=list(prefix), nodes=None if trees else list(nodes),
+                               trees=trees, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype=dtype,
+                               vocab=64, q_scale=q_scale, logit_scale=1.0, sm_scale=sm_scale, slot_gap=3)
+
+
+def pin_attention(lib):
+    # 1. dense textbook attention over the closure-derived visible set, and torch SDPA.
+    for seed, dtype, scale in ((11, F32, None), (12, BF16, None), (13, F32, 1.0), (14, BF16, 8.0 / 4)):
+        w = small_tree_workload(seed, dtype=dtype, sm_scale=scale)
+        out, lse, err = _attn(w, lib)
+        assert (err == 0).all()
+        for b in range(w.batch):
+            s, e = w.node_start[b], w.node_start[b + 1]
+            ref, ref_lse = bf.attention_seq(w, b)
+            _close(out[s:e], ref, what=f"bruteforce out seed {seed} seq {b}")
+            _close(lse[s:e], ref_lse, what=f"bruteforce lse seed {seed} seq {b}")
+            _close(out[s:e], bf.attention_seq_sdpa(w, b), rtol=1e-8, atol=1e-10, what="sdpa")
+    # 2. GQA groupings: G = 1 (plain multi-head) and a single KV head.
+    for hq, hkv in ((4, 4), (8, 1)):
+        w = small_tree_workload(21, hq=hq, hkv=hkv)
+        out, _, _ = _attn(w, lib)
+        for b in range(w.batch):
+            s, e = w.node_start[b], w.node_start[b + 1]
+            _close(out[s:e], bf.attention_seq_sdpa(w, b), rtol=1e-8, atol=1e-10, what=f"gqa {hq}/{hkv}")
+    # 3. chain tree == causal attention of the N queries over L + N keys (bottom-right aligned).
+    n, L = 7, 11
+    w = small_tree_workload(31, prefix=(L,), trees=[synth.chain_tree(n)], sm_scale=0.9)
+    causal = np.concatenate([np.ones((n, L), bool), np.tril(np.ones((n, n), bool))], axis=1)
+    out, _, _ = _attn(w, lib)
+    _close(out, bf.attention_seq_sdpa(w, 0, mask=causal), rtol=1e-8, atol=1e-10, what="chain==causal")
+    # 4. a single node == ordinary decode attention over prefix + itself.
+    w = small_tree_workload(32, prefix=(50,), trees=[synth.chain_tree(1)], sm_scale=1.3)
+    out, _, _ = _attn(w, lib)
+    _close(out, bf.attention_seq_sdpa(w, 0, mask=np.ones((1, 51), bool)), rtol=1e-8, atol=1e-10,
+           what="decode")
+    # 5. closed forms.
+    w = small_tree_workload(41)
+    w.k[:] = 0.0  # uniform weights: the mean of the visible V rows
+    out, _, _ = _attn(w, lib)
+    for b in range(w.batch):
+        s, e = w.node_start[b], w.node_start[b + 1]
+        L, s0 = int(w.prefix_len[b]), int(w.kv_start[b])
+        vis = bf.visible_mask(w.parent[s:e], L)
+        V = w.v[s0:s0 + vis.shape[1]].astype(np.float64)
+        for i in range(e - s):
+            mean = V[vis[i]].mean(axis=0)                       # [Hkv, D]
+            exp_rows = np.repeat(mean, w.num_q_heads // w.num_kv_heads, axis=0)
+            _close(out[s + i], exp_rows, rtol=1e-12, atol=1e-12, what="K=0 mean")
+    w = small_tree_workload(42)
+    w.v[:] = 0.625
+    out, _, _ = _attn(w, lib)
+    _close(out, np.full_like(out, 0.625), rtol=1e-13, atol=1e-13, what="V constant")
+    # planted dominant key: node i's own tree key aligned with its queries -> output ~ its V row;
+    # the same key planted at a non-ancestor must change nothing.
+    w = small_tree_workload(43, prefix=(20,), trees=[np.array([-1, 0, 0, 1, 2, 2], np.int32)], hq=2, hkv=1)
+    base, _, _ = _attn(w, lib)
+    tgt = 4                                    # ancestors of 4: {0, 2, 4}
+    L = int(w.prefix_len[0])
+    w.k[L + tgt, 0, :] = 40.0 * np.sign(w.q[tgt, 0, :])
+    out, _, _ = _attn(w, lib)
+    _close(out[tgt, 0], w.v[L + tgt, 0].astype(np.float64), rtol=0, atol=1e-6, what="planted key")
+    for i in (1, 3):                           # 4 is not an ancestor of 1 or 3: bit-identical
+        assert np.array_equal(out[i], base[i]), "planted key leaked to a non-descendant"
+    # 6. invariants: perturbing non-ancestor tree slots leaves a node's output bit-identical.
+    w = small_tree_workload(51, dtype=BF16)
+    base, base_lse, _ = _attn(w, lib)
+    b = 1
+    s, e = int(w.node_start[b]), int(w.node_start[b + 1])
+    L, s0 = int(w.prefix_len[b]), int(w.kv_start[b])
+    M = bf.ancestor_closure(w.parent[s:e])
+    i = e - s - 1
+    rng = np.random.default_rng(5)
+    for j in range(e - s):
+        if not M[i, j]:
+            w.k[s0 + L + j] = rng.integers(0, 1 << 15, w.k.shape[1:], dtype=np.uint16)
+            w.v[s0 + L + j] = rng.integers(0, 1 << 15, w.v.shape[1:], dtype=np.uint16)
+    out, lse, _ = _attn(w, lib)
+    assert np.array_equal(out[s + i], base[s + i]) and np.array_equal(lse[s + i], base_lse[s + i])
+    # relabelling the nodes in another topological order permutes the rows, bit for bit.
+    parent = np.array([-1, 0, 0, 1, 2, 1, 3], np.int32)
+    perm = np.array([0, 2, 1, 4, 3, 6, 5])     # new index of old node j is perm[j]
+    inv = np.argsort(perm)
+    new_parent = np.array([-1 if parent[inv[k]] < 0 else perm[parent[inv[k]]] for k in range(7)], np.int32)
+    assert all(new_parent[k] < k for k in range(1, 7))
+    w1 = small_tree_workload(52, prefix=(9,), trees=[parent])
+    w2 = small_tree_workload(52, prefix=(9,), trees=[new_parent])
+    w2.q[:] = w1.q[inv]
+    w2.k[:] = w1.k
+    w2.v[:] = w1.v
+    Lr = 9
+    w2.k[Lr:Lr + 7] = w1.k[Lr + inv]
+    w2.v[Lr:Lr + 7] = w1.v[Lr + inv]
+    o1, _, _ = _attn(w1, lib)
+    o2, _, _ = _attn(w2, lib)
+    assert np.array_equal(o2, o1[inv]), "relabelling changed results"
+
+
+def _bf16_rows(vals):
+    return synth.f32_to_bf16_bits(np.asarray(vals, np.float32))
+
+
+def pin_argmax(lib):
+    # numpy.argmax (documented: first occurrence) on the widened rows, fp32 and bf16, tie-heavy too.
+    rng = np.random.default_rng(7)
+    for dtype in (F32, BF16):
+        for V, spread in ((1000, None), (4099, 3)):
+            x = rng.standard_normal((37, V)).astype(np.float32) * 2 if spread is None else \
+                rng.integers(-spread, spread + 1, (37, V)).astype(np.float32)
+            raw = x if dtype == F32 else synth.f32_to_bf16_bits(x)
+            tgt, mx = oracle.node_argmax(raw, lib=lib)
+            ref = np.argmax(bf.as_f64(raw, dtype), axis=1)
+            assert np.array_equal(tgt, ref), "argmax disagrees with numpy.argmax"
+            _close(mx, bf.as_f64(raw, dtype)[np.arange(37), ref], rtol=0, atol=0, what="max value")
+    # row stride larger than the vocabulary: only the first `vocab` entries count.
+    x = rng.standard_normal((5, 40)).astype(np.float32)
+    x[:, 30:] = 100.0
+    tgt, _ = oracle.node_argmax(x, vocab=30, row_stride=40, lib=lib)
+    assert np.array_equal(tgt, np.argmax(x[:, :30], axis=1))
+    # hand rows (expected index written by hand from the rule: lowest index of the maximum,
+    # +0 == -0, NaN above everything so the first NaN wins).
+    nan, inf = float("nan"), float("inf")
+    cases = [([3.0, 3.0, 3.0, 3.0], 0), ([9.0, 1.0, 2.0, 3.0], 0), ([1.0, 2.0, 3.0, 9.0], 3),
+             ([1.0, 7.0, 2.0, 7.0], 1), ([-0.0, 0.0, -1.0, -2.0], 0), ([-1.0, 0.0, -0.0, -3.0], 1),
+             ([-5.0, -0.0, 0.0, -0.0], 1), ([1.0, inf, 3.0, inf], 1), ([-inf, -inf, -inf, -inf], 0),
+             ([1.0, nan, 5.0, nan], 1), ([inf, 2.0, nan, inf], 2), ([-nan, 1.0, 2.0, 3.0], 0),
+             ([-3.0, -2.0, -1.0, -1.0], 2)]
+    for vals, expect in cases:
+        for raw in (np.asarray([vals], np.float32), _bf16_rows([vals])):
+            tgt, _ = oracle.node_argmax(raw, lib=lib)
+            assert tgt[0] == expect, f"argmax hand row {vals}: got {tgt[0]}, want {expect}"
+
+
+def pin_accept(lib):
+    # hand-built cases, one at a time and all in one batch.
+    cases = bf.load_cases(os.path.join(GOLDEN, "accept_cases.txt"))
+    maxn = max(len(c[1]) for c in cases)
+    for name, parent, draft, target, ln, path, bonus, outt in cases:
+        r = oracle.greedy_accept([0, len(parent)], parent, draft, target, maxn, 1000, lib=lib)
+        assert r["seq_err"][0] == 0, name
+        assert r["accept_len"][0] == ln[0], (name, r["accept_len"][0], ln[0])
+        assert list(r["accept_path"][0][:ln[0]]) == path and (r["accept_path"][0][ln[0]:] == -1).all(), name
+        assert r["bonus"][0] == bonus[0], name
+        assert list(r["out_tokens"][0][:ln[0]]) == outt and (r["out_tokens"][0][ln[0]:] == -1).all(), name
+    ns = np.cumsum([0] + [len(c[1]) for c in cases])
+    r = oracle.greedy_accept(ns, np.concatenate([c[1] for c in cases]), np.concatenate([c[2] for c in cases]),
+                             np.concatenate([c[3] for c in cases]), maxn, 1000, lib=lib)
+    assert list(r["accept_len"]) == [c[4][0] for c in cases]
+    # path enumeration on random trees with heavy duplicate matches.
+    rng = np.random.default_rng(3)
+    for trial in range(300):
+        n = int(rng.integers(1, 24))
+        parent = synth.random_tree(rng, n, max_depth=int(rng.integers(1, 8)))
+        target = rng.integers(0, 3, n).astype(np.int32)
+        draft = rng.integers(0, 3, n).astype(np.int32)
+        r = oracle.greedy_accept([0, n], parent, draft, target, 32, 3, lib=lib)
+        ln, path, bonus, outt = bf.accept_paths(parent, draft, target)
+        assert r["accept_len"][0] == ln and list(r["accept_path"][0][:ln]) == path, trial
+        assert r["bonus"][0] == bonus and list(r["out_tokens"][0][:ln]) == outt, trial
+    # statistical closed form: a chain with independent planting p accepts
+    # E[len] = sum_{k<N} p^k nodes (root included).
+    n, p, trials = 4, 0.7, 3000
+    w = synth.make_workload("chain_stats", 99, prefix_lens=[0] * trials, trees=[synth.chain_tree(n)] * trials,
+                            num_q_heads=1, num_kv_heads=1, head_dim=1, dtype=F32, vocab=97, logit_scale=1.0,
+                            accept_prob=p)
+    tgt, _ = oracle.node_argmax(w.logits, lib=lib)
+    r = oracle.greedy_accept(w.node_start, w.parent, w.draft, tgt, n, w.vocab, lib=lib)
+    mean = r["accept_len"].mean()
+    expect = sum(p ** k for k in range(n))
+    se = r["accept_len"].std() / math.sqrt(trials)
+    assert abs(mean - expect) < 5 * se, (mean, expect, se)
+    # data errors: bad parent, bad node count, token out of range -> flagged and skipped.
+    r = oracle.greedy_accept([0, 3, 5, 5, 8], [-1, 0, 2, -1, 0, -1, 0, 1], [0, 1, 2, 0, 1, 0, 1, 1000],
+                             [1, 1, 1, 1, 1, 1, 1, 1], 4, 1000, lib=lib)
+    assert list(r["seq_err"]) == [1, 0, 2, 4], list(r["seq_err"])
+    assert list(r["accept_len"]) == [0, 2, 0, 0]
+
+
+def pin_compact(lib):
+    for name, L, N, ln, path, expect, new_len in bf.load_cases(os.path.join(GOLDEN, "compact_cases.txt")):
+        L, N, ln, new_len = L[0], N[0], ln[0], new_len[0]
+        slots = L + N
+        k = np.arange(slots, dtype=np.int32).reshape(1, slots, 1, 1)
+        v = (1000 + np.arange(slots, dtype=np.int32)).reshape(1, slots, 1, 1)
+        ap = np.full((1, N), -1, np.int32)
+        ap[0, :ln] = path
+        k2, v2, nl, err = oracle.compact_kv(k, v, [0], [L], [ln], ap, num_layers=1, total_slots=slots,
+                                            num_kv_heads=1, head_dim=1, lib=lib)
+        assert err[0] == 0 and nl[0] == new_len, name
+        assert list(k2.ravel()) == expect, (name, list(k2.ravel()), expect)
+        assert list(v2.ravel() - 1000) == expect, name
+    # random multi-layer, bf16-sized and fp32-sized rows vs a numpy gather.
+    rng = np.random.default_rng(8)
+    for dt in (np.uint16, np.float32):
+        B, H, D, layers, maxn = 5, 3, 8, 2, 9
+        Ls = rng.integers(0, 20, B)
+        starts = np.concatenate([[0], np.cumsum(Ls + maxn + 2)])[:-1]
+        total = int(starts[-1] + Ls[-1] + maxn + 2)
+        k = rng.integers(0, 60000, (layers, total, H, D)).astype(dt)
+        v = rng.integers(0, 60000, (layers, total, H, D)).astype(dt)
+        lens = rng.integers(0, maxn + 1, B)
+        path = np.full((B, maxn), -1, np.int32)
+        for b in range(B):
+            if lens[b] > 0:
+                path[b, :lens[b]] = np.sort(np.concatenate([[0], rng.choice(np.arange(1, maxn), lens[b] - 1,
+                                                                          replace=False)]))
+        k2, v2, nl, err = oracle.compact_kv(k, v, starts, Ls, lens, path, num_layers=layers, total_slots=total,
+                                            num_kv_heads=H, head_dim=D, lib=lib)
+        ek, ev = k.copy(), v.copy()
+        for b in range(B):
+            if lens[b] > 0:
+                dst = starts[b] + Ls[b] + np.arange(lens[b])
+                src = starts[b] + Ls[b] + path[b, :lens[b]]
+                ek[:, dst] = k[:, src]
+                ev[:, dst] = v[:, src]
+        assert np.array_equal(k2, ek) and np.array_equal(v2, ev)
+        assert np.array_equal(nl, Ls + lens) and (err == 0).all()
+    # malformed accepted paths and slot overflow are flagged; the cache is untouched.
+    k = np.arange(10, dtype=np.int32).reshape(1, 10, 1, 1)
+    bad = np.array([[1, 2, -1], [0, 2, 1], [0, 1, 2]], np.int32)
+    k2, _, nl, err = oracle.compact_kv(k, k, [0, 0, 6], [2, 2, 2], [2, 3, 3], bad, num_layers=1, total_slots=10,
+                                       num_kv_heads=1, head_dim=1, lib=lib)
+    assert list(err) == [16, 16, 8] and list(nl) == [2, 2, 2] and np.array_equal(k2, k)
+
+
+def pin_tree_rules(lib):
+    assert oracle.tree_errors([-1], 4, lib=lib) == 0
+    assert oracle.tree_errors([-1, 0, 0, 2], 4, lib=lib) == 0
+    assert oracle.tree_errors([-1, 0, 0, 2], 3, lib=lib) == 2      # more nodes than allowed
+    assert oracle.tree_errors([], 4, lib=lib) == 2                 # empty tree
+    assert oracle.tree_errors([0, 0], 4, lib=lib) == 1             # root has a parent
+    assert oracle.tree_errors([-1, 1], 4, lib=lib) == 1            # self-parent
+    assert oracle.tree_errors([-1, 2, 0], 4, lib=lib) == 1         # parent after child
+    assert oracle.tree_errors([-1, -1], 4, lib=lib) == 1           # second root
+    assert list(oracle.ancestor_path([-1, 0, 1, 0, 3, 4], 5, lib=lib)) == [0, 3, 4, 5]
+    assert list(oracle.ancestor_path([-1, 0, 1, 0, 3, 4], 0, lib=lib)) == [0]
+
+
+ALL_PINS = (pin_attention, pin_argmax, pin_accept, pin_compact, pin_tree_rules)

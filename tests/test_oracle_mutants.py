@@ -1,0 +1,72 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Every mutant is the oracle source with one plausible slip applied textually (a dropped term, a
+wrong sign or index, a swapped operand, a wrong tie-break, an unsafe in-place order), built with
+gcc into a temporary directory.  The real oracle is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+
+from . import pins
+
+MUTANTS = {
+    "self_not_in_ancestors": ("for (int32_t j = i; j >= 0; j = parent[j]) rev[n++] = j;",
+                              "for (int32_t j = parent[i]; j >= 0; j = parent[j]) rev[n++] = j;\n"
+                              "    if (n == 0) rev[n++] = i;"),
+    "gqa_modulo_mapping": ("const int32_t g = h / G;", "const int32_t g = h % hkv;"),
+    "prefix_off_by_one": ("for (int32_t t = 0; t < L; ++t) slots[nvis++] = s0 + t;",
+                          "for (int32_t t = 1; t < L; ++t) slots[nvis++] = s0 + t;"),
+    "softmax_sign": ("scratch[t] = exp(scratch[t] - m);", "scratch[t] = exp(m - scratch[t]);"),
+    "scale_dropped": ("scratch[t] = sm_scale * dot;", "scratch[t] = dot;"),
+    "k_v_swapped": ("dot += elem(q, dtype, qrow + c) * elem(k, dtype, krow + c);",
+                    "dot += elem(q, dtype, qrow + c) * elem(v, dtype, krow + c);"),
+    "lse_base2": ("*lse = m + log(sum);", "*lse = m + log2(sum);"),
+    "argmax_last_tie": ("if (x > bv) { best = t; bv = x; }", "if (x >= bv) { best = t; bv = x; }"),
+    "argmax_ignores_nan": ("if (isnan(x)) { best = t; bv = x; break; }", "if (0) { best = t; bv = x; break; }"),
+    "accept_highest_index_tie": ("if (acc[i] && depth[i] > depth[best]) best = i;",
+                                 "if (acc[i] && depth[i] >= depth[best]) best = i;"),
+    "accept_ignores_ancestors": ("acc[i] = acc[p] && draft[s + i] == target[s + p];",
+                                 "acc[i] = draft[s + i] == target[s + p];"),
+    "accept_own_target": ("acc[i] = acc[p] && draft[s + i] == target[s + p];",
+                          "acc[i] = acc[p] && draft[s + i] == target[s + i];"),
+    "bonus_from_root": ("bonus_token[b] = target[s + best];", "bonus_token[b] = target[s];"),
+    "compact_descending_in_place": (
+        "            for (int32_t t = 0; t < len; ++t) {\n"
+        "                const size_t dst = lo + (size_t)(base + t) * row;\n"
+        "                const size_t src = lo + (size_t)(base + path[t]) * row;\n"
+        "                memcpy((char *)k_out + dst, (const char *)k_in + src, row);\n"
+        "                memcpy((char *)v_out + dst, (const char *)v_in + src, row);",
+        "            for (int32_t t = len - 1; t >= 0; --t) {\n"
+        "                const size_t dst = lo + (size_t)(base + t) * row;\n"
+        "                const size_t src = lo + (size_t)(base + path[t]) * row;\n"
+        "                memcpy((char *)k_out + dst, (const char *)k_out + src, row);\n"
+        "                memcpy((char *)v_out + dst, (const char *)v_out + src, row);"),
+    "new_len_excludes_bonus": ("new_len[b] = prefix_len[b] + len;", "new_len[b] = prefix_len[b] + len - 1;"),
+    "tree_rule_allows_self_parent": ("if (parent[i] < 0 || parent[i] >= i) err |= 1;",
+                                     "if (parent[i] < 0 || parent[i] > i) err |= 1;"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(os.path.join(os.path.dirname(oracle.__file__), "ev_oracle.c")) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    src = tmp_path / "mutant.c"
+    src.write_text(source.replace(old, new))
+    lib = oracle.load(oracle.build(str(src), str(tmp_path / "libmutant.so")))
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, IndexError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches mutant {name}"

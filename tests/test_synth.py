@@ -1,0 +1,58 @@
+"""The seeded input generator: rounding, determinism and the workloads' stated shapes."""
+import numpy as np
+import torch
+
+from draft_tree_verification_amd import synth
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 3,
+                        np.array([0.0, -0.0, 1.0, -1.0, 3.4e38, -3.4e38, 1e-40, np.inf, -np.inf], np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(synth.f32_to_bf16_bits(x), ref)
+    assert np.array_equal(synth.bf16_bits_to_f32(ref), torch.from_numpy(ref.view(np.int16)).view(
+        torch.bfloat16).float().numpy())
+
+
+def test_chunked_draws_equal_one_draw(monkeypatch):
+    a = synth._normal(np.random.Generator(np.random.PCG64(5)), 1000, 0.5, synth.BF16)
+    monkeypatch.setattr(synth, "_CHUNK", 37)
+    b = synth._normal(np.random.Generator(np.random.PCG64(5)), 1000, 0.5, synth.BF16)
+    assert np.array_equal(a, b)
+
+
+def test_random_tree_rules():
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        n = int(rng.integers(1, 65))
+        p = synth.random_tree(rng, n, 6)
+        assert p[0] == -1 and all(0 <= p[i] < i for i in range(1, n))
+        d = np.zeros(n, int)
+        for i in range(1, n):
+            d[i] = d[p[i]] + 1
+        assert d.max() <= 6
+
+
+def test_workload_shapes_and_determinism():
+    w = synth.make_config("tiny")
+    assert (w.batch, w.total_nodes, w.num_q_heads, w.num_kv_heads, w.head_dim, w.vocab) == (1, 4, 8, 2, 64, 1024)
+    assert w.q.dtype == np.float32 and list(w.parent) == [-1, 0, 1, 2] and w.prefix_len[0] == 256
+    assert w.digest() == synth.make_config("tiny").digest()
+    w = synth.make_config("c8")
+    assert w.batch == 8 and (w.nodes_per_seq == 16).all()
+    assert ((w.prefix_len >= 1024) & (w.prefix_len <= 8192)).all()
+    assert w.k.dtype == np.uint16 and w.k.shape == (w.total_slots, 8, 128) and w.logits.shape == (128, 151936)
+    # N(0,1)/sqrt(128)-scaled Q and N(0, 2^2) logits
+    q = synth.bf16_bits_to_f32(w.q)
+    assert abs(q.std() * np.sqrt(128) - 1) < 0.02
+    assert abs(synth.bf16_bits_to_f32(w.logits[:4]).std() - 2) < 0.02
+
+
+def test_planting_rule():
+    w = synth.make_workload("plant", 3, prefix_lens=[0] * 400, nodes=[8] * 400, num_q_heads=1, num_kv_heads=1,
+                            head_dim=1, dtype=synth.F32, vocab=50, logit_scale=1.0, accept_prob=0.6)
+    greedy = np.argmax(w.logits, axis=1)
+    hits = [w.draft[i] == greedy[w.node_start[b] + w.parent[i]]
+            for b in range(w.batch) for i in range(w.node_start[b] + 1, w.node_start[b + 1])]
+    assert abs(np.mean(hits) - 0.6) < 0.03
