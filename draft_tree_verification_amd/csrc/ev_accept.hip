@@ -1,0 +1,212 @@
+// ev_accept.hip -- greedy longest-accepted-path selection and in-place KV compaction (gfx950).
+//
+// Acceptance follows the verification rule on the pages (kongchang.com English article,
+// "Technical Background"): the target keeps the drafted prefix that agrees with its own greedy
+// choices and adds one token of its own after it; with a draft tree several root-to-node paths
+// are candidates at once.  A node is accepted when its parent is accepted and its draft token
+// equals the parent's greedy target token; the deepest accepted node wins (lowest index on equal
+// depth) and its target token is the bonus.  Per-sequence acceptance lengths differ inside one
+// batch (same article, "Current Limitation"), so compaction moves each sequence's accepted rows
+// right after its own prefix.
+//
+// One wavefront per sequence, lane i = tree node i (trees have at most 64 nodes).
+#include "ev_internal.h"
+
+namespace {
+
+struct AcceptArgs {
+    const int32_t *node_start, *parent, *draft, *target;
+    int32_t batch, total_nodes, max_nodes, vocab;
+    int32_t *accept_len, *accept_path, *bonus, *out_tokens, *err_flag;
+};
+
+__global__ __launch_bounds__(64) void greedy_accept_kernel(const AcceptArgs a) {
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    int32_t *path = a.accept_path + static_cast<size_t>(b) * a.max_nodes;
+    int32_t *outt = a.out_tokens + static_cast<size_t>(b) * a.max_nodes;
+    const int ns0 = a.node_start[b], ns1 = a.node_start[b + 1];
+    const int n = ns1 - ns0;
+    int err = 0;
+    if (ns0 < 0 || ns1 > a.total_nodes || n < 1 || n > a.max_nodes) err = EV_DATA_BAD_NODES;
+    int par = -1, tgt = 0, dft = 0;
+    if (!err && lane < n) {
+        par = a.parent[ns0 + lane];
+        tgt = a.target[ns0 + lane];
+        dft = a.draft[ns0 + lane];
+        if (lane == 0 ? par != -1 : (par < 0 || par >= lane)) err |= EV_DATA_BAD_PARENT;
+        if (tgt < 0 || tgt >= a.vocab) err |= EV_DATA_BAD_TOKEN;
+        if (lane > 0 && (dft < 0 || dft >= a.vocab)) err |= EV_DATA_BAD_TOKEN;
+    }
+    // OR of the error bits over the wave
+    for (int o = 32; o > 0; o >>= 1) err |= __shfl_xor(err, o, 64);
+    if (err) {
+        if (lane == 0) {
+            ev::flag_error(a.err_flag, err);
+            a.accept_len[b] = 0;
+            a.bonus[b] = -1;
+        }
+        for (int i = lane; i < a.max_nodes; i += 64) path[i] = outt[i] = -1;
+        return;
+    }
+    // an edge agrees when the child's draft token is the parent's greedy token
+    const int tpar = __shfl(tgt, par >= 0 ? par : 0, 64);
+    const bool agree = lane < n && (lane == 0 || dft == tpar);
+    // accepted(i) = every edge on the root path agrees; depth(i) = edges on it; anc = bitmask
+    bool acc = agree;
+    int depth = 0;
+    uint64_t anc = lane < n ? (1ull << lane) : 0ull;
+    int j = lane < n ? par : -1;
+    while (__any(j >= 0)) {
+        const int jj = j >= 0 ? j : 0;
+        const bool ag = __shfl(static_cast<int>(agree), jj, 64) != 0;
+        const int pj = __shfl(par, jj, 64);
+        if (j >= 0) {
+            acc = acc && ag;
+            ++depth;
+            anc |= 1ull << j;
+            j = pj;
+        }
+    }
+    // deepest accepted node, lowest index on equal depth: maximise (depth << 8) | (255 - index)
+    int key = (lane < n && acc) ? (depth << 8) | (255 - lane) : -1;
+    for (int o = 32; o > 0; o >>= 1) key = max(key, __shfl_xor(key, o, 64));
+    const int best = 255 - (key & 255);
+    const int len = (key >> 8) + 1;
+    const uint32_t mlo = __shfl(static_cast<uint32_t>(anc), best, 64);
+    const uint32_t mhi = __shfl(static_cast<uint32_t>(anc >> 32), best, 64);
+    const uint64_t on_path = (static_cast<uint64_t>(mhi) << 32) | mlo;
+    const int bonus = __shfl(tgt, best, 64);
+    // each position is written by exactly one lane: the on-path node of that depth, or lane d
+    if (lane < n && ((on_path >> lane) & 1ull)) {
+        path[depth] = lane;
+        if (lane > 0) outt[depth - 1] = dft;
+    }
+    if (lane >= len && lane < a.max_nodes) path[lane] = outt[lane] = -1;
+    if (lane == 0) {
+        outt[len - 1] = bonus;
+        a.accept_len[b] = len;
+        a.bonus[b] = bonus;
+    }
+}
+
+struct CompactArgs {
+    unsigned char *k, *v;
+    int64_t layer_stride;
+    const int32_t *kv_start, *prefix_len, *accept_len, *accept_path;
+    int32_t batch, max_nodes, row16;  // row16: 16-byte chunks per slot row
+    int64_t total_slots, row_bytes;
+    int32_t *new_len, *err_flag;
+};
+
+constexpr int kCompactThreads = 256;
+constexpr int kBatchRows = 8;
+
+// Block (b, layer).  Rows move in increasing d; a destination slot L+d can only be the source of
+// some d' <= d (path[d'] >= d' since the path strictly increases from 0), so every source is read
+// before anything overwrites it even though each thread streams its own columns independently.
+__global__ __launch_bounds__(kCompactThreads) void compact_kv_kernel(const CompactArgs a) {
+    const int b = blockIdx.x;
+    const int layer = blockIdx.y;
+    const int tid = threadIdx.x;
+    __shared__ int s_path[EV_MAX_NODES];
+    const int len = a.accept_len[b];
+    const int L = a.prefix_len[b];
+    const int s0 = a.kv_start[b];
+    int err = 0;
+    if (len > 0) {
+        if (len > a.max_nodes) err = EV_DATA_BAD_PATH;
+        if (!err && tid < len) {
+            const int p = a.accept_path[static_cast<size_t>(b) * a.max_nodes + tid];
+            s_path[tid] = p;
+            const int prev = tid ? a.accept_path[static_cast<size_t>(b) * a.max_nodes + tid - 1] : -1;
+            if (tid == 0 ? p != 0 : p <= prev) err = EV_DATA_BAD_PATH;
+        }
+    }
+    err = __syncthreads_or(err) ? EV_DATA_BAD_PATH : 0;
+    if (len > 0 && !err) {
+        const int last = s_path[len - 1];
+        if (s0 < 0 || L < 0 || static_cast<int64_t>(s0) + L + last >= a.total_slots) err = EV_DATA_BAD_SLOTS;
+    }
+    if (layer == 0 && tid == 0) {
+        a.new_len[b] = (len > 0 && !err) ? L + len : L;
+        ev::flag_error(a.err_flag, err);
+    }
+    if (len <= 1 || err) return;
+    const int64_t base = static_cast<int64_t>(layer) * a.layer_stride + (static_cast<int64_t>(s0) + L) * a.row_bytes;
+    for (int c = tid; c < 2 * a.row16; c += kCompactThreads) {
+        unsigned char *buf = (c < a.row16 ? a.k : a.v) + base + static_cast<int64_t>(c % a.row16) * 16;
+        for (int d0 = 1; d0 < len; d0 += kBatchRows) {
+            u32x4_t rows[kBatchRows];
+#pragma unroll
+            for (int i = 0; i < kBatchRows; ++i) {
+                const int d = d0 + i;
+                if (d < len && s_path[d] != d) rows[i] = ev::ld16(buf + static_cast<int64_t>(s_path[d]) * a.row_bytes);
+            }
+#pragma unroll
+            for (int i = 0; i < kBatchRows; ++i) {
+                const int d = d0 + i;
+                if (d < len && s_path[d] != d)
+                    *reinterpret_cast<u32x4_t *>(buf + static_cast<int64_t>(d) * a.row_bytes) = rows[i];
+            }
+        }
+    }
+}
+
+}  // namespace
+
+extern "C" ev_status ev_greedy_accept(const int32_t *node_start, const int32_t *parent, const int32_t *draft_token,
+                                      const int32_t *target_token, int32_t batch, int32_t total_nodes,
+                                      int32_t max_nodes, int32_t vocab, int32_t *accept_len, int32_t *accept_path,
+                                      int32_t *bonus_token, int32_t *out_tokens, int32_t *err_flag,
+                                      hipStream_t stream) {
+    if (!node_start || !parent || !draft_token || !target_token || !accept_len || !accept_path || !bonus_token ||
+        !out_tokens)
+        return EV_ERR_NULL;
+    if (batch < 0 || total_nodes < 0 || max_nodes < 1 || max_nodes > EV_MAX_NODES || vocab < 1) return EV_ERR_SHAPE;
+    const ev_status dev = ev::check_device();
+    if (dev != EV_OK) return dev;
+    if (batch == 0) return EV_OK;
+    AcceptArgs args{node_start, parent, draft_token, target_token, batch, total_nodes, max_nodes, vocab,
+                    accept_len, accept_path, bonus_token, out_tokens, err_flag};
+    hipLaunchKernelGGL(greedy_accept_kernel, dim3(batch), dim3(64), 0, stream, args);
+    return ev::launch_status();
+}
+
+extern "C" ev_status ev_compact_kv(void *k_cache, void *v_cache, int32_t elem_bytes, int32_t num_layers,
+                                   int64_t layer_stride_bytes, const int32_t *kv_start, const int32_t *prefix_len,
+                                   const int32_t *accept_len, const int32_t *accept_path, int32_t batch,
+                                   int32_t max_nodes, int64_t total_slots, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t *new_len, int32_t *err_flag, hipStream_t stream) {
+    if (!k_cache || !v_cache || !kv_start || !prefix_len || !accept_len || !accept_path || !new_len)
+        return EV_ERR_NULL;
+    if (batch < 0 || num_layers < 1 || max_nodes < 1 || max_nodes > EV_MAX_NODES || total_slots < 0 ||
+        num_kv_heads < 1 || head_dim < 1)
+        return EV_ERR_SHAPE;
+    if (elem_bytes != 2 && elem_bytes != 4) return EV_ERR_DTYPE;
+    const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * head_dim * elem_bytes;
+    if (layer_stride_bytes < total_slots * row_bytes) return EV_ERR_SHAPE;
+    if (!ev::aligned16(k_cache) || !ev::aligned16(v_cache) || row_bytes % 16 || layer_stride_bytes % 16)
+        return EV_ERR_ALIGN;
+    if (new_len == prefix_len) return EV_ERR_SHAPE;
+    const ev_status dev = ev::check_device();
+    if (dev != EV_OK) return dev;
+    if (batch == 0) return EV_OK;
+    CompactArgs args;
+    args.k = static_cast<unsigned char *>(k_cache);
+    args.v = static_cast<unsigned char *>(v_cache);
+    args.layer_stride = layer_stride_bytes;
+    args.kv_start = kv_start;
+    args.prefix_len = prefix_len;
+    args.accept_len = accept_len;
+    args.accept_path = accept_path;
+    args.batch = batch;
+    args.max_nodes = max_nodes;
+    args.row16 = static_cast<int32_t>(row_bytes / 16);
+    args.total_slots = total_slots;
+    args.row_bytes = row_bytes;
+    args.new_len = new_len;
+    args.err_flag = err_flag;
+    hipLaunchKernelGGL(compact_kv_kernel, dim3(batch, num_layers), dim3(kCompactThreads), 0, stream, args);
+    return ev::launch_status();
+}

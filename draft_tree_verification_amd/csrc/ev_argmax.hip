@@ -1,0 +1,228 @@
+// ev_argmax.hip -- per-node greedy target token (row argmax over the vocabulary) for gfx950.
+//
+// At temperature 0 the target's own choice at every tree node is the argmax of its logits row
+// (aiposthub.com analysis, "paper Table 2": greedy T=0 verification); the accept step compares
+// each child's draft token with it.  The result must be bit-exact, so the total order is fixed:
+// larger value first, lower index on ties, +0 == -0, any NaN above every number.
+//
+// HBM-bound streaming: each thread reads 16 bytes per load, four loads in flight.  Values are
+// mapped to order-preserving unsigned keys (sign-magnitude -> offset binary, both zeros to the
+// same key); for bf16 the key transform and the per-load maximum run on packed 16-bit integer
+// ops, and the index of a new maximum is searched only when a load beats the running best (rare
+// after the first few loads), so ties keep the earliest index for free.  Rows with few rows in the
+// batch are split across workgroups; the pieces meet through a 64-bit atomicMax on
+// (key << 32 | ~index) and the last-arriving workgroup writes the token.
+#include "ev_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 8;                        // elements per thread per load group
+constexpr int kSegQuantum = kThreads * kChunk;   // segment lengths are multiples of this
+constexpr int kTargetBlocks = 1024;
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef short ss2 __attribute__((ext_vector_type(2)));
+
+struct ArgmaxArgs {
+    const void *logits;
+    int64_t row_stride;
+    int32_t rows, vocab, splits, seg;
+    int32_t *target;
+    float *max_value;
+    unsigned long long *keys;  // [rows] (only when splits > 1)
+    int32_t *counters;         // [rows]
+};
+
+// Order-preserving key of a bf16 value (16 bits, in a uint32): +-0 -> 0x8000, NaN -> 0xFFFF.
+__device__ __forceinline__ uint32_t key_bf16(uint32_t h) {
+    const uint32_t mag = h & 0x7FFFu;
+    if (mag > 0x7F80u) return 0xFFFFu;
+    return (h & 0x8000u) ? 0x8000u - mag : 0x8000u + mag;
+}
+// Order-preserving key of an fp32 value: +-0 -> 0x80000000, NaN -> 0xFFFFFFFF.
+__device__ __forceinline__ uint32_t key_f32(uint32_t u) {
+    const uint32_t mag = u & 0x7FFFFFFFu;
+    if (mag > 0x7F800000u) return 0xFFFFFFFFu;
+    return (u & 0x80000000u) ? 0x80000000u - mag : 0x80000000u + mag;
+}
+__device__ __forceinline__ float value_of_key(uint32_t key, bool f32) {
+    if (f32) {
+        if (key == 0xFFFFFFFFu) return __builtin_nanf("");
+        const uint32_t bits = key >= 0x80000000u ? key - 0x80000000u : (0x80000000u - key) | 0x80000000u;
+        return __builtin_bit_cast(float, bits);
+    }
+    if (key == 0xFFFFu) return __builtin_nanf("");
+    const uint32_t h = key >= 0x8000u ? key - 0x8000u : (0x8000u - key) | 0x8000u;
+    return __builtin_bit_cast(float, h << 16);
+}
+
+// Keys of two packed bf16 values without NaN handling (the caller checks for NaN separately).
+__device__ __forceinline__ us2 keys2(uint32_t w) {
+    const us2 h = __builtin_bit_cast(us2, w);
+    const us2 mag = h & static_cast<unsigned short>(0x7FFF);
+    const us2 smask = __builtin_bit_cast(us2, __builtin_bit_cast(ss2, h) >> static_cast<short>(15));
+    return ((mag ^ smask) - smask) + static_cast<unsigned short>(0x8000);
+}
+
+__device__ __forceinline__ unsigned long long pack(uint32_t key, int32_t idx) {
+    return (static_cast<unsigned long long>(key) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(idx));
+}
+
+template <bool F32IN>
+__global__ __launch_bounds__(kThreads) void node_argmax_kernel(const ArgmaxArgs a) {
+    const int row = blockIdx.x / a.splits, split = blockIdx.x % a.splits;
+    const int v0 = split * a.seg;
+    const int v1 = min(a.vocab, v0 + a.seg);
+    const int tid = threadIdx.x;
+    uint32_t best = 0;           // keys are >= 0x80 for every real value, so 0 means "none"
+    int32_t bidx = 0x7FFFFFFF;
+
+    if constexpr (!F32IN) {
+        const uint16_t *rp = static_cast<const uint16_t *>(a.logits) + static_cast<int64_t>(row) * a.row_stride;
+        int base = v0 + tid * kChunk;
+        auto consume = [&](u32x4_t w, int at) {
+            const us2 k0 = keys2(w[0]), k1 = keys2(w[1]), k2 = keys2(w[2]), k3 = keys2(w[3]);
+            const us2 km = __builtin_elementwise_max(__builtin_elementwise_max(k0, k1), __builtin_elementwise_max(k2, k3));
+            const us2 mags = __builtin_elementwise_max(
+                __builtin_elementwise_max(__builtin_bit_cast(us2, w[0] & 0x7FFF7FFFu),
+                                          __builtin_bit_cast(us2, w[1] & 0x7FFF7FFFu)),
+                __builtin_elementwise_max(__builtin_bit_cast(us2, w[2] & 0x7FFF7FFFu),
+                                          __builtin_bit_cast(us2, w[3] & 0x7FFF7FFFu)));
+            const uint32_t kmax = km[0] > km[1] ? km[0] : km[1];
+            const bool has_nan = mags[0] > 0x7F80u || mags[1] > 0x7F80u;
+            if (kmax > best || has_nan) {
+                // exact scan of these eight values in index order
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t h = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+                    const uint32_t k = key_bf16(h);
+                    if (k > best) { best = k; bidx = at + e; }
+                }
+            }
+        };
+        // main body: four 16-byte loads in flight per thread
+        for (; base + 3 * kSegQuantum + kChunk <= v1; base += 4 * kSegQuantum) {
+            const u32x4_t w0 = ev::ld16_stream(rp + base);
+            const u32x4_t w1 = ev::ld16_stream(rp + base + kSegQuantum);
+            const u32x4_t w2 = ev::ld16_stream(rp + base + 2 * kSegQuantum);
+            const u32x4_t w3 = ev::ld16_stream(rp + base + 3 * kSegQuantum);
+            consume(w0, base);
+            consume(w1, base + kSegQuantum);
+            consume(w2, base + 2 * kSegQuantum);
+            consume(w3, base + 3 * kSegQuantum);
+        }
+        for (; base + kChunk <= v1; base += kSegQuantum) consume(ev::ld16_stream(rp + base), base);
+        if (base < v1) {  // ragged end of the row: element by element
+            for (int e = base; e < v1; ++e) {
+                const uint32_t k = key_bf16(rp[e]);
+                if (k > best) { best = k; bidx = e; }
+            }
+        }
+    } else {
+        const float *rp = static_cast<const float *>(a.logits) + static_cast<int64_t>(row) * a.row_stride;
+        int base = v0 + tid * kChunk;
+        auto consume = [&](u32x4_t x, u32x4_t y, int at) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t k = key_f32(e < 4 ? x[e] : y[e - 4]);
+                if (k > best) { best = k; bidx = at + e; }
+            }
+        };
+        for (; base + kChunk <= v1; base += kSegQuantum)
+            consume(ev::ld16_stream(rp + base), ev::ld16_stream(rp + base + 4), base);
+        if (base < v1) {
+            for (int e = base; e < v1; ++e) {
+                const uint32_t k = key_f32(__builtin_bit_cast(uint32_t, rp[e]));
+                if (k > best) { best = k; bidx = e; }
+            }
+        }
+    }
+
+    // workgroup reduction of (key, -index)
+    unsigned long long p = best ? pack(best, bidx) : 0ull;
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long q = __shfl_xor(p, o, 64);
+        p = q > p ? q : p;
+    }
+    __shared__ unsigned long long s_red[kThreads / 64];
+    __shared__ int s_last;
+    if ((tid & 63) == 0) s_red[tid >> 6] = p;
+    __syncthreads();
+    if (tid != 0) return;
+    for (int w = 1; w < kThreads / 64; ++w) p = s_red[w] > p ? s_red[w] : p;
+
+    if (a.splits > 1) {
+        atomicMax(a.keys + row, p);
+        __threadfence();
+        const int old = __hip_atomic_fetch_add(a.counters + row, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old == a.splits - 1;
+        if (!s_last) return;
+        __threadfence();
+        p = atomicExch(a.keys + row, 0ull);
+        a.counters[row] = 0;
+    }
+    const uint32_t key = static_cast<uint32_t>(p >> 32);
+    a.target[row] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(p & 0xFFFFFFFFu));
+    if (a.max_value) a.max_value[row] = value_of_key(key, F32IN);
+}
+
+struct ArgmaxPlan {
+    int splits, seg;
+    size_t bytes;
+};
+
+ArgmaxPlan make_plan(int32_t rows, int32_t vocab) {
+    ArgmaxPlan p{};
+    int splits = rows >= kTargetBlocks ? 1 : (kTargetBlocks + rows - 1) / rows;
+    const int max_by_len = (vocab + 4 * kSegQuantum - 1) / (4 * kSegQuantum);  // >= 4 quanta each
+    if (splits > max_by_len) splits = max_by_len;
+    if (splits < 1) splits = 1;
+    int seg = (vocab + splits - 1) / splits;
+    seg = ((seg + kSegQuantum - 1) / kSegQuantum) * kSegQuantum;
+    splits = (vocab + seg - 1) / seg;
+    p.splits = splits;
+    p.seg = seg;
+    p.bytes = splits > 1 ? ((static_cast<size_t>(rows) * 12 + 255) / 256) * 256 : 0;
+    return p;
+}
+
+}  // namespace
+
+extern "C" size_t ev_node_argmax_workspace_size(int32_t num_rows, int32_t vocab) {
+    if (num_rows < 0 || vocab < 1) return 0;
+    return make_plan(num_rows, vocab).bytes;
+}
+
+extern "C" ev_status ev_node_argmax(const void *logits, ev_dtype dtype, int64_t row_stride, int32_t num_rows,
+                                    int32_t vocab, int32_t *target_token, float *max_value, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    if (!logits || !target_token) return EV_ERR_NULL;
+    if (num_rows < 0 || vocab < 1 || row_stride < vocab) return EV_ERR_SHAPE;
+    if (dtype != EV_BF16 && dtype != EV_F32) return EV_ERR_DTYPE;
+    const int esz = dtype == EV_BF16 ? 2 : 4;
+    if (!ev::aligned16(logits) || (row_stride * esz) % 16) return EV_ERR_ALIGN;
+    const ArgmaxPlan plan = make_plan(num_rows, vocab);
+    if (plan.bytes && (!workspace || workspace_bytes < plan.bytes)) return EV_ERR_WORKSPACE;
+    const ev_status dev = ev::check_device();
+    if (dev != EV_OK) return dev;
+    if (num_rows == 0) return EV_OK;
+    ArgmaxArgs args;
+    args.logits = logits;
+    args.row_stride = row_stride;
+    args.rows = num_rows;
+    args.vocab = vocab;
+    args.splits = plan.splits;
+    args.seg = plan.seg;
+    args.target = target_token;
+    args.max_value = max_value;
+    args.keys = static_cast<unsigned long long *>(workspace);
+    args.counters = reinterpret_cast<int32_t *>(static_cast<unsigned char *>(workspace) +
+                                                static_cast<size_t>(num_rows) * 8);
+    const dim3 grid(static_cast<unsigned>(num_rows) * plan.splits);
+    if (dtype == EV_BF16)
+        hipLaunchKernelGGL(node_argmax_kernel<false>, grid, dim3(kThreads), 0, stream, args);
+    else
+        hipLaunchKernelGGL(node_argmax_kernel<true>, grid, dim3(kThreads), 0, stream, args);
+    return ev::launch_status();
+}

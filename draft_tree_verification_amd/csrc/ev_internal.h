@@ -1,0 +1,64 @@
+// ev_internal.h -- helpers shared by the gfx950 kernels of the verification-step library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ev.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+namespace ev {
+
+// ---------------------------------------------------------------- host side
+ev_status check_device();         // current device must be gfx950
+int device_cu_count();            // compute units of the current device (cached per device)
+int current_device();
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline ev_status launch_status() { return hipGetLastError() == hipSuccess ? EV_OK : EV_ERR_HIP; }
+
+// ---------------------------------------------------------------- device side
+__device__ __forceinline__ u32x4_t ld16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
+
+// Streaming 16-byte load: data read exactly once, so keep it out of the caches' way.
+__device__ __forceinline__ u32x4_t ld16_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (round to nearest even) in one dword, low half first: one
+// v_cvt_pk_bf16_f32.  (Built from a bf16x2 vector: element-wise bit_casts out of u32x4
+// vectors were mis-translated by the compiler, converting only the first element.)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t f2bf_bits(float x) { return pack_bf16x2(x, 0.f) & 0xFFFFu; }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+__device__ __forceinline__ f32x4_t ld16f(const float *p) { return *reinterpret_cast<const f32x4_t *>(p); }
+__device__ __forceinline__ f32x4_t ld16f_stream(const float *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+}
+
+// Eight fp32 values (two 16-byte loads) -> eight bf16 in four dwords.
+__device__ __forceinline__ u32x4_t f32x8_to_bf16x8(f32x4_t a, f32x4_t b) {
+    return u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                   pack_bf16x2(b[2], b[3])};
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ void flag_error(int32_t *err_flag, int32_t bits) {
+    if (err_flag && bits) atomicOr(err_flag, bits);
+}
+
+}  // namespace ev

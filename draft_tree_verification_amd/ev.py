@@ -1,0 +1,288 @@
+"""Thin ctypes binding of ``libev.so`` (the C ABI in include/ev.h).
+
+Argument marshalling only: every step of the verification path runs in the library's HIP
+kernels.  The ``ev_*`` functions mirror the C entry points one to one (integer device
+addresses, sizes, a HIP stream handle).  The lower-case helpers accept torch tensors that
+live on a ROCm device, check shapes/dtypes/contiguity, allocate outputs and workspaces with
+torch and call the matching ``ev_*`` function on the current torch stream.
+
+There is no fallback: if the library is missing, importing the helpers raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libev.so")
+
+EV_BF16, EV_F32 = 0, 1
+EV_OK = 0
+STATUS = {0: "EV_OK", 1: "EV_ERR_NULL", 2: "EV_ERR_SHAPE", 3: "EV_ERR_DTYPE", 4: "EV_ERR_ALIGN",
+          5: "EV_ERR_WORKSPACE", 6: "EV_ERR_DEVICE", 7: "EV_ERR_HIP"}
+DATA_BAD_PARENT, DATA_BAD_NODES, DATA_BAD_TOKEN, DATA_BAD_SLOTS, DATA_BAD_PATH = 1, 2, 4, 8, 16
+MAX_NODES = 64
+MAX_BATCH = 2048
+
+EXPORTS = ("ev_status_string", "ev_tree_attention_workspace_size", "ev_tree_attention",
+           "ev_node_argmax_workspace_size", "ev_node_argmax", "ev_greedy_accept", "ev_compact_kv")
+
+_lib = None
+_P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class EvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libev.so (built by draft_tree_verification_amd.build); raise if it is absent."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m draft_tree_verification_amd.build` "
+                           "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    lib.ev_status_string.restype = ctypes.c_char_p
+    lib.ev_status_string.argtypes = [ctypes.c_int]
+    lib.ev_tree_attention_workspace_size.restype = _SZ
+    lib.ev_tree_attention_workspace_size.argtypes = [_I32, _I32, _I32, _I32, _I32]
+    lib.ev_tree_attention.restype = ctypes.c_int
+    lib.ev_tree_attention.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
+                                      _I32, ctypes.c_int, _F, _P, _SZ, _P, _P]
+    lib.ev_node_argmax_workspace_size.restype = _SZ
+    lib.ev_node_argmax_workspace_size.argtypes = [_I32, _I32]
+    lib.ev_node_argmax.restype = ctypes.c_int
+    lib.ev_node_argmax.argtypes = [_P, ctypes.c_int, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]
+    lib.ev_greedy_accept.restype = ctypes.c_int
+    lib.ev_greedy_accept.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]
+    lib.ev_compact_kv.restype = ctypes.c_int
+    lib.ev_compact_kv.argtypes = [_P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P,
+                                  _P, _P]
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------------------------ raw C entry points
+def ev_status_string(status: int) -> str:
+    return load().ev_status_string(status).decode()
+
+
+def ev_tree_attention_workspace_size(batch, max_nodes, num_q_heads, num_kv_heads, head_dim) -> int:
+    return int(load().ev_tree_attention_workspace_size(batch, max_nodes, num_q_heads, num_kv_heads, head_dim))
+
+
+def ev_tree_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch, total_nodes,
+                      max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype, sm_scale, workspace,
+                      workspace_bytes, err_flag, stream) -> int:
+    return load().ev_tree_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
+                                    total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype,
+                                    sm_scale, workspace, workspace_bytes, err_flag, stream)
+
+
+def ev_node_argmax_workspace_size(num_rows, vocab) -> int:
+    return int(load().ev_node_argmax_workspace_size(num_rows, vocab))
+
+
+def ev_node_argmax(logits, dtype, row_stride, num_rows, vocab, target_token, max_value, workspace, workspace_bytes,
+                   stream) -> int:
+    return load().ev_node_argmax(logits, dtype, row_stride, num_rows, vocab, target_token, max_value, workspace,
+                                 workspace_bytes, stream)
+
+
+def ev_greedy_accept(node_start, parent, draft_token, target_token, batch, total_nodes, max_nodes, vocab, accept_len,
+                     accept_path, bonus_token, out_tokens, err_flag, stream) -> int:
+    return load().ev_greedy_accept(node_start, parent, draft_token, target_token, batch, total_nodes, max_nodes,
+                                   vocab, accept_len, accept_path, bonus_token, out_tokens, err_flag, stream)
+
+
+def ev_compact_kv(k_cache, v_cache, elem_bytes, num_layers, layer_stride_bytes, kv_start, prefix_len, accept_len,
+                  accept_path, batch, max_nodes, total_slots, num_kv_heads, head_dim, new_len, err_flag,
+                  stream) -> int:
+    return load().ev_compact_kv(k_cache, v_cache, elem_bytes, num_layers, layer_stride_bytes, kv_start, prefix_len,
+                                accept_len, accept_path, batch, max_nodes, total_slots, num_kv_heads, head_dim,
+                                new_len, err_flag, stream)
+
+
+# ------------------------------------------------------------------------------ torch helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _addr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    return (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != EV_OK:
+        raise EvError(status, where)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return EV_BF16
+    if t.dtype == torch.float32:
+        return EV_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _need(t, name, dtype=None, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+class Workspace:
+    """A device byte buffer zeroed once at creation and reused across calls on one stream."""
+
+    def __init__(self, nbytes: int, device):
+        torch = _torch()
+        self.nbytes = int(nbytes)
+        self.buf = torch.zeros(max(self.nbytes, 256), dtype=torch.uint8, device=device)
+
+    @property
+    def ptr(self):
+        return self.buf.data_ptr()
+
+
+def tree_attention(q, k_cache, v_cache, node_start, parent, kv_start, prefix_len, *, max_nodes: int,
+                   sm_scale: float, out=None, lse=None, workspace: Workspace = None, err_flag=None, stream=None):
+    """Tree-masked GQA attention (ev_tree_attention).  q [T, Hq, D]; caches [slots, Hkv, D]; metadata int32.
+    Returns (out, lse, workspace)."""
+    torch = _torch()
+    _need(q, "q", ndim=3)
+    _need(k_cache, "k_cache", q.dtype, 3)
+    _need(v_cache, "v_cache", q.dtype, 3)
+    for name, t in (("node_start", node_start), ("parent", parent), ("kv_start", kv_start),
+                    ("prefix_len", prefix_len)):
+        _need(t, name, torch.int32, 1)
+    T, Hq, D = q.shape
+    slots, Hkv, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q / k_cache / v_cache shapes disagree")
+    B = prefix_len.shape[0]
+    if node_start.shape[0] != B + 1 or kv_start.shape[0] != B or parent.shape[0] != T:
+        raise ValueError("metadata lengths disagree with batch / total nodes")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    need = ev_tree_attention_workspace_size(B, max_nodes, Hq, Hkv, D)
+    if workspace is None or workspace.nbytes < need:
+        workspace = Workspace(need, q.device)
+    st = ev_tree_attention(_addr(q), _addr(k_cache), _addr(v_cache), _addr(out), _addr(lse), _addr(node_start),
+                           _addr(parent), _addr(kv_start), _addr(prefix_len), B, T, max_nodes, slots, Hq, Hkv, D,
+                           _dtype_code(q), float(sm_scale), workspace.ptr, workspace.nbytes, _addr(err_flag),
+                           _stream(stream))
+    _check(st, "ev_tree_attention")
+    return out, lse, workspace
+
+
+def node_argmax(logits, *, vocab: int = None, target=None, max_value=None, workspace: Workspace = None,
+                stream=None):
+    """Greedy token per row (ev_node_argmax).  logits [R, stride] bf16/fp32.  Returns (target, max_value, ws)."""
+    torch = _torch()
+    _need(logits, "logits", ndim=2)
+    R, stride = logits.shape
+    vocab = stride if vocab is None else vocab
+    if target is None:
+        target = torch.empty(R, dtype=torch.int32, device=logits.device)
+    if max_value is None:
+        max_value = torch.empty(R, dtype=torch.float32, device=logits.device)
+    need = ev_node_argmax_workspace_size(R, vocab)
+    if need and (workspace is None or workspace.nbytes < need):
+        workspace = Workspace(need, logits.device)
+    st = ev_node_argmax(_addr(logits), _dtype_code(logits), stride, R, vocab, _addr(target), _addr(max_value),
+                        workspace.ptr if workspace is not None else None,
+                        workspace.nbytes if workspace is not None else 0, _stream(stream))
+    _check(st, "ev_node_argmax")
+    return target, max_value, workspace
+
+
+def greedy_accept(node_start, parent, draft_token, target_token, *, max_nodes: int, vocab: int, out=None,
+                  err_flag=None, stream=None):
+    """Longest accepted path per sequence (ev_greedy_accept).
+    Returns dict(accept_len [B], accept_path [B, max_nodes], bonus [B], out_tokens [B, max_nodes])."""
+    torch = _torch()
+    for name, t in (("node_start", node_start), ("parent", parent), ("draft_token", draft_token),
+                    ("target_token", target_token)):
+        _need(t, name, torch.int32, 1)
+    B = node_start.shape[0] - 1
+    T = parent.shape[0]
+    dev = parent.device
+    if out is None:
+        out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+               "accept_path": torch.empty((B, max_nodes), dtype=torch.int32, device=dev),
+               "bonus": torch.empty(B, dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((B, max_nodes), dtype=torch.int32, device=dev)}
+    st = ev_greedy_accept(_addr(node_start), _addr(parent), _addr(draft_token), _addr(target_token), B, T, max_nodes,
+                          vocab, _addr(out["accept_len"]), _addr(out["accept_path"]), _addr(out["bonus"]),
+                          _addr(out["out_tokens"]), _addr(err_flag), _stream(stream))
+    _check(st, "ev_greedy_accept")
+    return out
+
+
+def compact_kv(k_cache, v_cache, kv_start, prefix_len, accept_len, accept_path, *, new_len=None, err_flag=None,
+               stream=None):
+    """In-place KV compaction (ev_compact_kv).  Caches [slots, Hkv, D] or [layers, slots, Hkv, D]."""
+    torch = _torch()
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache", k_cache.dtype)
+    if k_cache.dim() == 3:
+        layers, (slots, Hkv, D) = 1, k_cache.shape
+    elif k_cache.dim() == 4:
+        layers, slots, Hkv, D = k_cache.shape
+    else:
+        raise ValueError("caches must be [slots, Hkv, D] or [layers, slots, Hkv, D]")
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache / v_cache shapes disagree")
+    B = prefix_len.shape[0]
+    max_nodes = accept_path.shape[1]
+    if new_len is None:
+        new_len = torch.empty(B, dtype=torch.int32, device=k_cache.device)
+    esz = k_cache.element_size()
+    st = ev_compact_kv(_addr(k_cache), _addr(v_cache), esz, layers, slots * Hkv * D * esz, _addr(kv_start),
+                       _addr(prefix_len), _addr(accept_len), _addr(accept_path), B, max_nodes, slots, Hkv, D,
+                       _addr(new_len), _addr(err_flag), _stream(stream))
+    _check(st, "ev_compact_kv")
+    return new_len
+
+
+def verify_step(q, k_cache, v_cache, logits, node_start, parent, kv_start, prefix_len, draft_token, *,
+                max_nodes: int, sm_scale: float, state: dict = None, stream=None):
+    """One whole verification step: attention, argmax, acceptance, compaction (four launches, one stream).
+    ``state`` carries reusable outputs and workspaces between calls."""
+    torch = _torch()
+    state = {} if state is None else state
+    if "err" not in state:
+        state["err"] = torch.zeros(1, dtype=torch.int32, device=q.device)
+    out, lse, ws = tree_attention(q, k_cache, v_cache, node_start, parent, kv_start, prefix_len, max_nodes=max_nodes,
+                                  sm_scale=sm_scale, out=state.get("out"), lse=state.get("lse"),
+                                  workspace=state.get("attn_ws"), err_flag=state["err"], stream=stream)
+    state.update(out=out, lse=lse, attn_ws=ws)
+    tgt, mx, aws = node_argmax(logits, target=state.get("target"), max_value=state.get("max_value"),
+                               workspace=state.get("argmax_ws"), stream=stream)
+    state.update(target=tgt, max_value=mx, argmax_ws=aws)
+    acc = greedy_accept(node_start, parent, draft_token, tgt, max_nodes=max_nodes, vocab=logits.shape[1],
+                        out=state.get("accept"), err_flag=state["err"], stream=stream)
+    state["accept"] = acc
+    state["new_len"] = compact_kv(k_cache, v_cache, kv_start, prefix_len, acc["accept_len"], acc["accept_path"],
+                                  new_len=state.get("new_len"), err_flag=state["err"], stream=stream)
+    return state

@@ -1,0 +1,181 @@
+/*
+ * ev.h -- C ABI of the draft-tree verification step on AMD MI355X (gfx950).
+ *
+ * Speculative decoding (kongchang.com English article, section "Technical Background"): a small
+ * draft model proposes tokens, the target model checks all of them in ONE parallel forward pass,
+ * keeps the prefix that agrees with its own choice and then contributes one token of its own;
+ * EAGLE-2's dynamic draft tree lets that one pass cover several candidate paths.  This library
+ * is the target-side hot path of that check for one attention layer at temperature 0 (greedy;
+ * aiposthub.com analysis, "paper Table 2"), in four calls:
+ *
+ *   ev_tree_attention   tree-masked GQA attention of every tree node over its sequence's KV
+ *                       prefix plus its own ancestors (and itself)
+ *   ev_node_argmax      the target's greedy token for every tree node (row argmax of logits)
+ *   ev_greedy_accept    the longest accepted root-to-node path per sequence, its bonus token
+ *                       and the tokens the round emits
+ *   ev_compact_kv       in-place move of the accepted nodes' K/V rows right after the prefix,
+ *                       so the next round sees prefix + accepted tokens contiguously (the pages
+ *                       name per-sequence acceptance lengths under continuous batching as the
+ *                       main integration difficulty: same article, "Current Limitation")
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is a DEVICE pointer owned by the caller; the library allocates
+ *     nothing and keeps no per-call state between calls (a small per-device cache of device
+ *     properties aside).  Calls are asynchronous on `stream` and never synchronize.
+ *   - Host-visible argument problems return an ev_status synchronously and launch nothing.
+ *   - Problems that live in device data (a malformed tree, a token outside the vocabulary, a
+ *     slot range outside the cache) are OR-ed into `*err_flag` (nullable device int32, never
+ *     cleared by the library) with the EV_DATA_* bits; the affected sequence is skipped.
+ *   - Trees: per sequence b, N_b nodes in topological order, node 0 the root (the token decided
+ *     last round, always accepted), parent[node_start[b] + 0] == -1 and
+ *     0 <= parent[node_start[b] + i] < i for i >= 1 (LOCAL indices).  1 <= N_b <= max_nodes
+ *     <= EV_MAX_NODES.
+ *   - KV cache: [total_slots][num_kv_heads][head_dim], contiguous.  Sequence b's prefix sits in
+ *     slots kv_start[b] .. kv_start[b]+prefix_len[b]-1 and the K/V of its tree node i have
+ *     already been written to slot kv_start[b] + prefix_len[b] + i.
+ *   - Q and the attention output: [total_nodes][num_q_heads][head_dim]; q head h reads KV head
+ *     h / (num_q_heads / num_kv_heads).
+ *   - Base pointers of q, k_cache, v_cache, out and logits must be 16-byte aligned.
+ */
+#ifndef EV_H_
+#define EV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EV_OK = 0,
+    EV_ERR_NULL = 1,      /* a required pointer is NULL */
+    EV_ERR_SHAPE = 2,     /* unsupported or inconsistent sizes */
+    EV_ERR_DTYPE = 3,     /* unsupported element type */
+    EV_ERR_ALIGN = 4,     /* a base pointer, stride or row size breaks the alignment rules */
+    EV_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the matching *_workspace_size() */
+    EV_ERR_DEVICE = 6,    /* the current device is not gfx950 */
+    EV_ERR_HIP = 7        /* a HIP runtime call or kernel launch failed */
+} ev_status;
+
+typedef enum { EV_BF16 = 0, EV_F32 = 1 } ev_dtype;
+
+/* Bits OR-ed into *err_flag for problems found in device data. */
+#define EV_DATA_BAD_PARENT 1 /* parent[0] != -1 or parent[i] outside [0, i) */
+#define EV_DATA_BAD_NODES 2  /* N_b = node_start[b+1] - node_start[b] outside [1, max_nodes] */
+#define EV_DATA_BAD_TOKEN 4  /* a compared draft token or a target token outside [0, vocab) */
+#define EV_DATA_BAD_SLOTS 8  /* kv_start / prefix_len negative or slots past total_slots */
+#define EV_DATA_BAD_PATH 16  /* accepted path not strictly increasing from node 0, or too long */
+
+#define EV_MAX_NODES 64
+#define EV_MAX_BATCH 2048
+
+/* Human-readable name of a status code (static string). */
+const char *ev_status_string(ev_status status);
+
+/* ---------------------------------------------------------------------------------------------
+ * ev_tree_attention
+ *
+ * For every sequence b, tree node i and q head h (KV head g = h / (Hq/Hkv)):
+ *   visible slots  S(i) = { s0 + t : 0 <= t < L }  U  { s0 + L + j : j ancestor of i or j == i }
+ *   out[i,h]       = sum_{s in S(i)} softmax_s( sm_scale * <q[i,h], k[s,g]> ) * v[s,g]
+ *   lse[i,h]       = natural-log log-sum-exp of the scaled scores
+ * with s0 = kv_start[b], L = prefix_len[b] (L = 0 allowed).  A node never sees its siblings,
+ * its descendants or other branches.  Arithmetic: bf16 operands on the matrix cores (fp32
+ * inputs are rounded to bf16 first), fp32 accumulation and softmax, probabilities rounded to
+ * bf16 for the value product; out has the input element type.
+ *
+ *   q, k_cache, v_cache   dtype elements, layouts above (read only)
+ *   out                   [total_nodes][num_q_heads][head_dim], written for valid sequences
+ *   lse                   [total_nodes][num_q_heads] fp32, nullable
+ *   node_start            int32 [batch+1], node_start[0] == 0, node_start[batch] == total_nodes
+ *   parent                int32 [total_nodes], local parent indices (see the tree rules)
+ *   kv_start, prefix_len  int32 [batch]
+ *   max_nodes             upper bound of N_b, 1..EV_MAX_NODES
+ *   total_slots           slots in the cache (bounds check)
+ *   head_dim              64 or 128;  num_q_heads % num_kv_heads == 0
+ *   workspace             >= ev_tree_attention_workspace_size(...) bytes, ZEROED ONCE by the
+ *                         caller before its first use; every call leaves it reusable (its
+ *                         counters are back at zero when the call's work completes).  Calls
+ *                         that share one workspace must be ordered (same stream).
+ * Data errors (EV_DATA_BAD_PARENT / _NODES / _SLOTS): the sequence's rows are not written.
+ * -------------------------------------------------------------------------------------------*/
+size_t ev_tree_attention_workspace_size(int32_t batch, int32_t max_nodes, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim);
+
+ev_status ev_tree_attention(const void *q, const void *k_cache, const void *v_cache, void *out, float *lse,
+                            const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                            const int32_t *prefix_len, int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                            int64_t total_slots, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            ev_dtype dtype, float sm_scale, void *workspace, size_t workspace_bytes,
+                            int32_t *err_flag, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ev_node_argmax
+ *
+ * target_token[r] = the LOWEST index v in [0, vocab) holding the maximum of logits row r (the
+ * target's greedy token at temperature 0).  +0 and -0 compare equal; a NaN ranks above every
+ * number, so a row's first NaN wins.  max_value[r] (nullable, fp32) receives that maximum.
+ *
+ *   logits       dtype elements, row r starts at logits + r * row_stride (elements);
+ *                row_stride >= vocab and row_stride * element size must be a multiple of 16 B
+ *   workspace    >= ev_node_argmax_workspace_size(num_rows, vocab) bytes (may be 0 bytes, then
+ *                NULL is fine), zeroed once before first use, left reusable by every call.
+ * -------------------------------------------------------------------------------------------*/
+size_t ev_node_argmax_workspace_size(int32_t num_rows, int32_t vocab);
+
+ev_status ev_node_argmax(const void *logits, ev_dtype dtype, int64_t row_stride, int32_t num_rows, int32_t vocab,
+                         int32_t *target_token, float *max_value, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ev_greedy_accept
+ *
+ * Per sequence b (one wavefront each): accepted(0) = true and, for i >= 1,
+ * accepted(i) = accepted(parent(i)) and draft_token[i] == target_token[parent(i)].
+ * i* = the accepted node of greatest depth, lowest index among equal depths.
+ *   accept_len[b]      depth(i*) + 1  (root included = tokens emitted this round)
+ *   accept_path[b, :]  the ancestors of i* root first (local indices), then -1 padding
+ *   bonus_token[b]     target_token[i*]  (the target's own token after the accepted path)
+ *   out_tokens[b, :]   draft tokens of accept_path[1..len-1], then the bonus, then -1 padding
+ * The root's draft token is never compared.  node_start/parent/draft_token/target_token are as in
+ * ev_tree_attention (total_nodes entries); all arrays int32; the [B, max_nodes] outputs are
+ * row-major.  Data errors (EV_DATA_BAD_PARENT / _NODES / _TOKEN): accept_len = 0, bonus = -1,
+ * path and tokens all -1 for that sequence.
+ * -------------------------------------------------------------------------------------------*/
+ev_status ev_greedy_accept(const int32_t *node_start, const int32_t *parent, const int32_t *draft_token,
+                           const int32_t *target_token, int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                           int32_t vocab,
+                           int32_t *accept_len, int32_t *accept_path, int32_t *bonus_token, int32_t *out_tokens,
+                           int32_t *err_flag, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ev_compact_kv
+ *
+ * In place, for every layer l, KV head and 0 <= d < len = accept_len[b]:
+ *   slot s0+L+d of layer l  <-  the bytes slot s0+L+path[d] held BEFORE the call
+ * (s0 = kv_start[b], L = prefix_len[b], path = accept_path[b, :]); every other byte is left
+ * unchanged (slots L+len .. L+N-1 keep stale rows).  new_len[b] = L + len.  A sequence with
+ * len <= 0 is left alone and gets new_len = L.  The path must start at 0 and strictly
+ * increase (ev_greedy_accept guarantees it), which makes the move safe in place.
+ *
+ *   k_cache, v_cache     layer l's cache starts at base + l * layer_stride_bytes; each layer
+ *                        is [total_slots][num_kv_heads][head_dim] of elem_bytes (2 or 4)
+ *                        elements; one slot's row (num_kv_heads*head_dim*elem_bytes bytes) and
+ *                        layer_stride_bytes must be multiples of 16, base pointers 16-aligned
+ *   new_len              int32 [batch]; must not alias prefix_len
+ * Data errors (EV_DATA_BAD_PATH / _SLOTS): that sequence is left alone, new_len = L.
+ * -------------------------------------------------------------------------------------------*/
+ev_status ev_compact_kv(void *k_cache, void *v_cache, int32_t elem_bytes, int32_t num_layers,
+                        int64_t layer_stride_bytes, const int32_t *kv_start, const int32_t *prefix_len,
+                        const int32_t *accept_len, const int32_t *accept_path, int32_t batch, int32_t max_nodes,
+                        int64_t total_slots, int32_t num_kv_heads, int32_t head_dim, int32_t *new_len,
+                        int32_t *err_flag, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EV_H_ */

@@ -1,0 +1,112 @@
+"""Helpers of the GPU parity tests: move a synthetic workload to the device, run the library,
+run the oracle on the same host arrays, compare (test infrastructure)."""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+
+import oracle
+from draft_tree_verification_amd import synth
+from draft_tree_verification_amd.synth import BF16
+
+# The attention bar: |gpu - oracle| <= ATOL + RTOL * |oracle| elementwise.
+ATOL, RTOL = 2e-2, 1e-2
+# Tighter bound derived from the kernel's arithmetic (bf16 probabilities: relative error 2^-9 per
+# weight, plus the bf16 rounding of the output): |gpu - oracle| <= 2^-7 * max|V| for bf16 inputs.
+TIGHT_FRAC = 2.0 ** -7
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(arr, dtype_code=None, device="cuda"):
+    import torch
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def to_host(t) -> np.ndarray:
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def widen(x: np.ndarray) -> np.ndarray:
+    return (synth.bf16_bits_to_f32(x) if x.dtype == np.uint16 else x).astype(np.float64)
+
+
+def dev_workload(w, device="cuda"):
+    import torch
+    d = {k: to_dev(getattr(w, k), device=device) for k in ("q", "k", "v", "logits")}
+    for k in ("node_start", "parent", "kv_start", "prefix_len", "draft"):
+        d[k] = torch.from_numpy(np.ascontiguousarray(getattr(w, k), dtype=np.int32)).to(device)
+    return d
+
+
+@functools.lru_cache(maxsize=2)
+def cached_config(name: str):
+    log(f"[gen] workload {name}")
+    return synth.make_config(name)
+
+
+def gpu_attention(w, d, sm_scale=None, err=None):
+    from draft_tree_verification_amd import ev
+    out, lse, _ = ev.tree_attention(d["q"], d["k"], d["v"], d["node_start"], d["parent"], d["kv_start"],
+                                    d["prefix_len"], max_nodes=max(w.max_nodes, 1),
+                                    sm_scale=w.sm_scale if sm_scale is None else sm_scale, err_flag=err)
+    return out, lse
+
+
+def oracle_attention(w, sm_scale=None):
+    return oracle.tree_attention(w.q, w.k, w.v, w.node_start, w.parent, w.kv_start, w.prefix_len,
+                                 num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                                 sm_scale=w.sm_scale if sm_scale is None else sm_scale, total_slots=w.total_slots,
+                                 max_nodes=max(w.max_nodes, 1))
+
+
+def oracle_rows(w, rows, sm_scale=None):
+    return oracle.tree_attention_rows(w.q, w.k, w.v, w.node_start, w.parent, w.kv_start, w.prefix_len, rows,
+                                      num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                                      head_dim=w.head_dim, sm_scale=w.sm_scale if sm_scale is None else sm_scale,
+                                      total_slots=w.total_slots, max_nodes=max(w.max_nodes, 1))
+
+
+def check_attention(gpu_out, ref_out, gpu_lse=None, ref_lse=None, vmax=None, what="", tight=True):
+    """Apply the bar (and the tighter arithmetic bound); return a dict of error statistics."""
+    g = widen(gpu_out).reshape(ref_out.shape)
+    err = np.abs(g - ref_out)
+    ok = err <= ATOL + RTOL * np.abs(ref_out)
+    stats = {"max_abs": float(err.max()) if err.size else 0.0,
+             "rms": float(np.sqrt((err ** 2).mean())) if err.size else 0.0}
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    assert ok.all(), f"{what}: {int((~ok).sum())} elements outside 2e-2 + 1e-2*|ref| (max abs {stats['max_abs']})"
+    if tight and vmax is not None:
+        assert stats["max_abs"] <= TIGHT_FRAC * vmax, f"{what}: max abs {stats['max_abs']} > 2^-7 * {vmax}"
+    if gpu_lse is not None:
+        le = np.abs(np.asarray(gpu_lse, np.float64).reshape(ref_lse.shape) - ref_lse)
+        stats["lse_max_abs"] = float(le.max()) if le.size else 0.0
+        assert stats["lse_max_abs"] <= 1e-2, f"{what}: lse error {stats['lse_max_abs']}"
+    log(f"[attn] {what}: {stats}")
+    return stats
+
+
+def sample_rows(w, n_rows: int, seed: int = 0) -> np.ndarray:
+    """(global node, q head) pairs: every node of the first and last sequence, plus random rows."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for b in {0, w.batch - 1}:
+        for i in range(int(w.node_start[b]), int(w.node_start[b + 1])):
+            for h in sorted({0, w.num_q_heads - 1, int(rng.integers(w.num_q_heads))}):
+                rows.append((i, h))
+    T = w.total_nodes
+    while len(rows) < n_rows:
+        rows.append((int(rng.integers(T)), int(rng.integers(w.num_q_heads))))
+    return np.array(rows, dtype=np.int32)

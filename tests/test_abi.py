@@ -1,0 +1,89 @@
+"""The C-ABI library loads and exports every entry point include/ev.h declares; host-side argument
+checks and workspace sizing (no kernel is launched here: these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from draft_tree_verification_amd import build, ev
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ev.LIB_PATH):
+        build.build()
+    return ev.load()
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "ev.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^[a-z_ ]*?\**\s*(ev_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declarations_match_binding():
+    names = declared_functions()
+    assert names == sorted(ev.EXPORTS), names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libev.so does not export {name}"
+
+
+def test_no_cpu_fallback_symbols(lib):
+    # the binding is a plain loader of the HIP library: nothing in it imports the oracle
+    src = open(ev.__file__).read()
+    assert "oracle" not in src.replace("no non-HIP fallback", "")
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        assert ev.ev_status_string(code).startswith(ev.STATUS[code])
+    assert "UNKNOWN" in ev.ev_status_string(99)
+
+
+def test_workspace_sizes(lib):
+    s = ev.ev_tree_attention_workspace_size(8, 16, 40, 8, 128)
+    assert s > 0 and s % 256 == 0
+    assert ev.ev_tree_attention_workspace_size(512, 4, 40, 8, 128) > 0
+    assert ev.ev_tree_attention_workspace_size(8, 65, 40, 8, 128) == 0      # too many nodes
+    assert ev.ev_tree_attention_workspace_size(8, 16, 40, 7, 128) == 0      # Hq % Hkv != 0
+    assert ev.ev_tree_attention_workspace_size(8, 16, 40, 8, 96) == 0       # head_dim
+    assert ev.ev_node_argmax_workspace_size(4096, 151936) == 0             # one workgroup per row
+    assert ev.ev_node_argmax_workspace_size(16, 151936) >= 16 * 12          # split rows need keys
+    assert ev.ev_node_argmax_workspace_size(16, 0) == 0
+
+
+def test_host_argument_checks_need_no_gpu(lib):
+    # null pointers, bad shapes and bad dtypes are refused before any HIP call
+    P = 0x1000
+    assert ev.ev_tree_attention(None, P, P, P, None, P, P, P, P, 1, 4, 4, 100, 8, 2, 64, 0, 0.1, P, 1 << 30,
+                                None, None) == 1
+    assert ev.ev_tree_attention(P, P, P, P, None, P, P, P, P, 1, 4, 65, 100, 8, 2, 64, 0, 0.1, P, 1 << 30,
+                                None, None) == 2
+    assert ev.ev_tree_attention(P, P, P, P, None, P, P, P, P, 1, 4, 4, 100, 8, 2, 64, 5, 0.1, P, 1 << 30,
+                                None, None) == 3
+    assert ev.ev_tree_attention(P + 2, P, P, P, None, P, P, P, P, 1, 4, 4, 100, 8, 2, 64, 0, 0.1, P, 1 << 30,
+                                None, None) == 4
+    assert ev.ev_tree_attention(P, P, P, P, None, P, P, P, P, 1, 4, 4, 100, 8, 2, 64, 0, 0.1, P, 16,
+                                None, None) == 5
+    assert ev.ev_node_argmax(None, 0, 8, 1, 8, P, None, None, 0, None) == 1
+    assert ev.ev_node_argmax(P, 0, 4, 1, 8, P, None, None, 0, None) == 2        # stride < vocab
+    assert ev.ev_node_argmax(P, 0, 12, 1, 8, P, None, None, 0, None) == 4       # 24-byte rows
+    assert ev.ev_node_argmax(P, 2, 8, 1, 8, P, None, None, 0, None) == 3
+    assert ev.ev_node_argmax(P, 0, 151936, 16, 151936, P, None, None, 0, None) == 5
+    assert ev.ev_greedy_accept(P, P, P, None, 1, 4, 4, 10, P, P, P, P, None, None) == 1
+    assert ev.ev_greedy_accept(P, P, P, P, 1, 4, 65, 10, P, P, P, P, None, None) == 2
+    assert ev.ev_compact_kv(P, P, 3, 1, 4096, P, P, P, P, 1, 4, 16, 8, 128, P + 64, None, None) == 3
+    assert ev.ev_compact_kv(P, P, 2, 1, 4096, P, P, P, P, 1, 4, 16, 1, 4, P + 64, None, None) == 4  # 8-byte rows
+    assert ev.ev_compact_kv(P, P, 2, 1, 100, P, P, P, P, 1, 4, 16, 8, 128, P + 64, None, None) == 2
+    assert ev.ev_compact_kv(P, P, 2, 1, 1 << 20, P, P, P, P, 1, 4, 16, 8, 128, P, None, None) == 2  # alias
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        ev.load(str(tmp_path / "libev.so"))

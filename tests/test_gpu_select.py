@@ -1,0 +1,190 @@
+"""GPU parity of ev_node_argmax, ev_greedy_accept and ev_compact_kv: bit-exact against the oracle."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from draft_tree_verification_amd import synth
+from draft_tree_verification_amd.synth import BF16, F32
+
+from . import bruteforce as bf
+from . import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _gpu_argmax(raw, vocab=None):
+    import torch
+    from draft_tree_verification_amd import ev
+    t = gu.to_dev(raw)
+    tgt, mx, _ = ev.node_argmax(t, vocab=vocab)
+    torch.cuda.synchronize()
+    return tgt.cpu().numpy(), mx.cpu().numpy()
+
+
+def _check_argmax(raw, vocab=None, what=""):
+    tgt, mx = _gpu_argmax(raw, vocab)
+    stride = raw.shape[1]
+    ref, ref_mx = oracle.node_argmax(raw, vocab=vocab or stride, row_stride=stride)
+    bad = np.nonzero(tgt != ref)[0]
+    assert bad.size == 0, f"{what}: rows {bad[:10]} gpu {tgt[bad[:10]]} oracle {ref[bad[:10]]}"
+    same = (mx == ref_mx.astype(np.float32)) | (np.isnan(mx) & np.isnan(ref_mx))
+    assert same.all(), f"{what}: max values differ"
+    gu.log(f"[argmax] {what}: {raw.shape[0]} rows bit-exact")
+
+
+@pytest.mark.parametrize("name", ["tiny", "c1x4k", "c8"])
+def test_argmax_workloads(name):
+    gu.log(f"[case] argmax {name}")
+    _check_argmax(gu.cached_config(name).logits, what=name)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32])
+@pytest.mark.parametrize("rows,vocab,stride,spread", [(3, 151936, 151936, 2), (40, 1001, 1008, 1),
+                                                      (1500, 4096, 4096, 3), (7, 5, 8, 1), (64, 20000, 20008, 0)])
+def test_argmax_ties_and_shapes(dtype, rows, vocab, stride, spread):
+    """Tie-heavy rows (small integer values) over split and unsplit rows, ragged tails, strides."""
+    gu.log(f"[case] argmax ties dtype={dtype} rows={rows} vocab={vocab}")
+    rng = np.random.default_rng(rows + vocab)
+    x = rng.integers(-spread, spread + 1, (rows, stride)).astype(np.float32)
+    x[:, vocab:] = 1e30  # beyond the vocabulary: never counted
+    raw = x if dtype == F32 else synth.f32_to_bf16_bits(x)
+    _check_argmax(raw, vocab=vocab, what=f"ties {rows}x{vocab}")
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_argmax_special_values(dtype):
+    gu.log(f"[case] argmax special values dtype={dtype}")
+    nan, inf = float("nan"), float("inf")
+    V = 5000
+    rows = np.zeros((9, V), np.float32)
+    rows[0, :] = -0.0; rows[0, 3000] = 0.0                     # -0 == +0: index 0
+    rows[1, :] = -1.0; rows[1, 4999] = -0.0; rows[1, 2] = 0.0  # zeros are the max: index 2
+    rows[2, :] = 1.0; rows[2, 17] = inf; rows[2, 4000] = inf   # first +inf
+    rows[3, :] = -inf                                          # all -inf: index 0
+    rows[4, :] = 3.0; rows[4, 2500] = nan; rows[4, 100] = -nan  # first NaN (any sign) wins
+    rows[5, :] = 2.0; rows[5, 4999] = nan                      # NaN in the ragged tail region
+    rows[6, :] = np.arange(V, dtype=np.float32) * -1           # max at 0
+    rows[7, :] = np.arange(V, dtype=np.float32)                # max at V-1
+    rows[8, :] = 1e-40; rows[8, 77] = 2e-40                    # subnormals (bf16 keeps few bits)
+    raw = rows if dtype == F32 else synth.f32_to_bf16_bits(rows)
+    _check_argmax(raw, what="special")
+    _check_argmax(np.ascontiguousarray(np.repeat(raw, 200, axis=0)), what="special x200")
+
+
+def _gpu_accept(node_start, parent, draft, target, max_nodes, vocab):
+    import torch
+    from draft_tree_verification_amd import ev
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = ev.greedy_accept(t(node_start), t(parent), t(draft), t(target), max_nodes=max_nodes, vocab=vocab,
+                           err_flag=err)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}, int(err.item())
+
+
+def _check_accept(node_start, parent, draft, target, max_nodes, vocab, what=""):
+    g, err = _gpu_accept(node_start, parent, draft, target, max_nodes, vocab)
+    r = oracle.greedy_accept(node_start, parent, draft, target, max_nodes, vocab)
+    for k in ("accept_len", "accept_path", "bonus", "out_tokens"):
+        assert np.array_equal(g[k], r[k]), f"{what}: {k} differs"
+    flags = int(np.bitwise_or.reduce(r["seq_err"])) if len(r["seq_err"]) else 0
+    assert err == flags, f"{what}: err flag {err} vs oracle {flags}"
+    gu.log(f"[accept] {what}: {len(node_start) - 1} sequences bit-exact")
+    return g
+
+
+def test_accept_golden_cases():
+    gu.log("[case] accept golden")
+    cases = bf.load_cases(os.path.join(GOLDEN, "accept_cases.txt"))
+    ns = np.cumsum([0] + [len(c[1]) for c in cases])
+    g = _check_accept(ns, np.concatenate([c[1] for c in cases]), np.concatenate([c[2] for c in cases]),
+                      np.concatenate([c[3] for c in cases]), 8, 1000, what="golden")
+    for b, c in enumerate(cases):
+        assert g["accept_len"][b] == c[4][0] and list(g["accept_path"][b][:c[4][0]]) == c[5], c[0]
+
+
+def test_accept_random_dense_matches():
+    gu.log("[case] accept random")
+    rng = np.random.default_rng(11)
+    B = 700
+    trees = [synth.random_tree(rng, int(rng.integers(1, 65)), int(rng.integers(1, 64))) for _ in range(B)]
+    ns = np.cumsum([0] + [len(t) for t in trees])
+    T = int(ns[-1])
+    _check_accept(ns, np.concatenate(trees), rng.integers(0, 2, T), rng.integers(0, 2, T), 64, 2, what="random")
+
+
+@pytest.mark.parametrize("name", ["tiny", "c8", "c512"])
+def test_accept_workloads(name):
+    gu.log(f"[case] accept {name}")
+    w = gu.cached_config(name)
+    tgt, _ = oracle.node_argmax(w.logits)
+    _check_accept(w.node_start, w.parent, w.draft, tgt, w.max_nodes, w.vocab, what=name)
+
+
+def test_accept_data_errors():
+    gu.log("[case] accept data errors")
+    _check_accept([0, 3, 5, 5, 8, 9], [-1, 0, 2, -1, 0, -1, 0, 1, -1], [0, 1, 2, 0, 1, 0, 1, 1000, 3],
+                  [1, 1, 1, 1, 1, 1, 1, 1, 1000], 4, 1000, what="errors")
+
+
+def _gpu_compact(k, v, kv_start, prefix_len, lens, path):
+    import torch
+    from draft_tree_verification_amd import ev
+    kd, vd = gu.to_dev(k), gu.to_dev(v)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nl = ev.compact_kv(kd, vd, t(kv_start), t(prefix_len), t(lens), t(path), err_flag=err)
+    torch.cuda.synchronize()
+    return gu.to_host(kd), gu.to_host(vd), nl.cpu().numpy(), int(err.item())
+
+
+def test_compact_golden_cases():
+    gu.log("[case] compact golden")
+    for name, L, N, ln, path, expect, new_len in bf.load_cases(os.path.join(GOLDEN, "compact_cases.txt")):
+        L, N, ln = L[0], N[0], ln[0]
+        slots = L + N
+        # 4-byte rows of 4 values each: [layers=1, slots, heads=1, dim=4]
+        k = np.repeat(np.arange(slots, dtype=np.float32), 4).reshape(1, slots, 1, 4)
+        v = k + 1000
+        p = np.full((1, N), -1, np.int32)
+        p[0, :ln] = path
+        k2, v2, nl, err = _gpu_compact(k, v, [0], [L], [ln], p)
+        assert err == 0 and nl[0] == new_len[0], name
+        assert list(k2[0, :, 0, 0].astype(int)) == expect and list((v2[0, :, 0, 3] - 1000).astype(int)) == expect
+
+
+@pytest.mark.parametrize("dtype", [np.uint16, np.float32])
+def test_compact_random_layers(dtype):
+    gu.log(f"[case] compact random {dtype}")
+    rng = np.random.default_rng(4)
+    B, H, D, layers, maxn = 37, 8, 128, 3, 64
+    Ls = rng.integers(0, 50, B)
+    ns = rng.integers(1, maxn + 1, B)
+    starts = np.concatenate([[0], np.cumsum(Ls + ns)])[:-1]
+    total = int(starts[-1] + Ls[-1] + ns[-1])
+    k = rng.integers(0, 60000, (layers, total, H, D)).astype(dtype)
+    v = rng.integers(0, 60000, (layers, total, H, D)).astype(dtype)
+    lens = np.array([rng.integers(0, n + 1) for n in ns])
+    path = np.full((B, maxn), -1, np.int32)
+    for b in range(B):
+        if lens[b] > 0:
+            path[b, :lens[b]] = np.sort(np.concatenate([[0], rng.choice(np.arange(1, ns[b]), lens[b] - 1,
+                                                                     replace=False)]))
+    path[0, :5] = [0, 1, 3, 4, -1]; lens[0] = 4     # the overlap case
+    k2, v2, nl, err = _gpu_compact(k, v, starts, Ls, lens, path)
+    rk, rv, rnl, rerr = oracle.compact_kv(k, v, starts, Ls, lens, path, num_layers=layers, total_slots=total,
+                                          num_kv_heads=H, head_dim=D)
+    assert err == 0 and (rerr == 0).all()
+    assert np.array_equal(nl, rnl)
+    assert np.array_equal(k2, rk) and np.array_equal(v2, rv)
+
+
+def test_compact_data_errors():
+    gu.log("[case] compact data errors")
+    k = np.arange(10 * 8, dtype=np.float32).reshape(1, 10, 1, 8)
+    bad = np.array([[1, 2, -1], [0, 2, 1], [0, 1, 2], [0, 1, 2]], np.int32)
+    k2, _, nl, err = _gpu_compact(k, k.copy(), [0, 0, 6, 0], [2, 2, 2, 1], [2, 3, 3, 0], bad)
+    assert err == 16 | 8 and list(nl) == [2, 2, 2, 1] and np.array_equal(k2, k)
