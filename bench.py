@@ -1,0 +1,280 @@
+"""Benchmark of the draft-tree verification step on one MI355X.
+
+One step = the whole hot path over one batch: tree-masked GQA attention, per-node argmax, greedy
+acceptance and in-place KV compaction (four launches on one stream).  Inputs are seeded synthetic
+data already resident in HBM; several identical input sets sit at different addresses and the
+steps rotate over them, so the 256 MB Infinity Cache cannot serve one step's reads from the
+previous step's.  Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload c8|c128k|c512|c1x4k|tiny] [--no-cpu]
+  python bench.py --copy-calibration     (a plain device copy of known size, for counter scaling)
+
+The default workload is the 8-sequence batch (prefix lengths uniform in [1024, 8192], 16-node
+trees, 40 q heads / 8 KV heads, head_dim 128, bf16 KV, vocab 151936).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import re
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MALL_BYTES = 256 << 20
+HBM_PEAK_GBPS = 8000.0
+METRIC = "verified tree-tokens/s + accepted tokens/s; KV-read HBM GB/s as % of peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="c8")
+    p.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0: enough to defeat the MALL)")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--copy-calibration", action="store_true")
+    return p.parse_args()
+
+
+def copy_calibration():
+    """A device-to-device copy of exactly 1 GiB, repeated 5 times: the reference for counter scaling."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+
+
+def lscpu_model() -> str:
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True).stdout
+        m = re.search(r"Model name:\s*(.+)", out)
+        return m.group(1).strip() if m else platform.processor()
+    except OSError:
+        return platform.processor()
+
+
+def counters_for(kernel_src: str, workload: str):
+    """HBM traffic per attention launch from the committed counter summary, if it was taken on
+    the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"tree_attention_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        m = re.match(r"\s*([a-z_]+)\s*[:=]\s*(\S+)", line)
+        if m:
+            vals[m.group(1)] = m.group(2)
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    if vals.get("kernel_source_sha") != sha or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(w, target_seconds: float):
+    """The oracle (plain C, OpenMP over rows) on the host cores, on a bounded sample of the workload:
+    whole steps over the first sequences, repeated until about target_seconds of CPU time."""
+    import numpy as np
+    import oracle
+    lib = oracle.load()
+    threads = oracle.num_threads(lib)
+    # sample: the first sequences whose oracle attention fits one pass in about a quarter of the budget
+    flops_per_s = 1.0e9 * threads  # rough fp64 plain-loop rate, only used to size the sample
+    B = w.batch
+    per_seq = [4.0 * (int(w.prefix_len[b]) + int(w.nodes_per_seq[b])) * w.head_dim * w.num_q_heads *
+               int(w.nodes_per_seq[b]) for b in range(B)]
+    nb, acc = 0, 0.0
+    while nb < B and (acc + per_seq[nb]) / flops_per_s < target_seconds / 4:
+        acc += per_seq[nb]
+        nb += 1
+    nb = max(nb, 1)
+    s_end = int(w.node_start[nb])
+    slot_end = int(w.kv_start[nb - 1] + w.prefix_len[nb - 1] + w.nodes_per_seq[nb - 1])
+    q, k, v = w.q[:s_end], w.k[:slot_end], w.v[:slot_end]
+    ns, par, ks, pl = w.node_start[:nb + 1], w.parent[:s_end], w.kv_start[:nb], w.prefix_len[:nb]
+    logits, draft = w.logits[:s_end], w.draft[:s_end]
+    reps, tokens, t0 = 0, 0, time.perf_counter()
+    while True:
+        oracle.tree_attention(q, k, v, ns, par, ks, pl, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                              head_dim=w.head_dim, sm_scale=w.sm_scale, total_slots=slot_end,
+                              max_nodes=w.max_nodes, lib=lib)
+        tgt, _ = oracle.node_argmax(logits, lib=lib)
+        acc_r = oracle.greedy_accept(ns, par, draft, tgt, w.max_nodes, w.vocab, lib=lib)
+        oracle.compact_kv(k[None], v[None], ks, pl, acc_r["accept_len"], acc_r["accept_path"], num_layers=1,
+                          total_slots=slot_end, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, lib=lib)
+        reps += 1
+        tokens += s_end
+        el = time.perf_counter() - t0
+        if el >= target_seconds or reps >= 1000:
+            break
+    return {"value": tokens / el, "unit": "tree-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nb} of {B} sequences ({s_end} tree nodes), whole step x{reps} in {el:.1f} s",
+            "cpu_model": lscpu_model()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the verification step "
+              "shards by sequence or KV head with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    from draft_tree_verification_amd import ev, synth
+
+    torch.cuda.set_device(0)
+    w = synth.make_config(args.workload)
+    print(f"[bench] workload {args.workload}: {synth.describe(w)}", file=sys.stderr, flush=True)
+    kv_bytes = w.kv_bytes()
+    set_bytes = kv_bytes + w.logits.nbytes + w.q.nbytes
+    nsets = args.sets or max(1, math.ceil(2 * MALL_BYTES / set_bytes))
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    meta = {n: dev(getattr(w, n).astype(np.int32)) for n in ("node_start", "parent", "kv_start", "prefix_len",
+                                                             "draft")}
+    host = {n: dev(getattr(w, n)) for n in ("q", "k", "v", "logits")}
+    sets = [host] + [{n: t.clone() for n, t in host.items()} for _ in range(nsets - 1)]
+    print(f"[bench] {nsets} input sets of {set_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+
+    B, T, maxn = w.batch, w.total_nodes, w.max_nodes
+    Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_dim
+    dt = ev.EV_BF16 if w.dtype == synth.BF16 else ev.EV_F32
+    esz = w.elem_bytes
+    i32 = lambda n: torch.empty(n, dtype=torch.int32, device="cuda")
+    out = [torch.empty_like(s["q"]) for s in sets]
+    lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    target, maxv = i32(T), torch.empty(T, dtype=torch.float32, device="cuda")
+    acc_len, bonus, new_len = i32(B), i32(B), i32(B)
+    acc_path, out_tok = i32((B, maxn)), i32((B, maxn))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    aws = ev.Workspace(ev.ev_tree_attention_workspace_size(B, maxn, Hq, Hkv, D), "cuda")
+    gws = ev.Workspace(max(ev.ev_node_argmax_workspace_size(T, w.vocab), 256), "cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    lib = ev.load()
+    p = lambda t: t.data_ptr()
+    m = {n: p(t) for n, t in meta.items()}
+    calls = []
+    for i, s in enumerate(sets):
+        calls.append((
+            (p(s["q"]), p(s["k"]), p(s["v"]), p(out[i]), p(lse), m["node_start"], m["parent"], m["kv_start"],
+             m["prefix_len"], B, T, maxn, w.total_slots, Hq, Hkv, D, dt, w.sm_scale, aws.ptr, aws.nbytes,
+             p(err), stream),
+            (p(s["logits"]), dt, w.vocab, T, w.vocab, p(target), p(maxv), gws.ptr, gws.nbytes, stream),
+            (m["node_start"], m["parent"], m["draft"], p(target), B, T, maxn, w.vocab, p(acc_len), p(acc_path),
+             p(bonus), p(out_tok), p(err), stream),
+            (p(s["k"]), p(s["v"]), esz, 1, w.total_slots * Hkv * D * esz, m["kv_start"], m["prefix_len"],
+             p(acc_len), p(acc_path), B, maxn, w.total_slots, Hkv, D, p(new_len), p(err), stream)))
+    f_attn, f_arg, f_acc, f_cmp = lib.ev_tree_attention, lib.ev_node_argmax, lib.ev_greedy_accept, lib.ev_compact_kv
+
+    def step(c, ev0=None, ev1=None):
+        if ev0 is not None:
+            ev0.record()
+        r = f_attn(*c[0])
+        if ev1 is not None:
+            ev1.record()
+        r |= f_arg(*c[1]) | f_acc(*c[2]) | f_cmp(*c[3])
+        return r
+
+    for i in range(args.warmup):
+        if step(calls[i % nsets]):
+            raise RuntimeError("a launch failed during warmup")
+    torch.cuda.synchronize()
+    if int(err.item()):
+        raise RuntimeError(f"data error flag {int(err.item())}")
+
+    K = args.steps
+    a0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    a1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    rc = 0
+    for i in range(K):
+        rc |= step(calls[i % nsets], a0[i], a1[i])
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    if rc:
+        raise RuntimeError("a launch failed in the timed region")
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / K
+    attn_ms = sum(a0[i].elapsed_time(a1[i]) for i in range(K)) / K
+
+    # per-kernel breakdown (separate pass, not part of the timed region)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    fns = (f_attn, f_arg, f_acc, f_cmp)
+    for i in range(K):
+        c = calls[i % nsets]
+        for j in range(4):
+            evs[i][j].record()
+            fns[j](*c[j])
+        evs[i][4].record()
+    torch.cuda.synchronize()
+    kernel_ms = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K
+                 for j, n in enumerate(("tree_attention", "node_argmax", "greedy_accept", "compact_kv"))}
+
+    acc_sum = int(acc_len.sum().item())
+    tree_tps = T / (ms_step / 1e3)
+    achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
+    traffic = counters_for(os.path.join(ROOT, "draft_tree_verification_amd", "csrc", "ev_attention.hip"),
+                           args.workload)
+    rec = {
+        "metric": METRIC,
+        "value": round(tree_tps, 1),
+        "unit": "tree-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == synth.BF16 else "f32",
+        "data": "synthetic (seeded; shapes of the workload, no dataset or weights)",
+        "config": dict(synth.describe(w), input_sets=nsets, kv_bytes=kv_bytes),
+        "accepted_tokens_per_s": round(acc_sum / (ms_step / 1e3), 1),
+        "accept_len_mean": acc_sum / B,
+        "kv_read_gbps": round(achieved, 1),
+        "kv_read_pct_of_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
+        "argmax_gbps": round(w.logits.nbytes / (kernel_ms["node_argmax"] * 1e-3) / 1e9, 1),
+        "wall_s_timed": round(t_wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "tree_attention", "attention_ms": round(attn_ms, 5),
+                     "algorithmic_bytes_per_launch": kv_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        del sets, out
+        torch.cuda.empty_cache()
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -146,21 +146,20 @@ __global__ __launch_bounds__(kThreads) void node_argmax_kernel(const ArgmaxArgs 
         p = q > p ? q : p;
     }
     __shared__ unsigned long long s_red[kThreads / 64];
-    __shared__ int s_last;
     if ((tid & 63) == 0) s_red[tid >> 6] = p;
     __syncthreads();
     if (tid != 0) return;
     for (int w = 1; w < kThreads / 64; ++w) p = s_red[w] > p ? s_red[w] : p;
 
     if (a.splits > 1) {
-        atomicMax(a.keys + row, p);
-        __threadfence();
-        const int old = __hip_atomic_fetch_add(a.counters + row, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = old == a.splits - 1;
-        if (!s_last) return;
-        __threadfence();
-        p = atomicExch(a.keys + row, 0ull);
-        a.counters[row] = 0;
+        // all three are device-coherent atomics on the same path: the max lands before this
+        // workgroup's arrival is counted, and the last arriver's exchange sees every max
+        __hip_atomic_fetch_max(a.keys + row, p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ev::vm_wait();
+        const int old = ev::atomic_add_agent(a.counters + row, 1);
+        if (old != a.splits - 1) return;
+        p = __hip_atomic_exchange(a.keys + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.counters + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     const uint32_t key = static_cast<uint32_t>(p >> 32);
     a.target[row] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(p & 0xFFFFFFFFu));

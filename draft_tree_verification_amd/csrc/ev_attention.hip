@@ -11,20 +11,25 @@
 //   * Work unit = (sequence, row group, KV head).  A unit's rows are all (node, q-head-in-group)
 //     pairs of that KV head -- up to 80 rows -- so every K/V byte is read from HBM exactly once
 //     and shared by all N*G rows (the arithmetic intensity is N*G flop per byte).
-//   * Stream-K split: each unit's keys are cut into 32-key steps; all steps of all units are laid
-//     end to end and the grid's workgroups take equal contiguous ranges (ragged prefix lengths
-//     cost nothing in balance).  Workgroup ranges are mapped XCD-major so the pieces of one unit
-//     mostly land on one XCD's L2.
-//   * Inside a workgroup the four waves take steps round-robin (split-K across waves).  Per step
-//     a wave loads 32 keys of K straight into MFMA A-operand registers (16-byte loads, 256-byte
-//     rows), computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (Q staged once per piece in
-//     LDS), applies the ancestor mask only on steps that reach the tree slots, runs the online
-//     softmax in fp32 with exp2, and accumulates O^T = V^T P^T.  V is transposed through a
-//     wave-private LDS tile; the score layout already matches P^T's operand layout, so P needs
-//     no shuffle and the output rows sit on the same lanes as the softmax state.
-//   * The four waves merge through LDS in a fixed order; a unit covered by one workgroup is
-//     written directly, otherwise each piece writes (m, l, O) partials and the last-arriving
-//     workgroup of the unit merges them in workgroup order (deterministic).
+//   * Stream-K split: each unit's keys are cut into stages (64 keys for 80-row units, 32 keys
+//     otherwise); all stages of all units are laid end to end and the grid's workgroups take
+//     equal contiguous ranges (ragged prefix lengths cost nothing in balance).  Ranges are
+//     mapped XCD-major so the pieces of one unit mostly land on one XCD.
+//   * bf16 inputs stream HBM -> LDS with direct 16-byte loads (global_load_lds_dwordx4), three
+//     stages in flight, no register staging.  K and V rows keep their natural layout with the
+//     16-byte chunks XOR-swizzled per row: K operand reads are ds_read_b128 and the V^T operand
+//     comes from ds_read_b64_tr_b16 transpose reads, both bank-conflict free.  fp32 inputs go
+//     through registers (converted to bf16) into a padded K tile and a transposed V tile.
+//   * Four waves per workgroup.  Wave w owns 16-row tile w; an 80-row unit's fifth tile is split
+//     by keys, each wave taking a 16-key quarter of every stage with the K and V^T operands it
+//     has already read (16x16x16 MFMA for that quarter's PV), and the four quarter states are
+//     merged through LDS at the end of each piece.  S^T = K Q^T and O^T = V^T P^T run on
+//     v_mfma_f32_16x16x32_bf16; the online softmax is fp32 base-2 with the scale folded into the
+//     exponent's FMA; the ancestor mask is applied only on stages that reach the tree slots.  The
+//     score layout already matches P^T's operand layout, so P needs no shuffle.
+//   * A unit covered by one workgroup is written directly; otherwise each piece publishes (m, l,
+//     O) partials with device-coherent stores and pieces merge hierarchically (groups of 8,
+//     last arriver merges in fixed order: deterministic, no L2 flushes).
 #include <cmath>
 #include <mutex>
 
@@ -34,10 +39,11 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStep = 32;          // keys per wave step (the K extent of one 16x16x32 MFMA)
 constexpr int kMaxGrid = 512;      // workgroups per launch (bounds the partial-result slots)
 constexpr int kMaxRowTiles = 5;    // 16-row tiles per unit: at most 80 rows
-constexpr int kVtPitch = 72;       // bytes per row of a wave's V^T tile (32 keys + pad)
+constexpr int kFanIn = 8;          // pieces merged per group in the hierarchical merge
+constexpr int kMergeLevels = 3;    // 8^3 >= kMaxGrid pieces
+constexpr int kStages = 4;         // LDS stage buffers of the bf16 path: three stages in flight
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -53,76 +59,93 @@ struct AttnArgs {
     const int32_t *prefix_len;
     int64_t total_slots;
     int32_t batch, total_nodes, max_nodes, hq, hkv, group, row_groups;
-    float scale_log2;  // sm_scale * log2(e): scores live in the base-2 domain
-    int32_t *counters; // [batch * row_groups * hkv] arrival counters
+    float scale_log2;  // sm_scale * log2(e) > 0: scores live in the base-2 domain
+    int32_t *counters; // [kMergeLevels][2 * kMaxGrid] group arrival counters (per first-member slot)
     float *part;       // [2 * kMaxGrid] partial-result slots
     int32_t *err_flag;
 };
 
-template <int D, int RT>
+template <int D, int RT, bool F32IN>
 struct Layout {
+    static constexpr bool X5 = RT == 5;             // four full tiles + one split by keys
+    static constexpr int KST = X5 ? 64 : 32;        // keys per stage
     static constexpr int R = RT * 16;
-    static constexpr int QP = D + 8;     // bf16 per staged Q row (pad breaks bank aliasing)
-    static constexpr int OP = D + 4;     // floats per row of a merge buffer
-    static constexpr int kScan = EV_MAX_BATCH * 8;
-    static constexpr int kMisc = 64;
-    static constexpr int kQ = R * QP * 2;
-    static constexpr int kVt = kWaves * D * kVtPitch;
-    static constexpr int kMerge = 2 * R * OP * 4 + 2 * kWaves * R * 4;
-    static constexpr int kBody = (kQ + kVt) > kMerge ? (kQ + kVt) : kMerge;
-    static constexpr int kTotal = kScan + kMisc + kBody;
+    static constexpr int kScan = EV_MAX_BATCH * 4;  // int32 inclusive scan of per-sequence stages
+    static constexpr int kMisc = 32;                // wave sums and the last-arriver flag
+    // fp32 inputs: two register-staged buffers (K row-major padded, V transposed)
+    static constexpr int KP = 2 * D + 16;
+    static constexpr int VTP = 2 * KST + 8;
+    static constexpr int kK = KST * KP;
+    static constexpr int kVt = D * VTP;
+    // bf16 inputs: kStages buffers filled straight from HBM (K then V, rows XOR-swizzled)
+    static constexpr int kRowB = 2 * D;
+    static constexpr int kTensorB = KST * kRowB;
+    static constexpr int kStageBytes = F32IN ? kK + kVt : 2 * kTensorB;
+    static constexpr int kBuffers = F32IN ? 2 : kStages;
+    static constexpr int kTotal = kScan + kMisc + kBuffers * kStageBytes;
     static constexpr size_t kSlotFloats = (size_t)R * D + 2 * R;  // O [R][D], then m [R], l [R]
+    static_assert(!X5 || 4 * 16 * (D + 4) * 4 + 2 * 64 * 4 <= kBuffers * kStageBytes, "tile-4 merge space");
 };
 
-__device__ __forceinline__ int64_t shfl_up_i64(int64_t x, int o) {
-    const int lo = __shfl_up(static_cast<int>(x & 0xFFFFFFFF), o, 64);
-    const int hi = __shfl_up(static_cast<int>(x >> 32), o, 64);
-    return (static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo);
+template <int N>
+__device__ __forceinline__ void vm_wait_n() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Workgroup (logical index) whose step range contains step x: the largest w with
+// Workgroup barrier without a memory fence (ordering is explicit: counted vmcnt waits before it).
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Workgroup (logical index) whose stage range contains stage x: the largest w with
 // floor(w*S/P) <= x.
 __device__ __forceinline__ int wg_of(int64_t x, int64_t S, int P) {
     return static_cast<int>(((x + 1) * P - 1) / S);
 }
 
 template <int D, int RT, bool F32IN>
-__global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel(const AttnArgs a) {
-    using Lay = Layout<D, RT>;
+__device__ __forceinline__ void attention_body(const AttnArgs &a) {
+    using Lay = Layout<D, RT, F32IN>;
+    constexpr bool X5 = Lay::X5;
+    constexpr int KST = Lay::KST;
+    constexpr int U = KST / 16;                // 16-key sub-tiles per stage
+    constexpr int KC = KST / 32;               // 32-key halves per stage (PV MFMA extent)
+    constexpr int NW = kWaves;
+    constexpr int NT = kThreads;
     constexpr int R = Lay::R;
-    constexpr int QP = Lay::QP;
-    constexpr int OP = Lay::OP;
-    constexpr int KS = D / 32;          // k-steps of the QK^T contraction
-    constexpr int DT = D / 16;          // 16-wide d tiles of O^T
-    constexpr int CPR = D / 8;          // 8-element chunks per K/V row
-    constexpr int KG = 64 / CPR;        // key rows covered by one V load instruction
-    constexpr int NQ = kStep / (4 * KG);  // quads of 4 keys per lane per step
-    static_assert(NQ >= 1, "V load mapping");
+    constexpr int KS = D / 32;                 // k-steps of the QK^T contraction
+    constexpr int DT = D / 16;                 // 16-wide d tiles of O^T
+    constexpr int CPR = D / 8;                 // 8-element chunks per K/V row
+    constexpr int NTL = X5 ? 2 : 1;            // register tiles per wave: own tile (+ tile 4's quarter)
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::kTotal];
-    int64_t *s_cum = reinterpret_cast<int64_t *>(smem);
-    int64_t *s_wsum = reinterpret_cast<int64_t *>(smem + Lay::kScan);  // [kWaves]
-    int32_t *s_flag = reinterpret_cast<int32_t *>(smem + Lay::kScan + 32);
-    unsigned char *body = smem + Lay::kScan + Lay::kMisc;
-    uint16_t *s_q = reinterpret_cast<uint16_t *>(body);
-    float *s_oa = reinterpret_cast<float *>(body);
-    float *s_ob = s_oa + R * OP;
-    float *s_mw = s_ob + R * OP;
-    float *s_lw = s_mw + kWaves * R;
+    int32_t *s_cum = reinterpret_cast<int32_t *>(smem);
+    int32_t *s_misc = reinterpret_cast<int32_t *>(smem + Lay::kScan);
+    unsigned char *stage_buf = smem + Lay::kScan + Lay::kMisc;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // The wave index must be visibly uniform: every wave-dependent choice below (which tiles a
+    // wave owns, which key quarter it takes) then compiles to a scalar branch.  Under an
+    // EXEC-masked branch the compiler may drop the skip jump around a short block, and an MFMA
+    // in such a block still writes its accumulator when no lane is active.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15;
     const int lq = lane >> 4;
-    unsigned char *s_vt = body + Lay::kQ + wave * D * kVtPitch;
     const int G = a.group;
+    const float c2 = a.scale_log2;
 
-    // ---- schedule: per-sequence step counts and their inclusive scan (identical in every WG)
-    int64_t carry = 0;
-    for (int b0 = 0; b0 < a.batch; b0 += kThreads) {
+    // ---- schedule: per-sequence stage counts and their inclusive scan (identical in every WG)
+    int carry = 0;
+    for (int b0 = 0; b0 < a.batch; b0 += NT) {
         const int b = b0 + tid;
-        int64_t work = 0;
+        int work = 0;
         if (b < a.batch) {
             const int ns0 = a.node_start[b], ns1 = a.node_start[b + 1];
             const int n = ns1 - ns0;
@@ -135,32 +158,35 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel(const AttnA
             if (err) {
                 if (blockIdx.x == 0) ev::flag_error(a.err_flag, err);
             } else {
-                work = static_cast<int64_t>(a.hkv) * ((n * G + R - 1) / R) * ((L + n + kStep - 1) / kStep);
+                work = a.hkv * ((n * G + R - 1) / R) * ((L + n + KST - 1) / KST);
             }
         }
-        int64_t x = work;
+        int x = work;
         for (int o = 1; o < 64; o <<= 1) {
-            const int64_t y = shfl_up_i64(x, o);
+            const int y = __shfl_up(x, o, 64);
             if (lane >= o) x += y;
         }
-        if (lane == 63) s_wsum[wave] = x;
+        if (lane == 63) s_misc[wave] = x;
         __syncthreads();
-        int64_t wbase = 0, tot = 0;
-        for (int w = 0; w < kWaves; ++w) {
-            if (w < wave) wbase += s_wsum[w];
-            tot += s_wsum[w];
+        int wbase = 0, tot = 0;
+        for (int w = 0; w < NW; ++w) {
+            if (w < wave) wbase += s_misc[w];
+            tot += s_misc[w];
         }
         if (b < a.batch) s_cum[b] = carry + wbase + x;
         carry += tot;
         __syncthreads();
     }
     const int64_t S = carry;
-    const int P = gridDim.x;
-    const int wl = (P % 8 == 0) ? (blockIdx.x % 8) * (P / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int grid = gridDim.x;
+    const int wl = (grid % 8 == 0) ? (blockIdx.x % 8) * (grid / 8) + blockIdx.x / 8 : blockIdx.x;
+    // logical workgroups: never more than stages, so every logical range is non-empty
+    const int P = static_cast<int>(S < grid ? S : grid);
+    if (wl >= P) return;
     const int64_t begin = S * wl / P, end = S * (wl + 1) / P;
 
     for (int64_t pos = begin; pos < end;) {
-        // ---- locate the unit that holds step `pos`
+        // ---- locate the unit that holds stage `pos`
         int lo = 0, hi = a.batch - 1;
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
@@ -172,10 +198,10 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel(const AttnA
         const int n = a.node_start[b + 1] - ns0;
         const int L = a.prefix_len[b];
         const int64_t s0 = a.kv_start[b];
-        const int steps = (L + n + kStep - 1) / kStep;
-        const int ui = static_cast<int>((pos - seq_base) / steps);
+        const int stages = (L + n + KST - 1) / KST;
+        const int ui = static_cast<int>((pos - seq_base) / stages);
         const int rg = ui / a.hkv, g = ui % a.hkv;
-        const int64_t ustart = seq_base + static_cast<int64_t>(ui) * steps, uend = ustart + steps;
+        const int64_t ustart = seq_base + static_cast<int64_t>(ui) * stages, uend = ustart + stages;
         const int64_t pend = end < uend ? end : uend;
         const int st0 = static_cast<int>(pos - ustart), st1 = static_cast<int>(pend - ustart);
         pos = pend;
@@ -199,279 +225,505 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel(const AttnA
             j = j >= 0 ? pj : -1;
         }
         const int nrows = n * G;
-        uint64_t rmask[RT];
+
+        // ---- this wave's tiles (slot 0: tile `wave`; slot 1: tile 4 when X5): Q^T operands in
+        // registers, ancestor masks, softmax state
+        const bool have_main = wave < RT;
+        uint64_t rmask[NTL];
+        bf16x8_t qop[NTL][KS];
+        f32x4_t o[NTL][DT];
+        float m_run[NTL], l_run[NTL];
 #pragma unroll
-        for (int t = 0; t < RT; ++t) {
+        for (int tt = 0; tt < NTL; ++tt) {
+            const int t = tt == 0 ? wave : 4;
             const int row = rg * R + 16 * t + lr;
-            const int node = row < nrows ? row / G : 0;
+            const bool live = t < RT && row < nrows;
+            const int node = live ? row / G : 0;
             const uint32_t mlo = __shfl(static_cast<uint32_t>(anc), node, 64);
             const uint32_t mhi = __shfl(static_cast<uint32_t>(anc >> 32), node, 64);
-            rmask[t] = row < nrows ? ((static_cast<uint64_t>(mhi) << 32) | mlo) : 0ull;
-        }
-
-        // ---- stage this unit's Q rows (bf16) in LDS
-        __syncthreads();
-        for (int c = tid; c < R * CPR; c += kThreads) {
-            const int r = c / CPR, ch = c % CPR;
-            const int row = rg * R + r;
-            u32x4_t val = {0u, 0u, 0u, 0u};
-            if (row < nrows) {
-                const int node = row / G, h = g * G + row % G;
-                const size_t off = (static_cast<size_t>(ns0 + node) * a.hq + h) * D + ch * 8;
-                if constexpr (F32IN) {
-                    const float *qp = static_cast<const float *>(a.q) + off;
-                    val = ev::f32x8_to_bf16x8(ev::ld16f(qp), ev::ld16f(qp + 4));
-                } else {
-                    val = ev::ld16(static_cast<const uint16_t *>(a.q) + off);
+            rmask[tt] = live ? ((static_cast<uint64_t>(mhi) << 32) | mlo) : 0ull;
+            const int h = g * G + (live ? row % G : 0);
+            const size_t qoff = (static_cast<size_t>(ns0 + node) * a.hq + h) * D;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                u32x4_t val = {0u, 0u, 0u, 0u};
+                if (live) {
+                    if constexpr (F32IN) {
+                        const float *qp = static_cast<const float *>(a.q) + qoff + 32 * s + 8 * lq;
+                        val = ev::f32x8_to_bf16x8(ev::ld16f(qp), ev::ld16f(qp + 4));
+                    } else {
+                        val = ev::ld16(static_cast<const uint16_t *>(a.q) + qoff + 32 * s + 8 * lq);
+                    }
                 }
+                qop[tt][s] = __builtin_bit_cast(bf16x8_t, val);
             }
-            *reinterpret_cast<u32x4_t *>(s_q + r * QP + ch * 8) = val;
+            m_run[tt] = -INFINITY;
+            l_run[tt] = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[tt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        __syncthreads();
 
-        // ---- this wave's steps
         const int kv_end = L + n;  // unit-relative key positions below this exist
         const size_t slot_stride = static_cast<size_t>(a.hkv) * D;  // elements between slots
         const size_t head_off = static_cast<size_t>(s0) * slot_stride + static_cast<size_t>(g) * D;
-        const int vc = lane % CPR, vkg = lane / CPR;
 
-        f32x4_t o[RT][DT];
-        float m_run[RT], l_run[RT];
+        // Online-softmax update of tile slot tt from raw scores (masked entries are -inf): the
+        // running max moves to the stage's max (scaled), the exponent folds the scale into one
+        // FMA, the state rescales only when some row's max moved.  emit(p_of) lets the caller pack
+        // the probabilities where it needs them.
+        auto softmax_update = [&](int tt, float mx_raw, auto &&emit) {
+            mx_raw = fmaxf(mx_raw, __shfl_xor(mx_raw, 16, 64));
+            mx_raw = fmaxf(mx_raw, __shfl_xor(mx_raw, 32, 64));
+            const float m_new = fmaxf(m_run[tt], mx_raw * c2);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run[tt] - m_use);
+            float psum = 0.f;
+            emit([&](float s) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s, c2, -m_use));
+                psum += p;
+                return p;
+            });
+            l_run[tt] = l_run[tt] * alpha + psum;
+            if (__any(alpha != 1.f)) {
 #pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            m_run[t] = -INFINITY;
-            l_run[t] = 0.f;
+                for (int dt = 0; dt < DT; ++dt) o[tt][dt] *= alpha;
+            }
+            m_run[tt] = m_new;
+        };
+        auto mask_scores = [&](int tt, int kb, int key0, f32x4_t &sc) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+            for (int r = 0; r < 4; ++r) {
+                const int p = kb + key0 + 4 * lq + r;
+                const bool vis = p < L || (p < kv_end && ((rmask[tt] >> (p - L)) & 1ull));
+                if (!vis) sc[r] = -INFINITY;
+            }
+        };
 
-        auto load_step = [&](int st, u32x4_t (&kd)[2][KS], u32x4_t (&vd)[NQ][4]) {
-            const int kb = st * kStep;
+        // One stage of this wave's tiles, given the K operand and V^T operand readers.  The V^T
+        // reader returns the operand for keys (32kc + 4*lq + 0..3, then 32kc + 16 + 4*lq + 0..3).
+        auto compute_stage = [&](int kb, auto kop_at, auto vop_at) {
+            if constexpr (!X5) {
+                if (!have_main) return;  // a wave without a tile of this unit
+            }
+            // every operand read of the stage is issued before the first MFMA needs one: the V^T
+            // reads complete under the QK^T MFMAs and the softmax
+            bf16x8_t kop[U][KS];
+            u32x4_t vop[KC][DT];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int p = kb + 16 * u + lr;
-                const size_t base = head_off + static_cast<size_t>(p) * slot_stride + 8 * lq;
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    u32x4_t val = {0u, 0u, 0u, 0u};
-                    if (p < kv_end) {
-                        if constexpr (F32IN) {
-                            const float *kp = static_cast<const float *>(a.k) + base + 32 * s;
-                            val = ev::f32x8_to_bf16x8(ev::ld16f_stream(kp), ev::ld16f_stream(kp + 4));
-                        } else {
-                            val = ev::ld16_stream(static_cast<const uint16_t *>(a.k) + base + 32 * s);
-                        }
+                for (int s = 0; s < KS; ++s) kop[u][s] = kop_at(u, s);
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) vop[kc][dt] = vop_at(kc, dt);
+            // S^T = K Q^T : sc[u] holds raw scores of keys 16u + 4*lq + r for row 16t + lr
+            f32x4_t sc[U], scx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                if (have_main) {
+#pragma unroll
+                    for (int s = 0; s < KS; ++s)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u][s], qop[0][s], acc, 0, 0, 0);
+                }
+                sc[u] = acc;
+                if constexpr (X5) {
+                    if (u == wave) {
+#pragma unroll
+                        for (int s = 0; s < KS; ++s)
+                            scx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u][s], qop[1][s], scx, 0, 0, 0);
                     }
-                    kd[u][s] = val;
                 }
             }
+            const bool edge = kb + KST > L;  // the stage reaches the tree slots or the unit's end
+            u32x4_t pw[KC];
+            uint32_t pwx[2] = {0u, 0u};
+            if (have_main) {
+                if (edge) {
 #pragma unroll
-            for (int qd = 0; qd < NQ; ++qd) {
+                    for (int u = 0; u < U; ++u) mask_scores(0, kb, 16 * u, sc[u]);
+                }
+                float mx = -INFINITY;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int p = kb + 4 * (vkg + KG * qd) + jj;
-                    u32x4_t val = {0u, 0u, 0u, 0u};
-                    if (p < kv_end) {
-                        const size_t off = head_off + static_cast<size_t>(p) * slot_stride + 8 * vc;
-                        if constexpr (F32IN) {
-                            const float *vp = static_cast<const float *>(a.v) + off;
-                            val = ev::f32x8_to_bf16x8(ev::ld16f_stream(vp), ev::ld16f_stream(vp + 4));
-                        } else {
-                            val = ev::ld16_stream(static_cast<const uint16_t *>(a.v) + off);
+                for (int u = 0; u < U; ++u)
+                    mx = fmaxf(mx, fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3])));
+                softmax_update(0, mx, [&](auto &&p_of) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2)
+                            pw[u >> 1][2 * (u & 1) + h2] =
+                                ev::pack_bf16x2(p_of(sc[u][2 * h2]), p_of(sc[u][2 * h2 + 1]));
+                    }
+                });
+            }
+            if constexpr (X5) {
+                if (edge) mask_scores(1, kb, 16 * wave, scx);
+                const float mx = fmaxf(fmaxf(scx[0], scx[1]), fmaxf(scx[2], scx[3]));
+                softmax_update(1, mx, [&](auto &&p_of) {
+                    pwx[0] = ev::pack_bf16x2(p_of(scx[0]), p_of(scx[1]));
+                    pwx[1] = ev::pack_bf16x2(p_of(scx[2]), p_of(scx[3]));
+                });
+            }
+            // O^T += V^T P^T per 32-key half (the quarter tile uses the matching 16-key half of
+            // the same V^T operand with a 16x16x16 MFMA)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[kc]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const u32x4_t vv = vop[kc][dt];
+                    if (have_main)
+                        o[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv), pop,
+                                                                           o[0][dt], 0, 0, 0);
+                    if constexpr (X5) {
+                        if (kc == (wave >> 1)) {
+                            const u32x2_t half = (wave & 1) ? u32x2_t{vv[2], vv[3]} : u32x2_t{vv[0], vv[1]};
+                            o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                                __builtin_bit_cast(v4i16_t, half), __builtin_bit_cast(v4i16_t, u32x2_t{pwx[0], pwx[1]}),
+                                o[1][dt], 0, 0, 0);
                         }
                     }
-                    vd[qd][jj] = val;
                 }
             }
         };
 
-        int st = st0 + wave;
-        u32x4_t kr[2][KS], vr[NQ][4];
-        if (st < st1) load_step(st, kr, vr);
-        for (; st < st1; st += kWaves) {
-            u32x4_t kn[2][KS], vn[NQ][4];
-            const bool more = st + kWaves < st1;
-            if (more) load_step(st + kWaves, kn, vn);
-
-            // V^T tile: row d holds this step's 32 keys of column d (4 keys per 8-byte write)
+        if constexpr (F32IN) {
+            // fp32 inputs: global -> registers (one stage ahead) -> bf16 in LDS
+            constexpr int KP = Lay::KP;
+            constexpr int VTP = Lay::VTP;
+            constexpr int KLD = (KST * CPR + NT - 1) / NT;        // K chunks per thread per stage
+            constexpr int VLD = (KST / 4 * CPR + NT - 1) / NT;    // V key-quads per thread
+            u32x4_t kreg[KLD][2], vreg[VLD][4][2];
+            auto load_stage = [&](int st) {
+                const int kb = st * KST;
 #pragma unroll
-            for (int qd = 0; qd < NQ; ++qd) {
-                const int kq = 4 * (vkg + KG * qd);
+                for (int i = 0; i < KLD; ++i) {
+                    const int id = tid + NT * i;
+                    const int key = id / CPR, c = id % CPR;
+                    const int p = kb + key;
+                    const bool ok_ld = id < KST * CPR && p < kv_end;
+                    const float *src = static_cast<const float *>(a.k) + head_off +
+                                       static_cast<size_t>(ok_ld ? p : 0) * slot_stride + 8 * c;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                    const uint32_t w0 = __builtin_amdgcn_perm(vr[qd][1][e >> 1], vr[qd][0][e >> 1], sel);
-                    const uint32_t w1 = __builtin_amdgcn_perm(vr[qd][3][e >> 1], vr[qd][2][e >> 1], sel);
-                    *reinterpret_cast<u32x2_t *>(s_vt + (8 * vc + e) * kVtPitch + 2 * kq) = u32x2_t{w0, w1};
+                    for (int e = 0; e < 2; ++e)
+                        kreg[i][e] = ok_ld ? __builtin_bit_cast(u32x4_t, ev::ld16f_stream(src + 4 * e))
+                                           : u32x4_t{0u, 0u, 0u, 0u};
                 }
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-
-            // S^T = K Q^T : sc[u][t] holds keys 16u + 4*lq + r for row 16t + lr
-            f32x4_t sc[2][RT];
 #pragma unroll
-            for (int t = 0; t < RT; ++t) {
-                bf16x8_t qop[KS];
+                for (int i = 0; i < VLD; ++i) {
+                    const int id = tid + NT * i;
+                    const int c = id % CPR, kq = 4 * (id / CPR);
 #pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    qop[s] = *reinterpret_cast<const bf16x8_t *>(s_q + (16 * t + lr) * QP + 32 * s + 8 * lq);
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int p = kb + kq + jj;
+                        const bool ok_ld = id < KST / 4 * CPR && p < kv_end;
+                        const float *src = static_cast<const float *>(a.v) + head_off +
+                                           static_cast<size_t>(ok_ld ? p : 0) * slot_stride + 8 * c;
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < KS; ++s)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, kr[u][s]), qop[s], acc, 0, 0, 0);
-                    sc[u][t] = acc * a.scale_log2;
+                        for (int e = 0; e < 2; ++e)
+                            vreg[i][jj][e] = ok_ld ? __builtin_bit_cast(u32x4_t, ev::ld16f_stream(src + 4 * e))
+                                                   : u32x4_t{0u, 0u, 0u, 0u};
+                    }
                 }
-            }
-            const int kb = st * kStep;
-            if (kb + kStep > L) {  // this step reaches the tree slots or the unit's end
+            };
+            auto to_bf16 = [&](const u32x4_t (&x)[2]) -> u32x4_t {
+                return ev::f32x8_to_bf16x8(__builtin_bit_cast(f32x4_t, x[0]), __builtin_bit_cast(f32x4_t, x[1]));
+            };
+            auto store_stage = [&](unsigned char *buf) {
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int i = 0; i < KLD; ++i) {
+                    const int id = tid + NT * i;
+                    if (id < KST * CPR) {
+                        const int key = id / CPR, c = id % CPR;
+                        *reinterpret_cast<u32x4_t *>(buf + key * KP + 16 * c) = to_bf16(kreg[i]);
+                    }
+                }
+                unsigned char *vt = buf + Lay::kK;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int p = kb + 16 * u + 4 * lq + r;
+                for (int i = 0; i < VLD; ++i) {
+                    const int id = tid + NT * i;
+                    if (id < KST / 4 * CPR) {
+                        const int c = id % CPR, kq = 4 * (id / CPR);
+                        const u32x4_t v0 = to_bf16(vreg[i][0]), v1 = to_bf16(vreg[i][1]);
+                        const u32x4_t v2 = to_bf16(vreg[i][2]), v3 = to_bf16(vreg[i][3]);
 #pragma unroll
-                        for (int t = 0; t < RT; ++t) {
-                            const bool vis = p < L || (p < kv_end && ((rmask[t] >> (p - L)) & 1ull));
-                            if (!vis) sc[u][t][r] = -INFINITY;
+                        for (int e = 0; e < 8; ++e) {
+                            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                            const uint32_t w0 = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], sel);
+                            const uint32_t w1 = __builtin_amdgcn_perm(v3[e >> 1], v2[e >> 1], sel);
+                            *reinterpret_cast<u32x2_t *>(vt + (8 * c + e) * VTP + 2 * kq) = u32x2_t{w0, w1};
                         }
                     }
                 }
+            };
+            __syncthreads();  // the previous piece is done with both stage buffers
+            load_stage(st0);
+            store_stage(stage_buf);
+            __syncthreads();
+            for (int st = st0; st < st1; ++st) {
+                unsigned char *cur = stage_buf + ((st - st0) & 1) * Lay::kStageBytes;
+                unsigned char *nxt = stage_buf + ((st - st0 + 1) & 1) * Lay::kStageBytes;
+                const bool more = st + 1 < st1;
+                if (more) load_stage(st + 1);
+                const unsigned char *vt = cur + Lay::kK;
+                compute_stage(
+                    st * KST,
+                    [&](int u, int s) {
+                        return *reinterpret_cast<const bf16x8_t *>(cur + (16 * u + lr) * KP + 2 * (32 * s + 8 * lq));
+                    },
+                    [&](int kc, int dt) {
+                        const unsigned char *vrow = vt + (16 * dt + lr) * VTP + 2 * (32 * kc + 4 * lq);
+                        const u32x2_t v0 = *reinterpret_cast<const u32x2_t *>(vrow);
+                        const u32x2_t v1 = *reinterpret_cast<const u32x2_t *>(vrow + 32);
+                        return u32x4_t{v0[0], v0[1], v1[0], v1[1]};
+                    });
+                if (more) store_stage(nxt);
+                __syncthreads();
             }
-
-            // online softmax (fp32); P rounded to bf16 and laid out as the P^T operand
-            bf16x8_t pop[RT];
+        } else {
+            // bf16 inputs: HBM -> LDS with direct 16-byte loads, kStages - 1 stages in flight and
+            // no register staging.  K and V rows keep their natural layout; within a row the
+            // 16-byte chunks are XOR-swizzled per row so both the K operand reads (16 rows, one
+            // chunk each) and the V transpose reads (8 rows, two chunks each, per half-wave)
+            // spread over all LDS banks.
+            constexpr int ROWB = Lay::kRowB;
+            constexpr int TB = Lay::kTensorB;
+            constexpr int RPI = 1024 / ROWB;                    // rows per 1-KB wave load
+            constexpr int INSTR = 2 * TB / 1024;                // wave loads per stage (K and V)
+            constexpr int PERL = INSTR / NW;                    // loads per wave per stage
+            constexpr int SWZ = 16 / CPR;                       // rows per 256-byte bank cycle
+            static_assert(INSTR % (2 * NW) == 0, "loader split");
+            static_assert(PERL * (kStages - 2) < 64, "vmcnt range");
+            const uint16_t *kbase = static_cast<const uint16_t *>(a.k) + head_off;
+            const uint16_t *vbase = static_cast<const uint16_t *>(a.v) + head_off;
+            auto fk = [](int r) { return (r / SWZ) & (CPR - 1); };
+            auto fv = [](int r) { return 2 * ((r / SWZ) & (CPR / 2 - 1)); };
+            auto issue = [&](int st, int bi) {
+                unsigned char *buf = stage_buf + bi * Lay::kStageBytes;
 #pragma unroll
-            for (int t = 0; t < RT; ++t) {
-                float mx = fmaxf(fmaxf(fmaxf(sc[0][t][0], sc[0][t][1]), fmaxf(sc[0][t][2], sc[0][t][3])),
-                                 fmaxf(fmaxf(sc[1][t][0], sc[1][t][1]), fmaxf(sc[1][t][2], sc[1][t][3])));
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                const float m_new = fmaxf(m_run[t], mx);
-                const float m_use = m_new == -INFINITY ? 0.f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_use);
-                u32x4_t pw;
-                float psum = 0.f;
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const uint32_t w = ev::pack_bf16x2(__builtin_amdgcn_exp2f(sc[u][t][2 * h2] - m_use),
-                                                           __builtin_amdgcn_exp2f(sc[u][t][2 * h2 + 1] - m_use));
-                        psum += ev::bf_lo(w) + ev::bf_hi(w);
-                        pw[2 * u + h2] = w;
-                    }
+                for (int i = 0; i < PERL; ++i) {
+                    const int ins = wave * PERL + i;
+                    const bool isv = ins >= INSTR / 2;            // uniform per wave
+                    const int local = isv ? ins - INSTR / 2 : ins;
+                    const int row = local * RPI + lane / CPR;
+                    const int p = lane % CPR;
+                    const int kp = st * KST + row;
+                    const int c = p ^ (isv ? fv(row) : fk(row));
+                    const int kpc = kp < kv_end ? kp : 0;          // rows past the unit: any finite row
+                    const uint16_t *src = (isv ? vbase : kbase) + static_cast<size_t>(kpc) * slot_stride + 8 * c;
+                    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(buf + (isv ? TB : 0) + local * 1024), 16, 0,
+                                                     0);
                 }
-                pop[t] = __builtin_bit_cast(bf16x8_t, pw);
-                l_run[t] = l_run[t] * alpha + psum;
-                if (__any(alpha != 1.f)) {
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
-                }
-                m_run[t] = m_new;
+            };
+            __syncthreads();  // the previous piece is done with the stage buffers
+            const int nst = st1 - st0;
+            for (int i = 0; i < kStages - 1 && i < nst; ++i) issue(st0 + i, i);
+            for (int i = 0; i < nst; ++i) {
+                const int later = min(kStages - 2, nst - 1 - i);   // stages issued after this one
+                if (later >= 2) vm_wait_n<2 * PERL>();
+                else if (later == 1) vm_wait_n<PERL>();
+                else vm_wait_n<0>();
+                // Stage i is in LDS and every wave is done with stage i - 1.  A bare barrier: the
+                // fence of __syncthreads would drain the loads still in flight for later stages.
+                bare_barrier();
+                if (i + kStages - 1 < nst) issue(st0 + i + kStages - 1, (i + kStages - 1) % kStages);
+                const unsigned char *cur = stage_buf + (i % kStages) * Lay::kStageBytes;
+                compute_stage(
+                    (st0 + i) * KST,
+                    [&](int u, int s) {
+                        const int row = 16 * u + lr;
+                        return *reinterpret_cast<const bf16x8_t *>(cur + row * ROWB + 16 * ((4 * s + lq) ^ fk(row)));
+                    },
+                    [&](int kc, int dt) {
+                        const int c = 2 * dt + ((lr & 3) >> 1);
+                        const int r0 = 32 * kc + 4 * lq + (lr >> 2), r1 = r0 + 16;
+                        const unsigned char *vb = cur + TB;
+                        const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_v4i16_t *)(vb + r0 * ROWB + 16 * (c ^ fv(r0)) + 8 * (lr & 1)));
+                        const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_v4i16_t *)(vb + r1 * ROWB + 16 * (c ^ fv(r1)) + 8 * (lr & 1)));
+                        const u32x2_t y0 = __builtin_bit_cast(u32x2_t, x0), y1 = __builtin_bit_cast(u32x2_t, x1);
+                        return u32x4_t{y0[0], y0[1], y1[0], y1[1]};
+                    });
             }
-
-            // O^T += V^T P^T
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const unsigned char *vrow = s_vt + (16 * dt + lr) * kVtPitch + 8 * lq;
-                const u32x2_t v0 = *reinterpret_cast<const u32x2_t *>(vrow);
-                const u32x2_t v1 = *reinterpret_cast<const u32x2_t *>(vrow + 32);
-                const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, u32x4_t{v0[0], v0[1], v1[0], v1[1]});
-#pragma unroll
-                for (int t = 0; t < RT; ++t)
-                    o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[t], o[t][dt], 0, 0, 0);
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-
-            if (more) {
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int s = 0; s < KS; ++s) kr[u][s] = kn[u][s];
-#pragma unroll
-                for (int qd = 0; qd < NQ; ++qd)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) vr[qd][jj] = vn[qd][jj];
-            }
+            __syncthreads();  // every wave is done with the stage buffers
         }
 
         // ---- per-row sums over the four lanes that share a row
 #pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            l_run[t] += __shfl_xor(l_run[t], 16, 64);
-            l_run[t] += __shfl_xor(l_run[t], 32, 64);
+        for (int tt = 0; tt < NTL; ++tt) {
+            l_run[tt] += __shfl_xor(l_run[tt], 16, 64);
+            l_run[tt] += __shfl_xor(l_run[tt], 32, 64);
         }
 
-        // ---- merge the four waves (fixed order: (w0 + w2) + (w1 + w3))
-        __syncthreads();
-        if (lq == 0) {
+        // ---- tile 4: merge the four key-quarter states into wave 0 (fixed order)
+        if constexpr (X5) {
+            float *xo = reinterpret_cast<float *>(stage_buf);   // [4][16][D + 4]
+            float *xm = xo + 4 * 16 * (D + 4);                  // [4][16]
+            float *xl = xm + 64;                                // [4][16]
 #pragma unroll
-            for (int t = 0; t < RT; ++t) {
-                s_mw[wave * R + 16 * t + lr] = m_run[t];
-                s_lw[wave * R + 16 * t + lr] = l_run[t];
+            for (int dt = 0; dt < DT; ++dt)
+                *reinterpret_cast<f32x4_t *>(xo + (wave * 16 + lr) * (D + 4) + 16 * dt + 4 * lq) = o[1][dt];
+            if (lq == 0) {
+                xm[wave * 16 + lr] = m_run[1];
+                xl[wave * 16 + lr] = l_run[1];
             }
+            __syncthreads();
+            if (wave == 0) {
+                float M = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) M = fmaxf(M, xm[w * 16 + lr]);
+                const float Mu = M == -INFINITY ? 0.f : M;
+                float lt = 0.f;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o[1][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const float f = __builtin_amdgcn_exp2f(xm[w * 16 + lr] - Mu);
+                    lt += f * xl[w * 16 + lr];
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt)
+                        o[1][dt] += f * *reinterpret_cast<const f32x4_t *>(xo + (w * 16 + lr) * (D + 4) + 16 * dt + 4 * lq);
+                }
+                m_run[1] = M;
+                l_run[1] = lt;
+            }
+            __syncthreads();
         }
-        __syncthreads();
-        float m_tot[RT], l_tot[RT];
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            const int row = 16 * t + lr;
-            float M = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_mw[w * R + row]);
-            const float Mu = M == -INFINITY ? 0.f : M;
-            float lt = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) lt += s_lw[w * R + row] * __builtin_amdgcn_exp2f(s_mw[w * R + row] - Mu);
-            const float c = __builtin_amdgcn_exp2f(m_run[t] - Mu);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[t][dt] *= c;
-            m_tot[t] = M;
-            l_tot[t] = lt;
-        }
-        auto store_o = [&](float *buf) {
-#pragma unroll
-            for (int t = 0; t < RT; ++t)
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    *reinterpret_cast<f32x4_t *>(buf + (16 * t + lr) * OP + 16 * dt + 4 * lq) = o[t][dt];
-        };
-        auto add_o = [&](const float *buf) {
-#pragma unroll
-            for (int t = 0; t < RT; ++t)
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    o[t][dt] += *reinterpret_cast<const f32x4_t *>(buf + (16 * t + lr) * OP + 16 * dt + 4 * lq);
-        };
-        __syncthreads();
-        if (wave == 2) store_o(s_oa);
-        if (wave == 3) store_o(s_ob);
-        __syncthreads();
-        if (wave == 0) add_o(s_oa);
-        if (wave == 1) add_o(s_ob);
-        __syncthreads();
-        if (wave == 1) store_o(s_oa);
-        __syncthreads();
-        if (wave == 0) add_o(s_oa);
+        // tiles this wave finally holds: slot 0 (tile `wave`), slot 1 (tile 4, wave 0 only)
+        auto tile_of = [&](int tt) { return tt == 0 ? (have_main ? wave : -1) : (wave == 0 ? 4 : -1); };
 
         // ---- output
         const bool whole = ustart >= begin && uend <= end;
         if (whole) {
-            if (wave == 0) {
 #pragma unroll
-                for (int t = 0; t < RT; ++t) {
-                    const int row = rg * R + 16 * t + lr;
-                    if (row >= nrows) continue;
-                    const int node = row / G, h = g * G + row % G;
-                    const size_t orow = static_cast<size_t>(ns0 + node) * a.hq + h;
-                    const float inv = 1.f / l_tot[t];
+            for (int tt = 0; tt < NTL; ++tt) {
+                const int t = tile_of(tt);
+                const int row = rg * R + 16 * t + lr;
+                if (t < 0 || row >= nrows) continue;
+                const int node = row / G, h = g * G + row % G;
+                const size_t orow = static_cast<size_t>(ns0 + node) * a.hq + h;
+                const float inv = 1.f / l_run[tt];
 #pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        const f32x4_t val = o[t][dt] * inv;
-                        const size_t off = orow * D + 16 * dt + 4 * lq;
+                for (int dt = 0; dt < DT; ++dt) {
+                    const f32x4_t val = o[tt][dt] * inv;
+                    const size_t off = orow * D + 16 * dt + 4 * lq;
+                    if constexpr (F32IN) {
+                        *reinterpret_cast<f32x4_t *>(static_cast<float *>(a.out) + off) = val;
+                    } else {
+                        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(a.out) + off) =
+                            u32x2_t{ev::pack_bf16x2(val[0], val[1]), ev::pack_bf16x2(val[2], val[3])};
+                    }
+                }
+                if (a.lse && lq == 0) a.lse[orow] = (m_run[tt] + __log2f(l_run[tt])) * kLn2;
+            }
+            continue;
+        }
+
+        // ---- split unit: publish this piece's partial, then merge hierarchically.  The unit's pieces
+        // (consecutive workgroups w1..w2) form groups of 8; the last arriver of a group merges its
+        // members in order into the first member's slot and arrives one level up; the root group's
+        // last arriver writes the output.  Fixed grouping and order: deterministic.
+        const int w1 = wg_of(ustart, S, P), w2 = wg_of(uend - 1, S, P);
+        const int npieces = w2 - w1 + 1;
+        auto slot_of = [&](int piece) -> float * {
+            const int w = w1 + piece;
+            return a.part + static_cast<size_t>(piece == 0 ? 2 * w + 1 : 2 * w) * Lay::kSlotFloats;
+        };
+        {
+            float *slot = slot_of(wl - w1);
+#pragma unroll
+            for (int tt = 0; tt < NTL; ++tt) {
+                const int t = tile_of(tt);
+                if (t < 0) continue;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) ev::st_agent4(slot + (16 * t + lr) * D + 16 * dt + 4 * lq, o[tt][dt]);
+                if (lq == 0) {
+                    ev::st_agent(slot + R * D + 16 * t + lr, m_run[tt]);
+                    ev::st_agent(slot + R * D + R + 16 * t + lr, l_run[tt]);
+                }
+            }
+        }
+        float *s_fac = reinterpret_cast<float *>(stage_buf);   // [kFanIn][R] merge factors
+        float *s_ml = s_fac + kFanIn * R;                       // [2][R] merged m, l
+        int idx = wl - w1, n_lvl = npieces;
+        for (int level = 0;; ++level) {
+            ev::vm_wait();  // this workgroup's published partial / merged group is complete
+            __syncthreads();
+            const int first = (idx / kFanIn) * kFanIn;
+            const int members = min(kFanIn, n_lvl - first);
+            const int shift = 3 * level;
+            int32_t *ctr = a.counters + level * (2 * kMaxGrid) + (slot_of(first << shift) - a.part) / Lay::kSlotFloats;
+            if (tid == 0) {
+                const int old = ev::atomic_add_agent(ctr, 1);
+                s_misc[NW] = old == members - 1;
+                if (old == members - 1) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            if (!s_misc[NW]) break;
+            const bool root = n_lvl <= kFanIn;
+            if (members > 1 || root) {
+                const float *src[kFanIn];
+#pragma unroll
+                for (int i = 0; i < kFanIn; ++i) src[i] = slot_of((first + (i < members ? i : 0)) << shift);
+                float *dst = const_cast<float *>(src[0]);
+                // per-row factors of every member
+                if (tid < R) {
+                    float mi[kFanIn], li[kFanIn], M = -INFINITY;
+#pragma unroll
+                    for (int i = 0; i < kFanIn; ++i) {
+                        mi[i] = i < members ? ev::ld_agent(src[i] + R * D + tid) : -INFINITY;
+                        li[i] = i < members ? ev::ld_agent(src[i] + R * D + R + tid) : 0.f;
+                    }
+#pragma unroll
+                    for (int i = 0; i < kFanIn; ++i) M = fmaxf(M, mi[i]);
+                    const float Mu = M == -INFINITY ? 0.f : M;
+                    float lt = 0.f;
+#pragma unroll
+                    for (int i = 0; i < kFanIn; ++i) {
+                        const float f = i < members ? __builtin_amdgcn_exp2f(mi[i] - Mu) : 0.f;
+                        s_fac[i * R + tid] = f;
+                        lt += f * li[i];
+                    }
+                    s_ml[tid] = M;
+                    s_ml[R + tid] = lt;
+                }
+                __syncthreads();
+                constexpr int C4 = R * D / 4;                  // float4 chunks of O
+                constexpr int PER = (C4 + NT - 1) / NT;
+                constexpr int BATCH = PER < (X5 ? 4 : 2) ? PER : (X5 ? 4 : 2);
+#pragma unroll
+                for (int z0 = 0; z0 < PER; z0 += BATCH) {
+                    // issue every member's loads for this batch before using any of them
+                    f32x4_t x[kFanIn][BATCH];
+#pragma unroll
+                    for (int i = 0; i < kFanIn; ++i) {
+#pragma unroll
+                        for (int z = 0; z < BATCH; ++z) {
+                            const int c = tid + NT * (z0 + z);
+                            x[i][z] = (i < members && z0 + z < PER && c < C4) ? ev::ld_agent4(src[i] + 4 * c)
+                                                                              : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        }
+                    }
+#pragma unroll
+                    for (int z = 0; z < BATCH; ++z) {
+                        const int c = tid + NT * (z0 + z);
+                        if (z0 + z >= PER || c >= C4) continue;
+                        const int r = (4 * c) / D, d0 = (4 * c) % D;
+                        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int i = 0; i < kFanIn; ++i) acc += s_fac[i * R + r] * x[i][z];
+                        if (!root) {
+                            ev::st_agent4(dst + 4 * c, acc);
+                            continue;
+                        }
+                        const int row = rg * R + r;
+                        if (row >= nrows) continue;
+                        const int node = row / G, h = g * G + row % G;
+                        const size_t off = (static_cast<size_t>(ns0 + node) * a.hq + h) * D + d0;
+                        const f32x4_t val = acc * (1.f / s_ml[R + r]);
                         if constexpr (F32IN) {
                             *reinterpret_cast<f32x4_t *>(static_cast<float *>(a.out) + off) = val;
                         } else {
@@ -479,70 +731,38 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel(const AttnA
                                 u32x2_t{ev::pack_bf16x2(val[0], val[1]), ev::pack_bf16x2(val[2], val[3])};
                         }
                     }
-                    if (a.lse && lq == 0) a.lse[orow] = (m_tot[t] + __log2f(l_tot[t])) * kLn2;
+                }
+                if (tid < R) {
+                    if (root) {
+                        const int row = rg * R + tid;
+                        if (a.lse && row < nrows) {
+                            const int node = row / G, h = g * G + row % G;
+                            a.lse[static_cast<size_t>(ns0 + node) * a.hq + h] =
+                                (s_ml[tid] + __log2f(s_ml[R + tid])) * kLn2;
+                        }
+                    } else {
+                        ev::st_agent(dst + R * D + tid, s_ml[tid]);
+                        ev::st_agent(dst + R * D + R + tid, s_ml[R + tid]);
+                    }
                 }
             }
-            continue;
+            if (root) break;
+            idx = first >> 3;
+            n_lvl = (n_lvl + kFanIn - 1) / kFanIn;
         }
-
-        // ---- split unit: publish this piece's partial, the last arriver merges all pieces
-        const int w1 = wg_of(ustart, S, P), w2 = wg_of(uend - 1, S, P);
-        float *slot = a.part + static_cast<size_t>(wl == w1 ? 2 * wl + 1 : 2 * wl) * Lay::kSlotFloats;
-        if (wave == 0) {
-#pragma unroll
-            for (int t = 0; t < RT; ++t) {
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    *reinterpret_cast<f32x4_t *>(slot + (16 * t + lr) * D + 16 * dt + 4 * lq) = o[t][dt];
-                if (lq == 0) {
-                    slot[R * D + 16 * t + lr] = m_tot[t];
-                    slot[R * D + R + 16 * t + lr] = l_tot[t];
-                }
-            }
-        }
-        __threadfence();
-        __syncthreads();
-        int32_t *counter = a.counters + (static_cast<size_t>(b) * a.row_groups + rg) * a.hkv + g;
-        if (tid == 0) {
-            int pieces = 0;
-            for (int w = w1; w <= w2; ++w) pieces += (S * w / P) < (S * (w + 1) / P);
-            const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-            s_flag[0] = old == pieces - 1;
-        }
-        __syncthreads();
-        if (!s_flag[0]) continue;
-        __threadfence();
-        for (int e = tid; e < R * D; e += kThreads) {
-            const int r = e / D, dc = e % D;
-            const int row = rg * R + r;
-            if (row >= nrows) continue;
-            float M = -INFINITY;
-            for (int w = w1; w <= w2; ++w) {
-                if (!((S * w / P) < (S * (w + 1) / P))) continue;
-                const float *ps = a.part + static_cast<size_t>(w == w1 ? 2 * w + 1 : 2 * w) * Lay::kSlotFloats;
-                M = fmaxf(M, ps[R * D + r]);
-            }
-            const float Mu = M == -INFINITY ? 0.f : M;
-            float acc = 0.f, lt = 0.f;
-            for (int w = w1; w <= w2; ++w) {
-                if (!((S * w / P) < (S * (w + 1) / P))) continue;
-                const float *ps = a.part + static_cast<size_t>(w == w1 ? 2 * w + 1 : 2 * w) * Lay::kSlotFloats;
-                const float f = __builtin_amdgcn_exp2f(ps[R * D + r] - Mu);
-                acc += f * ps[r * D + dc];
-                lt += f * ps[R * D + R + r];
-            }
-            const int node = row / G, h = g * G + row % G;
-            const size_t orow = static_cast<size_t>(ns0 + node) * a.hq + h;
-            const float val = acc / lt;
-            if constexpr (F32IN) {
-                static_cast<float *>(a.out)[orow * D + dc] = val;
-            } else {
-                static_cast<uint16_t *>(a.out)[orow * D + dc] = static_cast<uint16_t>(ev::f2bf_bits(val));
-            }
-            if (a.lse && dc == 0) a.lse[orow] = (M + __log2f(lt)) * kLn2;
-        }
-        if (tid == 0) *counter = 0;
+        __syncthreads();  // the merge used the stage buffers
     }
+}
+
+// Up to four row tiles: 32-key stages, two workgroups per CU.
+template <int D, int RT, bool F32IN>
+__global__ __launch_bounds__(kThreads, 2) void tree_attention_kernel(const AttnArgs a) {
+    attention_body<D, RT, F32IN>(a);
+}
+// 80-row units: 64-key stages, one workgroup per CU (each wave holds 1.25 tiles).
+template <int D, bool F32IN>
+__global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel5(const AttnArgs a) {
+    attention_body<D, 5, F32IN>(a);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -561,7 +781,7 @@ Plan make_plan(int32_t batch, int32_t max_nodes, int32_t hq, int32_t hkv, int32_
     p.R = 16 * p.RT;
     p.RG = (rows + p.R - 1) / p.R;
     p.slot_floats = static_cast<size_t>(p.R) * head_dim + 2 * p.R;
-    p.counters_bytes = ((static_cast<size_t>(batch) * p.RG * hkv * 4 + 255) / 256) * 256;
+    p.counters_bytes = ((static_cast<size_t>(kMergeLevels) * 2 * kMaxGrid * 4 + 255) / 256) * 256;
     p.bytes = p.counters_bytes + 2 * static_cast<size_t>(kMaxGrid) * p.slot_floats * 4;
     return p;
 }
@@ -575,7 +795,7 @@ KernelFn pick_rt(int rt) {
         case 2: return tree_attention_kernel<D, 2, F32IN>;
         case 3: return tree_attention_kernel<D, 3, F32IN>;
         case 4: return tree_attention_kernel<D, 4, F32IN>;
-        default: return tree_attention_kernel<D, 5, F32IN>;
+        default: return tree_attention_kernel5<D, F32IN>;
     }
 }
 
@@ -623,7 +843,7 @@ extern "C" ev_status ev_tree_attention(const void *q, const void *k_cache, const
         return EV_ERR_NULL;
     if (batch < 0 || batch > EV_MAX_BATCH || total_nodes < 0 || max_nodes < 1 || max_nodes > EV_MAX_NODES ||
         total_slots < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads ||
-        (head_dim != 64 && head_dim != 128) || !std::isfinite(sm_scale))
+        (head_dim != 64 && head_dim != 128) || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
         return EV_ERR_SHAPE;
     if (dtype != EV_BF16 && dtype != EV_F32) return EV_ERR_DTYPE;
     if (!ev::aligned16(q) || !ev::aligned16(k_cache) || !ev::aligned16(v_cache) || !ev::aligned16(out))
@@ -631,6 +851,9 @@ extern "C" ev_status ev_tree_attention(const void *q, const void *k_cache, const
     const Plan plan = make_plan(batch, max_nodes, num_q_heads, num_kv_heads, head_dim);
     if (!workspace || workspace_bytes < plan.bytes) return EV_ERR_WORKSPACE;
     if (!ev::aligned16(workspace)) return EV_ERR_ALIGN;
+    // stage counts are 32-bit in the kernel (32-key stages bound them from above)
+    const int64_t max_stages = static_cast<int64_t>(num_kv_heads) * plan.RG * (total_slots / 32 + 2 * batch);
+    if (max_stages >= (int64_t(1) << 31)) return EV_ERR_SHAPE;
     const ev_status dev = ev::check_device();
     if (dev != EV_OK) return dev;
     if (batch == 0 || total_nodes == 0) return EV_OK;
@@ -639,11 +862,9 @@ extern "C" ev_status ev_tree_attention(const void *q, const void *k_cache, const
     KernelFn fn = pick_kernel(head_dim, plan.RT, f32);
     const int variant = (head_dim == 64 ? 0 : 16) + (f32 ? 8 : 0) + plan.RT;
     const int resident = ev::device_cu_count() * blocks_per_cu(fn, variant);
-    // Upper bound of the step count: every sequence's keys fit in the cache.
-    const int64_t max_steps = static_cast<int64_t>(num_kv_heads) * plan.RG * (total_slots / kStep + 2 * batch);
     int64_t grid = resident;
     if (grid > kMaxGrid) grid = kMaxGrid;
-    const int64_t want = (max_steps + kWaves - 1) / kWaves;  // at least a step per wave
+    const int64_t want = (max_stages + 1) / 2;  // about two stages per workgroup at least
     if (grid > want) grid = want;
     if (grid >= 8) grid -= grid % 8;
     if (grid < 1) grid = 1;

@@ -10,6 +10,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint64_t u64x2_t __attribute__((ext_vector_type(2)));
 
 namespace ev {
 
@@ -50,6 +51,34 @@ __device__ __forceinline__ f32x4_t ld16f_stream(const float *p) {
 __device__ __forceinline__ u32x4_t f32x8_to_bf16x8(f32x4_t a, f32x4_t b) {
     return u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
                    pack_bf16x2(b[2], b[3])};
+}
+
+// Cross-workgroup publication without L2 flushes.  Agent-scope relaxed atomic stores/loads are
+// sc1 accesses (coherent across the XCDs' separate L2s); a writer drains them with vm_wait()
+// before its arrival counter's atomic, and the reader issues its sc1 loads after observing
+// the counter, so no buffer_wbl2 / buffer_inv is needed.
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void st_agent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// (Whole-vector bit casts only: casting single elements out of vectors was mis-translated.)
+__device__ __forceinline__ void st_agent4(float *p, f32x4_t v) {
+    const u64x2_t w = __builtin_bit_cast(u64x2_t, v);
+    uint64_t *q = reinterpret_cast<uint64_t *>(p);
+    __hip_atomic_store(q, w[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, w[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4_t ld_agent4(const float *p) {
+    uint64_t *q = reinterpret_cast<uint64_t *>(const_cast<float *>(p));
+    const u64x2_t w = {__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                       __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+    return __builtin_bit_cast(f32x4_t, w);
+}
+__device__ __forceinline__ int atomic_add_agent(int32_t *p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
