@@ -100,7 +100,83 @@ __device__ __forceinline__ void bare_barrier() {
 }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// Byte address of a shared-memory pointer in the LDS aperture.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    typedef const __attribute__((address_space(3))) unsigned char *lds_cptr;
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cptr)p));
+}
+
+// All V^T operand reads of one stage: x[dt][j] = ds_read_b64_tr_b16 at addr[dt] + j * 16 rows.
+// One asm block that waits for its own reads before it ends, so every output register holds its
+// value when the block is left.  Issued through the builtin instead, these reads get a
+// conservative wait for all outstanding global-to-LDS loads in front of them (the compiler
+// cannot tell that they touch another stage buffer), which would drain the stage pipeline.
+// Outputs are early-clobber: a read may land while later reads still need their address.
+#define EV_TR(o, a, off) "ds_read_b64_tr_b16 %" #o ", %" #a " offset:" #off "\n\t"
+#define EV_O(i) "=&v"(x[(i) / NJ][(i) % NJ])
+template <int D, int KC> struct TrRead;
+template <> struct TrRead<128, 2> {  // 16-row step 4096 bytes, 4 reads per d tile
+    static constexpr int NJ = 4;
+    __device__ static __forceinline__ void run(u32x2_t (&x)[8][4], const uint32_t (&a)[8]) {
+        asm volatile(EV_TR(0, 32, 0) EV_TR(1, 32, 4096) EV_TR(2, 32, 8192) EV_TR(3, 32, 12288)
+                     EV_TR(4, 33, 0) EV_TR(5, 33, 4096) EV_TR(6, 33, 8192) EV_TR(7, 33, 12288)
+                     EV_TR(8, 34, 0) EV_TR(9, 34, 4096) EV_TR(10, 34, 8192) EV_TR(11, 34, 12288)
+                     EV_TR(12, 35, 0) EV_TR(13, 35, 4096) EV_TR(14, 35, 8192) EV_TR(15, 35, 12288)
+                     EV_TR(16, 36, 0) EV_TR(17, 36, 4096) EV_TR(18, 36, 8192) EV_TR(19, 36, 12288)
+                     EV_TR(20, 37, 0) EV_TR(21, 37, 4096) EV_TR(22, 37, 8192) EV_TR(23, 37, 12288)
+                     EV_TR(24, 38, 0) EV_TR(25, 38, 4096) EV_TR(26, 38, 8192) EV_TR(27, 38, 12288)
+                     EV_TR(28, 39, 0) EV_TR(29, 39, 4096) EV_TR(30, 39, 8192) EV_TR(31, 39, 12288)
+                     "s_waitcnt lgkmcnt(0)"
+                     : EV_O(0), EV_O(1), EV_O(2), EV_O(3), EV_O(4), EV_O(5), EV_O(6), EV_O(7), EV_O(8),
+                       EV_O(9), EV_O(10), EV_O(11), EV_O(12), EV_O(13), EV_O(14), EV_O(15), EV_O(16),
+                       EV_O(17), EV_O(18), EV_O(19), EV_O(20), EV_O(21), EV_O(22), EV_O(23), EV_O(24),
+                       EV_O(25), EV_O(26), EV_O(27), EV_O(28), EV_O(29), EV_O(30), EV_O(31)
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+                     : "memory");
+    }
+};
+template <> struct TrRead<128, 1> {  // 2 reads per d tile
+    static constexpr int NJ = 2;
+    __device__ static __forceinline__ void run(u32x2_t (&x)[8][2], const uint32_t (&a)[8]) {
+        asm volatile(EV_TR(0, 16, 0) EV_TR(1, 16, 4096) EV_TR(2, 17, 0) EV_TR(3, 17, 4096)
+                     EV_TR(4, 18, 0) EV_TR(5, 18, 4096) EV_TR(6, 19, 0) EV_TR(7, 19, 4096)
+                     EV_TR(8, 20, 0) EV_TR(9, 20, 4096) EV_TR(10, 21, 0) EV_TR(11, 21, 4096)
+                     EV_TR(12, 22, 0) EV_TR(13, 22, 4096) EV_TR(14, 23, 0) EV_TR(15, 23, 4096)
+                     "s_waitcnt lgkmcnt(0)"
+                     : EV_O(0), EV_O(1), EV_O(2), EV_O(3), EV_O(4), EV_O(5), EV_O(6), EV_O(7), EV_O(8),
+                       EV_O(9), EV_O(10), EV_O(11), EV_O(12), EV_O(13), EV_O(14), EV_O(15)
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+                     : "memory");
+    }
+};
+template <> struct TrRead<64, 2> {  // 16-row step 2048 bytes
+    static constexpr int NJ = 4;
+    __device__ static __forceinline__ void run(u32x2_t (&x)[4][4], const uint32_t (&a)[4]) {
+        asm volatile(EV_TR(0, 16, 0) EV_TR(1, 16, 2048) EV_TR(2, 16, 4096) EV_TR(3, 16, 6144)
+                     EV_TR(4, 17, 0) EV_TR(5, 17, 2048) EV_TR(6, 17, 4096) EV_TR(7, 17, 6144)
+                     EV_TR(8, 18, 0) EV_TR(9, 18, 2048) EV_TR(10, 18, 4096) EV_TR(11, 18, 6144)
+                     EV_TR(12, 19, 0) EV_TR(13, 19, 2048) EV_TR(14, 19, 4096) EV_TR(15, 19, 6144)
+                     "s_waitcnt lgkmcnt(0)"
+                     : EV_O(0), EV_O(1), EV_O(2), EV_O(3), EV_O(4), EV_O(5), EV_O(6), EV_O(7), EV_O(8),
+                       EV_O(9), EV_O(10), EV_O(11), EV_O(12), EV_O(13), EV_O(14), EV_O(15)
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                     : "memory");
+    }
+};
+template <> struct TrRead<64, 1> {
+    static constexpr int NJ = 2;
+    __device__ static __forceinline__ void run(u32x2_t (&x)[4][2], const uint32_t (&a)[4]) {
+        asm volatile(EV_TR(0, 8, 0) EV_TR(1, 8, 2048) EV_TR(2, 9, 0) EV_TR(3, 9, 2048)
+                     EV_TR(4, 10, 0) EV_TR(5, 10, 2048) EV_TR(6, 11, 0) EV_TR(7, 11, 2048)
+                     "s_waitcnt lgkmcnt(0)"
+                     : EV_O(0), EV_O(1), EV_O(2), EV_O(3), EV_O(4), EV_O(5), EV_O(6), EV_O(7)
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                     : "memory");
+    }
+};
+#undef EV_O
+#undef EV_TR
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Workgroup (logical index) whose stage range contains stage x: the largest w with
@@ -299,9 +375,9 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
             }
         };
 
-        // One stage of this wave's tiles, given the K operand and V^T operand readers.  The V^T
-        // reader returns the operand for keys (32kc + 4*lq + 0..3, then 32kc + 16 + 4*lq + 0..3).
-        auto compute_stage = [&](int kb, auto kop_at, auto vop_at) {
+        // One stage of this wave's tiles, given the K operand reader and the V^T operand filler.
+        // vop[kc][dt] holds the operand for keys (32kc + 4*lq + 0..3, then 32kc + 16 + 4*lq + 0..3).
+        auto compute_stage = [&](int kb, auto kop_at, auto vload) {
             if constexpr (!X5) {
                 if (!have_main) return;  // a wave without a tile of this unit
             }
@@ -313,10 +389,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int s = 0; s < KS; ++s) kop[u][s] = kop_at(u, s);
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) vop[kc][dt] = vop_at(kc, dt);
+            vload(vop);
             // S^T = K Q^T : sc[u] holds raw scores of keys 16u + 4*lq + r for row 16t + lr
             f32x4_t sc[U], scx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -473,11 +546,16 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
                     [&](int u, int s) {
                         return *reinterpret_cast<const bf16x8_t *>(cur + (16 * u + lr) * KP + 2 * (32 * s + 8 * lq));
                     },
-                    [&](int kc, int dt) {
-                        const unsigned char *vrow = vt + (16 * dt + lr) * VTP + 2 * (32 * kc + 4 * lq);
-                        const u32x2_t v0 = *reinterpret_cast<const u32x2_t *>(vrow);
-                        const u32x2_t v1 = *reinterpret_cast<const u32x2_t *>(vrow + 32);
-                        return u32x4_t{v0[0], v0[1], v1[0], v1[1]};
+                    [&](u32x4_t (&vop)[KC][DT]) {
+#pragma unroll
+                        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+                            for (int dt = 0; dt < DT; ++dt) {
+                                const unsigned char *vrow = vt + (16 * dt + lr) * VTP + 2 * (32 * kc + 4 * lq);
+                                const u32x2_t v0 = *reinterpret_cast<const u32x2_t *>(vrow);
+                                const u32x2_t v1 = *reinterpret_cast<const u32x2_t *>(vrow + 32);
+                                vop[kc][dt] = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
+                            }
                     });
                 if (more) store_stage(nxt);
                 __syncthreads();
@@ -536,16 +614,23 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
                         const int row = 16 * u + lr;
                         return *reinterpret_cast<const bf16x8_t *>(cur + row * ROWB + 16 * ((4 * s + lq) ^ fk(row)));
                     },
-                    [&](int kc, int dt) {
-                        const int c = 2 * dt + ((lr & 3) >> 1);
-                        const int r0 = 32 * kc + 4 * lq + (lr >> 2), r1 = r0 + 16;
-                        const unsigned char *vb = cur + TB;
-                        const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_v4i16_t *)(vb + r0 * ROWB + 16 * (c ^ fv(r0)) + 8 * (lr & 1)));
-                        const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_v4i16_t *)(vb + r1 * ROWB + 16 * (c ^ fv(r1)) + 8 * (lr & 1)));
-                        const u32x2_t y0 = __builtin_bit_cast(u32x2_t, x0), y1 = __builtin_bit_cast(u32x2_t, x1);
-                        return u32x4_t{y0[0], y0[1], y1[0], y1[1]};
+                    [&](u32x4_t (&vop)[KC][DT]) {
+                        // Lane address of d tile dt for keys 4*lq + lr/4 (+16, +32, +48: the same
+                        // swizzle, so those are immediate offsets).  The swizzle term is even, so
+                        // (2dt + b) ^ fv = 2 (dt ^ fv/2) + b.
+                        const int r0 = 4 * lq + (lr >> 2);
+                        const uint32_t row_addr = lds_addr(cur + TB) + r0 * ROWB + 16 * ((lr & 3) >> 1) + 8 * (lr & 1);
+                        uint32_t addr[DT];
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt) addr[dt] = row_addr + 32 * (dt ^ (fv(r0) >> 1));
+                        u32x2_t x[DT][2 * KC];
+                        TrRead<D, KC>::run(x, addr);
+#pragma unroll
+                        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+                            for (int dt = 0; dt < DT; ++dt)
+                                vop[kc][dt] = u32x4_t{x[dt][2 * kc][0], x[dt][2 * kc][1], x[dt][2 * kc + 1][0],
+                                                      x[dt][2 * kc + 1][1]};
                     });
             }
             __syncthreads();  // every wave is done with the stage buffers
