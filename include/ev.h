@@ -96,6 +96,7 @@ const char *ev_status_string(ev_status status);
  *   max_nodes             upper bound of N_b, 1..EV_MAX_NODES
  *   total_slots           slots in the cache (bounds check)
  *   head_dim              64 or 128;  num_q_heads % num_kv_heads == 0
+ *   sm_scale              finite and > 0 (EV_ERR_SHAPE otherwise)
  *   workspace             >= ev_tree_attention_workspace_size(...) bytes, ZEROED ONCE by the
  *                         caller before its first use; every call leaves it reusable (its
  *                         counters are back at zero when the call's work completes).  Calls
