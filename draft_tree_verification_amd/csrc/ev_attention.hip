@@ -32,6 +32,7 @@
 //     last arriver merges in fixed order: deterministic, no L2 flushes).
 #include <cmath>
 #include <mutex>
+#include <type_traits>
 
 #include "ev_internal.h"
 
@@ -41,8 +42,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxGrid = 512;      // workgroups per launch (bounds the partial-result slots)
 constexpr int kMaxRowTiles = 5;    // 16-row tiles per unit: at most 80 rows
-constexpr int kFanIn = 8;          // pieces merged per group in the hierarchical merge
-constexpr int kMergeLevels = 3;    // 8^3 >= kMaxGrid pieces
 constexpr int kStages = 4;         // LDS stage buffers of the bf16 path: three stages in flight
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -60,7 +59,7 @@ struct AttnArgs {
     int64_t total_slots;
     int32_t batch, total_nodes, max_nodes, hq, hkv, group, row_groups;
     float scale_log2;  // sm_scale * log2(e) > 0: scores live in the base-2 domain
-    int32_t *counters; // [kMergeLevels][2 * kMaxGrid] group arrival counters (per first-member slot)
+    int4 *table;       // [grid] per logical workgroup: the split unit whose first piece it holds
     float *part;       // [2 * kMaxGrid] partial-result slots
     int32_t *err_flag;
 };
@@ -185,39 +184,25 @@ __device__ __forceinline__ int wg_of(int64_t x, int64_t S, int P) {
     return static_cast<int>(((x + 1) * P - 1) / S);
 }
 
-template <int D, int RT, bool F32IN>
-__device__ __forceinline__ void attention_body(const AttnArgs &a) {
-    using Lay = Layout<D, RT, F32IN>;
-    constexpr bool X5 = Lay::X5;
-    constexpr int KST = Lay::KST;
-    constexpr int U = KST / 16;                // 16-key sub-tiles per stage
-    constexpr int KC = KST / 32;               // 32-key halves per stage (PV MFMA extent)
-    constexpr int NW = kWaves;
+// Partial-result slot of piece `piece` of the split unit whose first piece is held by logical
+// workgroup w1: a workgroup holds at most two split pieces, the last piece of a unit begun
+// earlier (slot 2w) and the first piece of a unit that continues past it (slot 2w + 1).
+__device__ __forceinline__ float *slot_of_piece(float *part, int w1, int piece, int slot_floats) {
+    const int w = w1 + piece;
+    return part + static_cast<size_t>(piece == 0 ? 2 * w + 1 : 2 * w) * slot_floats;
+}
+
+// Per-sequence stage counts of the whole batch and their inclusive scan into s_cum (identical
+// in every workgroup); returns the total stage count.  Sequences with bad geometry get no stages
+// and raise their error bit once.
+template <int R, int KST>
+__device__ __forceinline__ int64_t schedule_scan(const AttnArgs &a, int32_t *s_cum, int32_t *s_misc) {
     constexpr int NT = kThreads;
-    constexpr int R = Lay::R;
-    constexpr int KS = D / 32;                 // k-steps of the QK^T contraction
-    constexpr int DT = D / 16;                 // 16-wide d tiles of O^T
-    constexpr int CPR = D / 8;                 // 8-element chunks per K/V row
-    constexpr int NTL = X5 ? 2 : 1;            // register tiles per wave: own tile (+ tile 4's quarter)
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::kTotal];
-    int32_t *s_cum = reinterpret_cast<int32_t *>(smem);
-    int32_t *s_misc = reinterpret_cast<int32_t *>(smem + Lay::kScan);
-    unsigned char *stage_buf = smem + Lay::kScan + Lay::kMisc;
-
+    constexpr int NW = kWaves;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    // The wave index must be visibly uniform: every wave-dependent choice below (which tiles a
-    // wave owns, which key quarter it takes) then compiles to a scalar branch.  Under an
-    // EXEC-masked branch the compiler may drop the skip jump around a short block, and an MFMA
-    // in such a block still writes its accumulator when no lane is active.
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lr = lane & 15;
-    const int lq = lane >> 4;
+    const int wave = tid >> 6;
     const int G = a.group;
-    const float c2 = a.scale_log2;
-
-    // ---- schedule: per-sequence stage counts and their inclusive scan (identical in every WG)
     int carry = 0;
     for (int b0 = 0; b0 < a.batch; b0 += NT) {
         const int b = b0 + tid;
@@ -253,11 +238,47 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
         carry += tot;
         __syncthreads();
     }
-    const int64_t S = carry;
+    return carry;
+}
+
+template <int D, int RT, bool F32IN>
+__device__ __forceinline__ void attention_body(const AttnArgs &a) {
+    using Lay = Layout<D, RT, F32IN>;
+    constexpr bool X5 = Lay::X5;
+    constexpr int KST = Lay::KST;
+    constexpr int U = KST / 16;                // 16-key sub-tiles per stage
+    constexpr int KC = KST / 32;               // 32-key halves per stage (PV MFMA extent)
+    constexpr int NW = kWaves;
+    constexpr int NT = kThreads;
+    constexpr int R = Lay::R;
+    constexpr int KS = D / 32;                 // k-steps of the QK^T contraction
+    constexpr int DT = D / 16;                 // 16-wide d tiles of O^T
+    constexpr int CPR = D / 8;                 // 8-element chunks per K/V row
+    constexpr int NTL = X5 ? 2 : 1;            // register tiles per wave: own tile (+ tile 4's quarter)
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::kTotal];
+    int32_t *s_cum = reinterpret_cast<int32_t *>(smem);
+    int32_t *s_misc = reinterpret_cast<int32_t *>(smem + Lay::kScan);
+    unsigned char *stage_buf = smem + Lay::kScan + Lay::kMisc;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    // The wave index must be visibly uniform: every wave-dependent choice below (which tiles a
+    // wave owns, which key quarter it takes) then compiles to a scalar branch.  Under an
+    // EXEC-masked branch the compiler may drop the skip jump around a short block, and an MFMA
+    // in such a block still writes its accumulator when no lane is active.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15;
+    const int lq = lane >> 4;
+    const int G = a.group;
+    const float c2 = a.scale_log2;
+
+    const int64_t S = schedule_scan<R, KST>(a, s_cum, s_misc);
     const int grid = gridDim.x;
     const int wl = (grid % 8 == 0) ? (blockIdx.x % 8) * (grid / 8) + blockIdx.x / 8 : blockIdx.x;
     // logical workgroups: never more than stages, so every logical range is non-empty
     const int P = static_cast<int>(S < grid ? S : grid);
+    if (tid == 0) a.table[wl] = int4{0, 0, 0, 0};  // no split unit starts here (until one does)
     if (wl >= P) return;
     const int64_t begin = S * wl / P, end = S * (wl + 1) / P;
 
@@ -707,135 +728,25 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
             continue;
         }
 
-        // ---- split unit: publish this piece's partial, then merge hierarchically.  The unit's pieces
-        // (consecutive workgroups w1..w2) form groups of 8; the last arriver of a group merges its
-        // members in order into the first member's slot and arrives one level up; the root group's
-        // last arriver writes the output.  Fixed grouping and order: deterministic.
-        const int w1 = wg_of(ustart, S, P), w2 = wg_of(uend - 1, S, P);
-        const int npieces = w2 - w1 + 1;
-        auto slot_of = [&](int piece) -> float * {
-            const int w = w1 + piece;
-            return a.part + static_cast<size_t>(piece == 0 ? 2 * w + 1 : 2 * w) * Lay::kSlotFloats;
-        };
+        // ---- split unit: publish this piece's partial (m, l, unnormalised O); the merge launch
+        // combines the unit's pieces
+        const int w1 = wg_of(ustart, S, P);
         {
-            float *slot = slot_of(wl - w1);
+            float *slot = slot_of_piece(a.part, w1, wl - w1, Lay::kSlotFloats);
 #pragma unroll
             for (int tt = 0; tt < NTL; ++tt) {
                 const int t = tile_of(tt);
                 if (t < 0) continue;
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) ev::st_agent4(slot + (16 * t + lr) * D + 16 * dt + 4 * lq, o[tt][dt]);
+                for (int dt = 0; dt < DT; ++dt)
+                    *reinterpret_cast<f32x4_t *>(slot + (16 * t + lr) * D + 16 * dt + 4 * lq) = o[tt][dt];
                 if (lq == 0) {
-                    ev::st_agent(slot + R * D + 16 * t + lr, m_run[tt]);
-                    ev::st_agent(slot + R * D + R + 16 * t + lr, l_run[tt]);
+                    slot[R * D + 16 * t + lr] = m_run[tt];
+                    slot[R * D + R + 16 * t + lr] = l_run[tt];
                 }
             }
         }
-        float *s_fac = reinterpret_cast<float *>(stage_buf);   // [kFanIn][R] merge factors
-        float *s_ml = s_fac + kFanIn * R;                       // [2][R] merged m, l
-        int idx = wl - w1, n_lvl = npieces;
-        for (int level = 0;; ++level) {
-            ev::vm_wait();  // this workgroup's published partial / merged group is complete
-            __syncthreads();
-            const int first = (idx / kFanIn) * kFanIn;
-            const int members = min(kFanIn, n_lvl - first);
-            const int shift = 3 * level;
-            int32_t *ctr = a.counters + level * (2 * kMaxGrid) + (slot_of(first << shift) - a.part) / Lay::kSlotFloats;
-            if (tid == 0) {
-                const int old = ev::atomic_add_agent(ctr, 1);
-                s_misc[NW] = old == members - 1;
-                if (old == members - 1) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            __syncthreads();
-            if (!s_misc[NW]) break;
-            const bool root = n_lvl <= kFanIn;
-            if (members > 1 || root) {
-                const float *src[kFanIn];
-#pragma unroll
-                for (int i = 0; i < kFanIn; ++i) src[i] = slot_of((first + (i < members ? i : 0)) << shift);
-                float *dst = const_cast<float *>(src[0]);
-                // per-row factors of every member
-                if (tid < R) {
-                    float mi[kFanIn], li[kFanIn], M = -INFINITY;
-#pragma unroll
-                    for (int i = 0; i < kFanIn; ++i) {
-                        mi[i] = i < members ? ev::ld_agent(src[i] + R * D + tid) : -INFINITY;
-                        li[i] = i < members ? ev::ld_agent(src[i] + R * D + R + tid) : 0.f;
-                    }
-#pragma unroll
-                    for (int i = 0; i < kFanIn; ++i) M = fmaxf(M, mi[i]);
-                    const float Mu = M == -INFINITY ? 0.f : M;
-                    float lt = 0.f;
-#pragma unroll
-                    for (int i = 0; i < kFanIn; ++i) {
-                        const float f = i < members ? __builtin_amdgcn_exp2f(mi[i] - Mu) : 0.f;
-                        s_fac[i * R + tid] = f;
-                        lt += f * li[i];
-                    }
-                    s_ml[tid] = M;
-                    s_ml[R + tid] = lt;
-                }
-                __syncthreads();
-                constexpr int C4 = R * D / 4;                  // float4 chunks of O
-                constexpr int PER = (C4 + NT - 1) / NT;
-                constexpr int BATCH = PER < (X5 ? 4 : 2) ? PER : (X5 ? 4 : 2);
-#pragma unroll
-                for (int z0 = 0; z0 < PER; z0 += BATCH) {
-                    // issue every member's loads for this batch before using any of them
-                    f32x4_t x[kFanIn][BATCH];
-#pragma unroll
-                    for (int i = 0; i < kFanIn; ++i) {
-#pragma unroll
-                        for (int z = 0; z < BATCH; ++z) {
-                            const int c = tid + NT * (z0 + z);
-                            x[i][z] = (i < members && z0 + z < PER && c < C4) ? ev::ld_agent4(src[i] + 4 * c)
-                                                                              : f32x4_t{0.f, 0.f, 0.f, 0.f};
-                        }
-                    }
-#pragma unroll
-                    for (int z = 0; z < BATCH; ++z) {
-                        const int c = tid + NT * (z0 + z);
-                        if (z0 + z >= PER || c >= C4) continue;
-                        const int r = (4 * c) / D, d0 = (4 * c) % D;
-                        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int i = 0; i < kFanIn; ++i) acc += s_fac[i * R + r] * x[i][z];
-                        if (!root) {
-                            ev::st_agent4(dst + 4 * c, acc);
-                            continue;
-                        }
-                        const int row = rg * R + r;
-                        if (row >= nrows) continue;
-                        const int node = row / G, h = g * G + row % G;
-                        const size_t off = (static_cast<size_t>(ns0 + node) * a.hq + h) * D + d0;
-                        const f32x4_t val = acc * (1.f / s_ml[R + r]);
-                        if constexpr (F32IN) {
-                            *reinterpret_cast<f32x4_t *>(static_cast<float *>(a.out) + off) = val;
-                        } else {
-                            *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(a.out) + off) =
-                                u32x2_t{ev::pack_bf16x2(val[0], val[1]), ev::pack_bf16x2(val[2], val[3])};
-                        }
-                    }
-                }
-                if (tid < R) {
-                    if (root) {
-                        const int row = rg * R + tid;
-                        if (a.lse && row < nrows) {
-                            const int node = row / G, h = g * G + row % G;
-                            a.lse[static_cast<size_t>(ns0 + node) * a.hq + h] =
-                                (s_ml[tid] + __log2f(s_ml[R + tid])) * kLn2;
-                        }
-                    } else {
-                        ev::st_agent(dst + R * D + tid, s_ml[tid]);
-                        ev::st_agent(dst + R * D + R + tid, s_ml[R + tid]);
-                    }
-                }
-            }
-            if (root) break;
-            idx = first >> 3;
-            n_lvl = (n_lvl + kFanIn - 1) / kFanIn;
-        }
-        __syncthreads();  // the merge used the stage buffers
+        if (wl == w1 && tid == 0) a.table[wl] = int4{wg_of(uend - 1, S, P) - w1 + 1, b, ui, 0};
     }
 }
 
@@ -851,10 +762,534 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel5(const Attn
 }
 
 // ---------------------------------------------------------------------------------------------
+// 80-row units with bf16 inputs: key-split waves with private load pipelines.
+//
+// Every wave covers all five 16-row tiles (all N*G rows of the unit) for its own 16-key quarter
+// of each 64-key stage, so each K/V byte is read from LDS once (not once per row tile), and the
+// wave alone loads, reads and refills its quarter's LDS buffers: no workgroup barrier inside the
+// stage loop, and a buffer is refilled as soon as its operands are in registers, which keeps
+// about four stages in flight per wave.  The softmax keeps a running maximum per row and rescales
+// only when a new score exceeds it by more than 2^8 (in the exponent's base-2 domain), so the
+// cross-lane maximum is taken rarely; probabilities stay below 2^8 and lose nothing in bf16's
+// relative precision.  The four wave states meet through LDS at the end of each piece, each wave
+// finalising a quarter of the d columns.
+
+template <int D>
+struct LayKS {
+    static constexpr int R = 80;
+    static constexpr int RT = 5;
+    static constexpr int KST = 64;                        // keys per stage, 16 per wave
+    static constexpr int ROWB = 2 * D;                    // bytes per K/V row
+    static constexpr int SUB = 16 * ROWB;                 // one wave's 16 K (or V) rows
+    static constexpr int WBUF = 2 * SUB;                  // K rows then V rows
+    static constexpr int NB = 4;                          // buffers per wave
+    static constexpr int kScan = 4 * EV_MAX_BATCH;
+    static constexpr int kMisc = 32;
+    static constexpr int kBufs = kWaves * NB * WBUF;
+    static constexpr int kTotal = kScan + kMisc + kBufs;
+    static constexpr int DTW = D / 16 / kWaves;           // d tiles each wave finalises
+    static constexpr int XO = kWaves * (D / 16 - DTW) * RT * 64 * 16;  // merge exchange bytes
+    static_assert(XO + 2 * kWaves * R * 4 <= kBufs, "merge exchange space");
+};
+
+// One asm block per stage and wave: the K operand reads (ds_read_b128) and the V^T operand
+// transpose reads (ds_read_b64_tr_b16), waiting for all of them before the block ends.
+#define EV_RK(o, a) "ds_read_b128 %" #o ", %" #a "\n\t"
+#define EV_RV(o, a) "ds_read_b64_tr_b16 %" #o ", %" #a "\n\t"
+template <int D> struct ReadKV;
+template <> struct ReadKV<128> {
+    __device__ static __forceinline__ void run(u32x4_t (&k)[4], u32x2_t (&v)[8], const uint32_t (&ka)[4],
+                                               const uint32_t (&va)[8]) {
+        asm volatile(EV_RK(0, 12) EV_RK(1, 13) EV_RK(2, 14) EV_RK(3, 15)
+                     EV_RV(4, 16) EV_RV(5, 17) EV_RV(6, 18) EV_RV(7, 19)
+                     EV_RV(8, 20) EV_RV(9, 21) EV_RV(10, 22) EV_RV(11, 23)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]),
+                       "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+                     : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
+                       "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7])
+                     : "memory");
+    }
+};
+template <> struct ReadKV<64> {
+    __device__ static __forceinline__ void run(u32x4_t (&k)[2], u32x2_t (&v)[4], const uint32_t (&ka)[2],
+                                               const uint32_t (&va)[4]) {
+        asm volatile(EV_RK(0, 6) EV_RK(1, 7) EV_RV(2, 8) EV_RV(3, 9) EV_RV(4, 10) EV_RV(5, 11)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+                     : "v"(ka[0]), "v"(ka[1]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3])
+                     : "memory");
+    }
+};
+#undef EV_RK
+#undef EV_RV
+
+constexpr float kRescaleSlack = 8.f;  // log2 of the largest probability allowed before a rescale
+
+template <int D>
+__device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
+    using Lay = LayKS<D>;
+    constexpr int R = Lay::R;
+    constexpr int RT = Lay::RT;
+    constexpr int KST = Lay::KST;
+    constexpr int NW = kWaves;
+    constexpr int KS = D / 32;                 // k-steps of the QK^T contraction
+    constexpr int DT = D / 16;                 // 16-wide d tiles of O^T
+    constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+    constexpr int ROWB = Lay::ROWB;
+    constexpr int SUB = Lay::SUB;
+    constexpr int WBUF = Lay::WBUF;
+    constexpr int NB = Lay::NB;
+    constexpr int RPI = 1024 / ROWB;           // rows per 1-KB wave load
+    constexpr int PERK = 16 / RPI;             // wave loads per 16-row block
+    constexpr int PERW = 2 * PERK;             // wave loads per stage (K and V)
+    constexpr int SWZ = 16 / CPR;              // rows per 256-byte bank cycle
+    constexpr int DTW = Lay::DTW;
+    static_assert(PERW * (NB - 1) < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::kTotal];
+    int32_t *s_cum = reinterpret_cast<int32_t *>(smem);
+    int32_t *s_misc = reinterpret_cast<int32_t *>(smem + Lay::kScan);
+    unsigned char *bufs = smem + Lay::kScan + Lay::kMisc;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches only
+    const int G = a.group;
+    const float c2 = a.scale_log2;
+
+    const int64_t S = schedule_scan<R, KST>(a, s_cum, s_misc);
+    const int grid = gridDim.x;
+    const int wl = (grid % 8 == 0) ? (blockIdx.x % 8) * (grid / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int P = static_cast<int>(S < grid ? S : grid);
+    if (tid == 0) a.table[wl] = int4{0, 0, 0, 0};  // no split unit starts here (until one does)
+    if (wl >= P) return;
+    const int64_t begin = S * wl / P, end = S * (wl + 1) / P;
+
+    // Chunks are XOR-swizzled per row (same rule as the other bf16 path): K row r keeps global
+    // chunk c at slot c ^ fk(r), V row r at slot c ^ fv(r); rows are local to a 16-row block.
+    auto fk = [](int r) { return (r / SWZ) & (CPR - 1); };
+    auto fv = [](int r) { return 2 * ((r / SWZ) & (CPR / 2 - 1)); };
+    unsigned char *wbuf = bufs + wave * NB * WBUF;        // this wave's private buffers
+
+    for (int64_t pos = begin; pos < end;) {
+        // Lane-derived values are recomputed for every piece: kept live across the whole kernel
+        // they crowd the registers of the stage loop out and come back through scratch.
+        int lane = threadIdx.x & 63;
+        asm volatile("" : "+v"(lane));
+        const int lr = lane & 15;
+        const int lq = lane >> 4;
+        // ---- locate the unit that holds stage `pos`
+        int lo = 0, hi = a.batch - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (s_cum[mid] > pos) hi = mid; else lo = mid + 1;
+        }
+        const int b = lo;
+        const int64_t seq_base = b ? s_cum[b - 1] : 0;
+        const int ns0 = a.node_start[b];
+        const int n = a.node_start[b + 1] - ns0;
+        const int L = a.prefix_len[b];
+        const int64_t s0 = a.kv_start[b];
+        const int stages = (L + n + KST - 1) / KST;
+        const int ui = static_cast<int>((pos - seq_base) / stages);
+        const int rg = ui / a.hkv, g = ui % a.hkv;
+        const int64_t ustart = seq_base + static_cast<int64_t>(ui) * stages, uend = ustart + stages;
+        const int64_t pend = end < uend ? end : uend;
+        const int st0 = static_cast<int>(pos - ustart), st1 = static_cast<int>(pend - ustart);
+        pos = pend;
+
+        const int nrows = n * G;
+        const int kv_end = L + n;
+        const int nst = st1 - st0;
+        const size_t slot_stride = static_cast<size_t>(a.hkv) * D;
+        const size_t head_off = static_cast<size_t>(s0) * slot_stride + static_cast<size_t>(g) * D;
+        const uint16_t *kbase = static_cast<const uint16_t *>(a.k) + head_off;
+        const uint16_t *vbase = static_cast<const uint16_t *>(a.v) + head_off;
+
+        // lane offsets of the operand reads inside one buffer: K operand step s = row lr, chunk
+        // 4s + lq; V^T operand d tile dt = rows 4lq + lr/4, chunk 2dt + (lr&3)/2, half lr&1
+        const uint32_t wbuf_lds = lds_addr(wbuf);
+        uint32_t koff[KS], voff[DT];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) koff[s] = lr * ROWB + 16 * ((4 * s + lq) ^ fk(lr));
+        {
+            const int r0 = 4 * lq + (lr >> 2);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                voff[dt] = SUB + r0 * ROWB + 32 * (dt ^ (fv(r0) >> 1)) + 16 * ((lr & 3) >> 1) + 8 * (lr & 1);
+        }
+        // this wave's quarter of stage st (keys st*64 + 16*wave + 0..15) into buffer bi
+        auto issue = [&](int st, int bi) {
+            unsigned char *buf = wbuf + bi * WBUF;
+#pragma unroll
+            for (int i = 0; i < PERW; ++i) {
+                const bool isv = i >= PERK;
+                const int local = isv ? i - PERK : i;
+                const int row = local * RPI + lane / CPR;
+                const int c = (lane % CPR) ^ (isv ? fv(row) : fk(row));
+                const int kp = st * KST + 16 * wave + row;
+                const int kpc = kp < kv_end ? kp : 0;     // rows past the unit: any finite row (masked)
+                const uint16_t *src = (isv ? vbase : kbase) + static_cast<size_t>(kpc) * slot_stride + 8 * c;
+                __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(buf + (isv ? SUB : 0) + local * 1024), 16, 0, 0);
+            }
+        };
+
+        // ---- the piece's loads, in the order they are needed: the parents, this wave's first
+        // stage, the Q^T operands of all five tiles (rows past the unit read a real row: their
+        // results are never written), then the next NB-1 stages (indices clamped into the piece).
+        // The count is fixed, so waiting for Q below leaves only the later stages in flight.
+        int par = -1;
+        if (lane < n) par = a.parent[ns0 + lane];
+        // every wave is done with the previous piece's use of the buffers (a bare barrier: the
+        // parents' load stays in flight)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        bare_barrier();
+        issue(st0, 0);
+        bf16x8_t qop[RT][KS];
+        int tnode[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            const int row = rg * R + 16 * t + lr;
+            const bool live = row < nrows;
+            tnode[t] = live ? row / G : -1;
+            const int node = live ? row / G : 0;
+            const int h = g * G + (live ? row % G : 0);
+            const size_t qoff = (static_cast<size_t>(ns0 + node) * a.hq + h) * D;
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                qop[t][s] = __builtin_bit_cast(bf16x8_t, ev::ld16(static_cast<const uint16_t *>(a.q) + qoff + 32 * s + 8 * lq));
+        }
+#pragma unroll
+        for (int i = 1; i < NB; ++i) issue(st0 + min(i, nst - 1), i);
+
+        // ---- tree: validity and ancestor masks, while the loads are in flight
+        const bool ok = lane >= n || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
+        if (__any(!ok)) {
+            if (tid == 0) ev::flag_error(a.err_flag, EV_DATA_BAD_PARENT);
+            vm_wait_n<0>();
+            continue;  // uniform across the workgroup: every wave read the same parents
+        }
+        uint64_t anc = lane < n ? (1ull << lane) : 0ull;
+        int j = lane < n ? par : -1;
+        while (__any(j >= 0)) {
+            if (j >= 0) anc |= 1ull << j;
+            const int pj = __shfl(par, j >= 0 ? j : 0, 64);
+            j = j >= 0 ? pj : -1;
+        }
+        uint64_t rmask[RT];
+        f32x4_t o[RT][DT];
+        float m_run[RT], l_run[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            const int node = tnode[t] >= 0 ? tnode[t] : 0;
+            const uint32_t mlo = __shfl(static_cast<uint32_t>(anc), node, 64);
+            const uint32_t mhi = __shfl(static_cast<uint32_t>(anc >> 32), node, 64);
+            rmask[t] = tnode[t] >= 0 ? ((static_cast<uint64_t>(mhi) << 32) | mlo) : 0ull;
+            m_run[t] = -INFINITY;
+            l_run[t] = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        // Q is complete before the stage loop (the loop then only waits for its own stage loads)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qop[t][s]));
+
+        // P^T operands (bf16) from the scores with the current maxima, per-lane row sums, and
+        // O^T += V^T P^T over the block's 16 keys
+        auto accumulate = [&](const f32x4_t (&sc)[RT], const u32x2_t (&vq)[DT]) {
+            u32x2_t pw[RT];
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const float mu = m_run[t] == -INFINITY ? 0.f : m_run[t];
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][0], c2, -mu));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][1], c2, -mu));
+                const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][2], c2, -mu));
+                const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][3], c2, -mu));
+                l_run[t] += (p0 + p1) + (p2 + p3);
+                pw[t] = u32x2_t{ev::pack_bf16x2(p0, p1), ev::pack_bf16x2(p2, p3)};
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const v4i16_t vop = __builtin_bit_cast(v4i16_t, vq[dt]);
+#pragma unroll
+                for (int t = 0; t < RT; ++t)
+                    o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, __builtin_bit_cast(v4i16_t, pw[t]),
+                                                                          o[t][dt], 0, 0, 0);
+            }
+        };
+
+        // The hot loop never touches the accumulators outside the MFMAs (they stay in the matrix
+        // registers); a stage whose scores need new maxima leaves it, and the rescale runs below.
+        int i = 0;
+        for (;;) {
+            f32x4_t sc[RT];
+            float mloc[RT];
+            u32x2_t vq[DT];
+            bool rescale = false;
+            for (; i < nst; ++i) {
+                const int later = min(NB - 1, nst - 1 - i);  // this wave's stages issued after stage i
+                if (later >= 3) vm_wait_n<3 * PERW>();
+                else if (later == 2) vm_wait_n<2 * PERW>();
+                else if (later == 1) vm_wait_n<PERW>();
+                else vm_wait_n<0>();
+                const uint32_t base = wbuf_lds + (i % NB) * WBUF;
+                uint32_t ka[KS], va[DT];
+#pragma unroll
+                for (int s = 0; s < KS; ++s) ka[s] = base + koff[s];
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) va[dt] = base + voff[dt];
+                u32x4_t kq[KS];
+                ReadKV<D>::run(kq, vq, ka, va);
+                if (i + NB < nst) issue(st0 + i + NB, i % NB);  // the buffer's operands are in registers
+
+                const int kb = (st0 + i) * KST + 16 * wave;     // unit-relative first key of the block
+                // S^T = K Q^T: sc[t] holds raw scores of keys kb + 4*lq + r for row 16t + lr
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KS; ++s)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kq[s]), qop[t][s],
+                                                                      acc, 0, 0, 0);
+                    sc[t] = acc;
+                }
+                if (kb + 16 > L) {  // the block reaches the tree slots or the unit's end
+#pragma unroll
+                    for (int t = 0; t < RT; ++t)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int p = kb + 4 * lq + r;
+                            const bool vis = p < L || (p < kv_end && ((rmask[t] >> (p - L)) & 1ull));
+                            if (!vis) sc[t][r] = -INFINITY;
+                        }
+                }
+                // running maxima move only when a score exceeds them by more than the slack
+                bool need = false;
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    mloc[t] = fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3]));
+                    need |= mloc[t] * c2 > m_run[t] + kRescaleSlack;
+                }
+                if (__any(need)) {
+                    rescale = true;
+                    break;
+                }
+                accumulate(sc, vq);
+            }
+            if (!rescale) break;
+            // new maxima for stage i: rescale the states, then finish the stage
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                float mx = mloc[t];
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float m_new = fmaxf(m_run[t], mx * c2);
+                const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[t] - m_new);
+                if (__any(alpha != 1.f)) {
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
+                }
+                l_run[t] *= alpha;
+                m_run[t] = m_new;
+            }
+            accumulate(sc, vq);
+            ++i;
+        }
+
+        // ---- row sums over the four lanes that share a row
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            l_run[t] += __shfl_xor(l_run[t], 16, 64);
+            l_run[t] += __shfl_xor(l_run[t], 32, 64);
+        }
+
+        // ---- the four wave states meet in LDS; wave w finalises d tiles [w*DTW, (w+1)*DTW)
+        f32x4_t *xo = reinterpret_cast<f32x4_t *>(bufs);                       // [src][dt'][t][lane]
+        float *xm = reinterpret_cast<float *>(bufs + Lay::XO);                 // [src][R]
+        float *xl = xm + NW * R;                                               // [src][R]
+        __syncthreads();  // every wave is done with its stage buffers
+        {
+            int jj = 0;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                if (dt / DTW == wave) continue;
+#pragma unroll
+                for (int t = 0; t < RT; ++t) xo[((wave * (DT - DTW) + jj) * RT + t) * 64 + lane] = o[t][dt];
+                ++jj;
+            }
+            if (lq == 0) {
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    xm[wave * R + 16 * t + lr] = m_run[t];
+                    xl[wave * R + 16 * t + lr] = l_run[t];
+                }
+            }
+        }
+        __syncthreads();
+        float fac[NW][RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            float ms[NW], M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                ms[w] = xm[w * R + 16 * t + lr];
+                M = fmaxf(M, ms[w]);
+            }
+            const float Mu = M == -INFINITY ? 0.f : M;
+            float lt = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                fac[w][t] = __builtin_amdgcn_exp2f(ms[w] - Mu);
+                lt += fac[w][t] * xl[w * R + 16 * t + lr];
+            }
+            m_run[t] = M;
+            l_run[t] = lt;
+        }
+        // (one instantiation per wave keeps every register index a compile-time constant)
+        f32x4_t fin[RT][DTW];
+        auto finalise = [&](auto wc) {
+            constexpr int W = decltype(wc)::value;
+#pragma unroll
+            for (int k = 0; k < DTW; ++k) {
+                const int dt = W * DTW + k;
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) {
+                        f32x4_t x;
+                        if (w == W) {
+                            x = o[t][dt];
+                        } else {
+                            const int jw = dt < w * DTW ? dt : dt - DTW;  // dt's index among w's exported tiles
+                            x = xo[((w * (DT - DTW) + jw) * RT + t) * 64 + lane];
+                        }
+                        acc += fac[w][t] * x;
+                    }
+                    fin[t][k] = acc;
+                }
+            }
+        };
+        switch (wave) {
+            case 0: finalise(std::integral_constant<int, 0>{}); break;
+            case 1: finalise(std::integral_constant<int, 1>{}); break;
+            case 2: finalise(std::integral_constant<int, 2>{}); break;
+            default: finalise(std::integral_constant<int, 3>{}); break;
+        }
+
+        // ---- output
+        const bool whole = ustart >= begin && uend <= end;
+        if (whole) {
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const int row = rg * R + 16 * t + lr;
+                if (row >= nrows) continue;
+                const int node = row / G, h = g * G + row % G;
+                const size_t orow = static_cast<size_t>(ns0 + node) * a.hq + h;
+                const float inv = 1.f / l_run[t];
+#pragma unroll
+                for (int k = 0; k < DTW; ++k) {
+                    const f32x4_t val = fin[t][k] * inv;
+                    const size_t off = orow * D + 16 * (wave * DTW + k) + 4 * lq;
+                    *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(a.out) + off) =
+                        u32x2_t{ev::pack_bf16x2(val[0], val[1]), ev::pack_bf16x2(val[2], val[3])};
+                }
+                if (a.lse && wave == 0 && lq == 0) a.lse[orow] = (m_run[t] + __log2f(l_run[t])) * kLn2;
+            }
+            continue;
+        }
+        // split unit: publish this piece's partial; the merge launch combines the unit's pieces
+        const int w1 = wg_of(ustart, S, P);
+        {
+            float *slot = slot_of_piece(a.part, w1, wl - w1, R * D + 2 * R);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+#pragma unroll
+                for (int k = 0; k < DTW; ++k)
+                    *reinterpret_cast<f32x4_t *>(slot + (16 * t + lr) * D + 16 * (wave * DTW + k) + 4 * lq) = fin[t][k];
+                if (wave == 0 && lq == 0) {
+                    slot[R * D + 16 * t + lr] = m_run[t];
+                    slot[R * D + R + 16 * t + lr] = l_run[t];
+                }
+            }
+        }
+        if (wl == w1 && tid == 0) a.table[wl] = int4{wg_of(uend - 1, S, P) - w1 + 1, b, ui, 0};
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel_ks(const AttnArgs a) {
+    attention_ks_body<D>(a);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Merge of split units (second launch; the launch boundary makes the published partials visible).
+// Block (w, t, half): if logical workgroup w holds the first piece of a split unit, combine the
+// unit's pieces for row tile t and one half of the d columns: M = max_i m_i, O = sum_i 2^(m_i - M)
+// O_i / sum_i 2^(m_i - M) l_i, in piece order (deterministic).  16 rows x D/8 threads, one float4
+// of O each.
+template <int D, bool F32OUT>
+__global__ __launch_bounds__(2 * D) void tree_attention_merge_kernel(const AttnArgs a, int R) {
+    const int4 e = a.table[blockIdx.x];
+    const int npieces = e.x;
+    if (npieces == 0) return;
+    constexpr int CT = D / 8;                  // threads per row (float4 chunks per half row)
+    const int rr = threadIdx.x / CT, c = threadIdx.x % CT;
+    const int b = e.y, ui = e.z;
+    const int rg = ui / a.hkv, g = ui % a.hkv;
+    const int G = a.group;
+    const int ns0 = a.node_start[b];
+    const int n = a.node_start[b + 1] - ns0;
+    const int r = 16 * blockIdx.y + rr;        // row within the unit
+    const int row = rg * R + r;
+    if (r >= R || row >= n * G) return;
+    const int d0 = blockIdx.z * (D / 2) + 4 * c;
+    const int slot_floats = R * D + 2 * R;
+    const int w1 = blockIdx.x;
+    float M = -INFINITY;
+    for (int i = 0; i < npieces; ++i) M = fmaxf(M, slot_of_piece(a.part, w1, i, slot_floats)[R * D + r]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+    constexpr int BATCH = 8;
+    for (int i0 = 0; i0 < npieces; i0 += BATCH) {
+        f32x4_t x[BATCH];
+        float mi[BATCH], li[BATCH];
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            const int i = i0 + k < npieces ? i0 + k : i0;
+            const float *slot = slot_of_piece(a.part, w1, i, slot_floats);
+            x[k] = *reinterpret_cast<const f32x4_t *>(slot + r * D + d0);
+            mi[k] = slot[R * D + r];
+            li[k] = slot[R * D + R + r];
+        }
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            if (i0 + k >= npieces) break;
+            const float f = __builtin_amdgcn_exp2f(mi[k] - Mu);
+            acc += f * x[k];
+            l += f * li[k];
+        }
+    }
+    const int node = row / G, h = g * G + row % G;
+    const size_t orow = static_cast<size_t>(ns0 + node) * a.hq + h;
+    const f32x4_t val = acc * (1.f / l);
+    if constexpr (F32OUT) {
+        *reinterpret_cast<f32x4_t *>(static_cast<float *>(a.out) + orow * D + d0) = val;
+    } else {
+        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(a.out) + orow * D + d0) =
+            u32x2_t{ev::pack_bf16x2(val[0], val[1]), ev::pack_bf16x2(val[2], val[3])};
+    }
+    if (a.lse && blockIdx.z == 0 && c == 0) a.lse[orow] = (M + __log2f(l)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------------------------
 struct Plan {
     int RT, R, RG;
     size_t slot_floats;
-    size_t counters_bytes;
+    size_t table_bytes;
     size_t bytes;
 };
 
@@ -866,8 +1301,8 @@ Plan make_plan(int32_t batch, int32_t max_nodes, int32_t hq, int32_t hkv, int32_
     p.R = 16 * p.RT;
     p.RG = (rows + p.R - 1) / p.R;
     p.slot_floats = static_cast<size_t>(p.R) * head_dim + 2 * p.R;
-    p.counters_bytes = ((static_cast<size_t>(kMergeLevels) * 2 * kMaxGrid * 4 + 255) / 256) * 256;
-    p.bytes = p.counters_bytes + 2 * static_cast<size_t>(kMaxGrid) * p.slot_floats * 4;
+    p.table_bytes = static_cast<size_t>(kMaxGrid) * sizeof(int4);
+    p.bytes = p.table_bytes + 2 * static_cast<size_t>(kMaxGrid) * p.slot_floats * 4;
     return p;
 }
 
@@ -885,6 +1320,7 @@ KernelFn pick_rt(int rt) {
 }
 
 KernelFn pick_kernel(int head_dim, int rt, bool f32) {
+    if (rt == kMaxRowTiles && !f32) return head_dim == 64 ? tree_attention_kernel_ks<64> : tree_attention_kernel_ks<128>;
     if (head_dim == 64) return f32 ? pick_rt<64, true>(rt) : pick_rt<64, false>(rt);
     return f32 ? pick_rt<128, true>(rt) : pick_rt<128, false>(rt);
 }
@@ -973,9 +1409,19 @@ extern "C" ev_status ev_tree_attention(const void *q, const void *k_cache, const
     args.group = num_q_heads / num_kv_heads;
     args.row_groups = plan.RG;
     args.scale_log2 = sm_scale * kLog2e;
-    args.counters = static_cast<int32_t *>(workspace);
-    args.part = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + plan.counters_bytes);
+    args.table = static_cast<int4 *>(workspace);
+    args.part = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + plan.table_bytes);
     args.err_flag = err_flag;
     hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, args);
+    if (grid > 1) {  // units split over workgroups: combine their pieces
+        const dim3 mgrid(static_cast<unsigned>(grid), static_cast<unsigned>(plan.RT), 2u);
+        if (head_dim == 64) {
+            if (f32) hipLaunchKernelGGL((tree_attention_merge_kernel<64, true>), mgrid, dim3(128), 0, stream, args, plan.R);
+            else hipLaunchKernelGGL((tree_attention_merge_kernel<64, false>), mgrid, dim3(128), 0, stream, args, plan.R);
+        } else {
+            if (f32) hipLaunchKernelGGL((tree_attention_merge_kernel<128, true>), mgrid, dim3(256), 0, stream, args, plan.R);
+            else hipLaunchKernelGGL((tree_attention_merge_kernel<128, false>), mgrid, dim3(256), 0, stream, args, plan.R);
+        }
+    }
     return ev::launch_status();
 }

@@ -97,10 +97,11 @@ const char *ev_status_string(ev_status status);
  *   total_slots           slots in the cache (bounds check)
  *   head_dim              64 or 128;  num_q_heads % num_kv_heads == 0
  *   sm_scale              finite and > 0 (EV_ERR_SHAPE otherwise)
- *   workspace             >= ev_tree_attention_workspace_size(...) bytes, ZEROED ONCE by the
- *                         caller before its first use; every call leaves it reusable (its
- *                         counters are back at zero when the call's work completes).  Calls
- *                         that share one workspace must be ordered (same stream).
+ *   workspace             >= ev_tree_attention_workspace_size(...) bytes of device memory; no
+ *                         initialisation needed (every call writes what it later reads).  It
+ *                         holds the partial results of sequences split over workgroups, which a
+ *                         second launch on the same stream combines.  Calls that share one
+ *                         workspace must be ordered (same stream).
  * Data errors (EV_DATA_BAD_PARENT / _NODES / _SLOTS): the sequence's rows are not written.
  * -------------------------------------------------------------------------------------------*/
 size_t ev_tree_attention_workspace_size(int32_t batch, int32_t max_nodes, int32_t num_q_heads,
