@@ -59,7 +59,8 @@ struct AttnArgs {
     int64_t total_slots;
     int32_t batch, total_nodes, max_nodes, hq, hkv, group, row_groups;
     float scale_log2;  // sm_scale * log2(e) > 0: scores live in the base-2 domain
-    int4 *table;       // [grid] per logical workgroup: the split unit whose first piece it holds
+    int4 *table;       // [grid] per logical workgroup: {pieces, first node, nodes, unit index} of the
+                       // split unit whose first piece it holds (pieces = 0: none)
     float *part;       // [2 * kMaxGrid] partial-result slots
     int32_t *err_flag;
 };
@@ -746,7 +747,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
                 }
             }
         }
-        if (wl == w1 && tid == 0) a.table[wl] = int4{wg_of(uend - 1, S, P) - w1 + 1, b, ui, 0};
+        if (wl == w1 && tid == 0) a.table[wl] = int4{wg_of(uend - 1, S, P) - w1 + 1, ns0, n, ui};
     }
 }
 
@@ -785,8 +786,11 @@ struct LayKS {
     static constexpr int NB = 4;                          // buffers per wave
     static constexpr int kScan = 4 * EV_MAX_BATCH;
     static constexpr int kMisc = 32;
+    static constexpr int kPar = kWaves * 4 * EV_MAX_NODES;  // each wave's copy of the parents
+    static constexpr int kQ = R * ROWB;                   // the unit's Q rows (bf16, swizzled like K)
     static constexpr int kBufs = kWaves * NB * WBUF;
-    static constexpr int kTotal = kScan + kMisc + kBufs;
+    static constexpr int kTotal = kScan + kMisc + kPar + kQ + kBufs;
+    static_assert(kTotal <= 160 * 1024, "LDS");
     static constexpr int DTW = D / 16 / kWaves;           // d tiles each wave finalises
     static constexpr int XO = kWaves * (D / 16 - DTW) * RT * 64 * 16;  // merge exchange bytes
     static_assert(XO + 2 * kWaves * R * 4 <= kBufs, "merge exchange space");
@@ -824,6 +828,39 @@ template <> struct ReadKV<64> {
 #undef EV_RK
 #undef EV_RV
 
+// The Q^T operands of all five row tiles from the staged Q rows: q[t][s] at a[s] + t * 16 rows.
+#define EV_RQ(o, a, off) "ds_read_b128 %" #o ", %" #a " offset:" #off "\n\t"
+template <int D> struct ReadQ;
+template <> struct ReadQ<128> {  // 16 rows = 4096 bytes
+    __device__ static __forceinline__ void run(bf16x8_t (&q)[5][4], const uint32_t (&a)[4]) {
+        asm volatile(EV_RQ(0, 20, 0) EV_RQ(1, 21, 0) EV_RQ(2, 22, 0) EV_RQ(3, 23, 0)
+                     EV_RQ(4, 20, 4096) EV_RQ(5, 21, 4096) EV_RQ(6, 22, 4096) EV_RQ(7, 23, 4096)
+                     EV_RQ(8, 20, 8192) EV_RQ(9, 21, 8192) EV_RQ(10, 22, 8192) EV_RQ(11, 23, 8192)
+                     EV_RQ(12, 20, 12288) EV_RQ(13, 21, 12288) EV_RQ(14, 22, 12288) EV_RQ(15, 23, 12288)
+                     EV_RQ(16, 20, 16384) EV_RQ(17, 21, 16384) EV_RQ(18, 22, 16384) EV_RQ(19, 23, 16384)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(q[0][0]), "=&v"(q[0][1]), "=&v"(q[0][2]), "=&v"(q[0][3]), "=&v"(q[1][0]),
+                       "=&v"(q[1][1]), "=&v"(q[1][2]), "=&v"(q[1][3]), "=&v"(q[2][0]), "=&v"(q[2][1]),
+                       "=&v"(q[2][2]), "=&v"(q[2][3]), "=&v"(q[3][0]), "=&v"(q[3][1]), "=&v"(q[3][2]),
+                       "=&v"(q[3][3]), "=&v"(q[4][0]), "=&v"(q[4][1]), "=&v"(q[4][2]), "=&v"(q[4][3])
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                     : "memory");
+    }
+};
+template <> struct ReadQ<64> {  // 16 rows = 2048 bytes
+    __device__ static __forceinline__ void run(bf16x8_t (&q)[5][2], const uint32_t (&a)[2]) {
+        asm volatile(EV_RQ(0, 10, 0) EV_RQ(1, 11, 0) EV_RQ(2, 10, 2048) EV_RQ(3, 11, 2048)
+                     EV_RQ(4, 10, 4096) EV_RQ(5, 11, 4096) EV_RQ(6, 10, 6144) EV_RQ(7, 11, 6144)
+                     EV_RQ(8, 10, 8192) EV_RQ(9, 11, 8192)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(q[0][0]), "=&v"(q[0][1]), "=&v"(q[1][0]), "=&v"(q[1][1]), "=&v"(q[2][0]),
+                       "=&v"(q[2][1]), "=&v"(q[3][0]), "=&v"(q[3][1]), "=&v"(q[4][0]), "=&v"(q[4][1])
+                     : "v"(a[0]), "v"(a[1])
+                     : "memory");
+    }
+};
+#undef EV_RQ
+
 constexpr float kRescaleSlack = 8.f;  // log2 of the largest probability allowed before a rescale
 
 template <int D>
@@ -850,7 +887,9 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::kTotal];
     int32_t *s_cum = reinterpret_cast<int32_t *>(smem);
     int32_t *s_misc = reinterpret_cast<int32_t *>(smem + Lay::kScan);
-    unsigned char *bufs = smem + Lay::kScan + Lay::kMisc;
+    unsigned char *pbufs = smem + Lay::kScan + Lay::kMisc;               // [wave][64] int32 parents
+    unsigned char *qbuf = pbufs + Lay::kPar;                             // [80 rows][D] bf16
+    unsigned char *bufs = qbuf + Lay::kQ;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches only
@@ -918,50 +957,89 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
             for (int dt = 0; dt < DT; ++dt)
                 voff[dt] = SUB + r0 * ROWB + 32 * (dt ^ (fv(r0) >> 1)) + 16 * ((lr & 3) >> 1) + 8 * (lr & 1);
         }
-        // this wave's quarter of stage st (keys st*64 + 16*wave + 0..15) into buffer bi
+        // this wave's quarter of stage st (keys st*64 + 16*wave + 0..15) into buffer bi: a uniform
+        // block address plus loop-invariant lane offsets; rows past the unit (only in the block
+        // that crosses its end) read row 0 instead, a finite row that the mask removes
+        const uint32_t slot_bytes = static_cast<uint32_t>(slot_stride) * 2;
+        uint32_t doff[PERW];
+#pragma unroll
+        for (int i = 0; i < PERW; ++i) {
+            const bool isv = i >= PERK;
+            const int row = (isv ? i - PERK : i) * RPI + lane / CPR;
+            doff[i] = row * slot_bytes + 16 * ((lane % CPR) ^ (isv ? fv(row) : fk(row)));
+        }
+        const char *kb8 = reinterpret_cast<const char *>(kbase);
+        const char *vb8 = reinterpret_cast<const char *>(vbase);
         auto issue = [&](int st, int bi) {
             unsigned char *buf = wbuf + bi * WBUF;
+            const int kp0 = st * KST + 16 * wave;
+            if (kp0 + 16 <= kv_end) {
+                const size_t boff = static_cast<size_t>(kp0) * slot_bytes;
 #pragma unroll
-            for (int i = 0; i < PERW; ++i) {
-                const bool isv = i >= PERK;
-                const int local = isv ? i - PERK : i;
-                const int row = local * RPI + lane / CPR;
-                const int c = (lane % CPR) ^ (isv ? fv(row) : fk(row));
-                const int kp = st * KST + 16 * wave + row;
-                const int kpc = kp < kv_end ? kp : 0;     // rows past the unit: any finite row (masked)
-                const uint16_t *src = (isv ? vbase : kbase) + static_cast<size_t>(kpc) * slot_stride + 8 * c;
-                __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(buf + (isv ? SUB : 0) + local * 1024), 16, 0, 0);
+                for (int i = 0; i < PERW; ++i) {
+                    const bool isv = i >= PERK;
+                    const char *src = (isv ? vb8 : kb8) + boff + doff[i];
+                    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(buf + (isv ? SUB : 0) + (isv ? i - PERK : i) * 1024),
+                                                     16, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < PERW; ++i) {
+                    const bool isv = i >= PERK;
+                    const int local = isv ? i - PERK : i;
+                    const int row = local * RPI + lane / CPR;
+                    const int c = (lane % CPR) ^ (isv ? fv(row) : fk(row));
+                    const int kp = kp0 + row;
+                    const int kpc = kp < kv_end ? kp : 0;
+                    const char *src = (isv ? vb8 : kb8) + static_cast<size_t>(kpc) * slot_bytes + 16 * c;
+                    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(buf + (isv ? SUB : 0) + local * 1024), 16, 0, 0);
+                }
             }
         };
 
-        // ---- the piece's loads, in the order they are needed: the parents, this wave's first
-        // stage, the Q^T operands of all five tiles (rows past the unit read a real row: their
-        // results are never written), then the next NB-1 stages (indices clamped into the piece).
-        // The count is fixed, so waiting for Q below leaves only the later stages in flight.
-        int par = -1;
-        if (lane < n) par = a.parent[ns0 + lane];
-        // every wave is done with the previous piece's use of the buffers (a bare barrier: the
-        // parents' load stays in flight)
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // ---- the piece's loads, all global -> LDS (no register loads to wait for): this wave's
+        // copy of the parents, its share of the unit's Q rows (rows past the unit read a real
+        // row: their results are never written), then its first NB stages (indices clamped into
+        // the piece, so the count is fixed).  Waiting for the first stage covers the rest.
+        // Every wave is done with the previous piece's buffers and Q rows first.  (The builtin wait
+        // costs nothing here -- the unit's geometry loads above are complete -- but it tells the
+        // compiler that no earlier load is pending, so it adds no wait among the loads below.)
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
         bare_barrier();
-        issue(st0, 0);
-        bf16x8_t qop[RT][KS];
-        int tnode[RT];
+        unsigned char *pbuf = pbufs + wave * 4 * EV_MAX_NODES;
+        __builtin_amdgcn_global_load_lds(a.parent + ns0 + min(lane, n - 1), (lds_void_t *)pbuf, 4, 0, 0);
+        {
+            constexpr int NQ = Lay::kQ / 1024;                   // 1-KB wave loads of Q rows
 #pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            const int row = rg * R + 16 * t + lr;
-            const bool live = row < nrows;
-            tnode[t] = live ? row / G : -1;
-            const int node = live ? row / G : 0;
-            const int h = g * G + (live ? row % G : 0);
-            const size_t qoff = (static_cast<size_t>(ns0 + node) * a.hq + h) * D;
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                qop[t][s] = __builtin_bit_cast(bf16x8_t, ev::ld16(static_cast<const uint16_t *>(a.q) + qoff + 32 * s + 8 * lq));
+            for (int k0 = 0; k0 < NQ; k0 += NW) {
+                const int k = k0 + wave;
+                if (k < NQ) {
+                    const int r = k * RPI + lane / CPR;            // row within the unit
+                    const int c = (lane % CPR) ^ fk(r);
+                    const int row = rg * R + r;
+                    const bool live = row < nrows;
+                    const int node = live ? row / G : 0;
+                    const int h = g * G + (live ? row % G : 0);
+                    const uint16_t *src = static_cast<const uint16_t *>(a.q) +
+                                          (static_cast<size_t>(ns0 + node) * a.hq + h) * D + 8 * c;
+                    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(qbuf + k * 1024), 16, 0, 0);
+                }
+            }
         }
 #pragma unroll
-        for (int i = 1; i < NB; ++i) issue(st0 + min(i, nst - 1), i);
-
+        for (int i = 0; i < NB; ++i) issue(st0 + min(i, nst - 1), i);
+        vm_wait_n<(NB - 1) * PERW>();
+        bare_barrier();  // every wave's share of the Q rows has landed
+        int par;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(par) : "v"(lds_addr(pbuf) + 4 * lane) : "memory");
+        if (lane >= n) par = -1;
+        bf16x8_t qop[RT][KS];
+        {
+            uint32_t qa[KS];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) qa[s] = lds_addr(qbuf) + koff[s];
+            ReadQ<D>::run(qop, qa);
+        }
         // ---- tree: validity and ancestor masks, while the loads are in flight
         const bool ok = lane >= n || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
         if (__any(!ok)) {
@@ -976,26 +1054,15 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
             const int pj = __shfl(par, j >= 0 ? j : 0, 64);
             j = j >= 0 ? pj : -1;
         }
-        uint64_t rmask[RT];
         f32x4_t o[RT][DT];
         float m_run[RT], l_run[RT];
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
-            const int node = tnode[t] >= 0 ? tnode[t] : 0;
-            const uint32_t mlo = __shfl(static_cast<uint32_t>(anc), node, 64);
-            const uint32_t mhi = __shfl(static_cast<uint32_t>(anc >> 32), node, 64);
-            rmask[t] = tnode[t] >= 0 ? ((static_cast<uint64_t>(mhi) << 32) | mlo) : 0ull;
             m_run[t] = -INFINITY;
             l_run[t] = 0.f;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        // Q is complete before the stage loop (the loop then only waits for its own stage loads)
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-#pragma unroll
-            for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qop[t][s]));
-
         // P^T operands (bf16) from the scores with the current maxima, per-lane row sums, and
         // O^T += V^T P^T over the block's 16 keys
         auto accumulate = [&](const f32x4_t (&sc)[RT], const u32x2_t (&vq)[DT]) {
@@ -1057,13 +1124,20 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
                 }
                 if (kb + 16 > L) {  // the block reaches the tree slots or the unit's end
 #pragma unroll
-                    for (int t = 0; t < RT; ++t)
+                    for (int t = 0; t < RT; ++t) {
+                        // ancestor mask of this lane's row (rows past the unit see nothing)
+                        const int row = rg * R + 16 * t + lr;
+                        const int node = row < nrows ? row / G : 0;
+                        const uint32_t mlo = __shfl(static_cast<uint32_t>(anc), node, 64);
+                        const uint32_t mhi = __shfl(static_cast<uint32_t>(anc >> 32), node, 64);
+                        const uint64_t rmask = row < nrows ? ((static_cast<uint64_t>(mhi) << 32) | mlo) : 0ull;
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int p = kb + 4 * lq + r;
-                            const bool vis = p < L || (p < kv_end && ((rmask[t] >> (p - L)) & 1ull));
+                            const bool vis = p < L || (p < kv_end && ((rmask >> (p - L)) & 1ull));
                             if (!vis) sc[t][r] = -INFINITY;
                         }
+                    }
                 }
                 // running maxima move only when a score exceeds them by more than the slack
                 bool need = false;
@@ -1215,7 +1289,7 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
                 }
             }
         }
-        if (wl == w1 && tid == 0) a.table[wl] = int4{wg_of(uend - 1, S, P) - w1 + 1, b, ui, 0};
+        if (wl == w1 && tid == 0) a.table[wl] = int4{wg_of(uend - 1, S, P) - w1 + 1, ns0, n, ui};
     }
 }
 
@@ -1226,53 +1300,57 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel_ks(const At
 
 // ---------------------------------------------------------------------------------------------
 // Merge of split units (second launch; the launch boundary makes the published partials visible).
-// Block (w, t, half): if logical workgroup w holds the first piece of a split unit, combine the
-// unit's pieces for row tile t and one half of the d columns: M = max_i m_i, O = sum_i 2^(m_i - M)
-// O_i / sum_i 2^(m_i - M) l_i, in piece order (deterministic).  16 rows x D/8 threads, one float4
-// of O each.
-template <int D, bool F32OUT>
-__global__ __launch_bounds__(2 * D) void tree_attention_merge_kernel(const AttnArgs a, int R) {
-    const int4 e = a.table[blockIdx.x];
-    const int npieces = e.x;
-    if (npieces == 0) return;
+// A resident grid: every block compacts the table's split units in LDS, then the blocks stride
+// over the work items (unit, row tile, half of the d columns).  An item combines the unit's
+// pieces: M = max_i m_i, O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i, in piece order
+// (deterministic), 16 rows x D/8 threads with one float4 of O each.
+constexpr int kMergeBlocks = 512;
+
+template <int D, int BATCH, bool F32OUT>
+__device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int4 e, int t, int half) {
     constexpr int CT = D / 8;                  // threads per row (float4 chunks per half row)
     const int rr = threadIdx.x / CT, c = threadIdx.x % CT;
-    const int b = e.y, ui = e.z;
+    const int npieces = e.x, ns0 = e.y, n = e.z, ui = e.w;
     const int rg = ui / a.hkv, g = ui % a.hkv;
     const int G = a.group;
-    const int ns0 = a.node_start[b];
-    const int n = a.node_start[b + 1] - ns0;
-    const int r = 16 * blockIdx.y + rr;        // row within the unit
-    const int row = rg * R + r;
-    if (r >= R || row >= n * G) return;
-    const int d0 = blockIdx.z * (D / 2) + 4 * c;
+    const int r = 16 * t + rr;                 // row within the unit (every slot has R rows)
+    const int d0 = half * (D / 2) + 4 * c;
     const int slot_floats = R * D + 2 * R;
-    const int w1 = blockIdx.x;
-    float M = -INFINITY;
-    for (int i = 0; i < npieces; ++i) M = fmaxf(M, slot_of_piece(a.part, w1, i, slot_floats)[R * D + r]);
-    const float Mu = M == -INFINITY ? 0.f : M;
+    // one pass in batches of independent loads; the running maximum moves between batches
+    float M = -INFINITY, l = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
-    constexpr int BATCH = 8;
     for (int i0 = 0; i0 < npieces; i0 += BATCH) {
+        const float *slot[BATCH];
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) slot[k] = slot_of_piece(a.part, w1, i0 + k < npieces ? i0 + k : i0, slot_floats);
         f32x4_t x[BATCH];
         float mi[BATCH], li[BATCH];
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
-            const int i = i0 + k < npieces ? i0 + k : i0;
-            const float *slot = slot_of_piece(a.part, w1, i, slot_floats);
-            x[k] = *reinterpret_cast<const f32x4_t *>(slot + r * D + d0);
-            mi[k] = slot[R * D + r];
-            li[k] = slot[R * D + R + r];
+            x[k] = *reinterpret_cast<const f32x4_t *>(slot[k] + r * D + d0);
+            mi[k] = slot[k][R * D + r];
+            li[k] = slot[k][R * D + R + r];
         }
+        // (an empty asm that takes every loaded value: no use of one moves above a later load)
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) asm volatile("" : "+v"(x[k]), "+v"(mi[k]), "+v"(li[k]));
+        float mb = M;
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) mb = fmaxf(mb, i0 + k < npieces ? mi[k] : -INFINITY);
+        const float mu = mb == -INFINITY ? 0.f : mb;
+        const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mu);
+        acc *= alpha;
+        l *= alpha;
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
-            if (i0 + k >= npieces) break;
-            const float f = __builtin_amdgcn_exp2f(mi[k] - Mu);
+            const float f = i0 + k < npieces ? __builtin_amdgcn_exp2f(mi[k] - mu) : 0.f;
             acc += f * x[k];
             l += f * li[k];
         }
+        M = mb;
     }
+    const int row = rg * R + r;
+    if (row >= n * G) return;                  // rows past the unit's nodes
     const int node = row / G, h = g * G + row % G;
     const size_t orow = static_cast<size_t>(ns0 + node) * a.hq + h;
     const f32x4_t val = acc * (1.f / l);
@@ -1282,7 +1360,41 @@ __global__ __launch_bounds__(2 * D) void tree_attention_merge_kernel(const AttnA
         *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(a.out) + orow * D + d0) =
             u32x2_t{ev::pack_bf16x2(val[0], val[1]), ev::pack_bf16x2(val[2], val[3])};
     }
-    if (a.lse && blockIdx.z == 0 && c == 0) a.lse[orow] = (M + __log2f(l)) * kLn2;
+    if (a.lse && half == 0 && c == 0) a.lse[orow] = (M + __log2f(l)) * kLn2;
+}
+
+template <int D, bool F32OUT>
+__global__ __launch_bounds__(2 * D, 2) void tree_attention_merge_kernel(const AttnArgs a, int R, int RT, int entries) {
+    constexpr int NT = 2 * D;
+    __shared__ int s_idx[kMaxGrid];
+    __shared__ int s_cnt[NT / 64 + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // compact the table's split units (same order in every block)
+    int base = 0;
+    for (int e0 = 0; e0 < entries; e0 += NT) {
+        const int e = e0 + tid;
+        const bool act = e < entries && a.table[e].x > 0;
+        const uint64_t bal = __ballot(act);
+        const int before = __popcll(bal & ((1ull << lane) - 1));
+        if (lane == 0) s_cnt[wave] = __popcll(bal);
+        __syncthreads();
+        int off = base;
+        for (int w = 0; w < wave; ++w) off += s_cnt[w];
+        if (act) s_idx[off + before] = e;
+        int tot = 0;
+        for (int w = 0; w < NT / 64; ++w) tot += s_cnt[w];
+        base += tot;
+        __syncthreads();
+    }
+    const int items = base * RT * 2;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int u = it / (RT * 2), t = (it / 2) % RT, half = it % 2;
+        const int w1 = s_idx[u];
+        const int4 e = a.table[w1];
+        if (e.x <= 8) merge_item<D, 8, F32OUT>(a, R, w1, e, t, half);
+        else if (e.x <= 16) merge_item<D, 16, F32OUT>(a, R, w1, e, t, half);
+        else merge_item<D, 32, F32OUT>(a, R, w1, e, t, half);
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1414,13 +1526,14 @@ extern "C" ev_status ev_tree_attention(const void *q, const void *k_cache, const
     args.err_flag = err_flag;
     hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, args);
     if (grid > 1) {  // units split over workgroups: combine their pieces
-        const dim3 mgrid(static_cast<unsigned>(grid), static_cast<unsigned>(plan.RT), 2u);
+        const dim3 mgrid(static_cast<unsigned>(kMergeBlocks));
+        const int g32 = static_cast<int>(grid);
         if (head_dim == 64) {
-            if (f32) hipLaunchKernelGGL((tree_attention_merge_kernel<64, true>), mgrid, dim3(128), 0, stream, args, plan.R);
-            else hipLaunchKernelGGL((tree_attention_merge_kernel<64, false>), mgrid, dim3(128), 0, stream, args, plan.R);
+            if (f32) hipLaunchKernelGGL((tree_attention_merge_kernel<64, true>), mgrid, dim3(128), 0, stream, args, plan.R, plan.RT, g32);
+            else hipLaunchKernelGGL((tree_attention_merge_kernel<64, false>), mgrid, dim3(128), 0, stream, args, plan.R, plan.RT, g32);
         } else {
-            if (f32) hipLaunchKernelGGL((tree_attention_merge_kernel<128, true>), mgrid, dim3(256), 0, stream, args, plan.R);
-            else hipLaunchKernelGGL((tree_attention_merge_kernel<128, false>), mgrid, dim3(256), 0, stream, args, plan.R);
+            if (f32) hipLaunchKernelGGL((tree_attention_merge_kernel<128, true>), mgrid, dim3(256), 0, stream, args, plan.R, plan.RT, g32);
+            else hipLaunchKernelGGL((tree_attention_merge_kernel<128, false>), mgrid, dim3(256), 0, stream, args, plan.R, plan.RT, g32);
         }
     }
     return ev::launch_status();

@@ -72,3 +72,15 @@ def test_no_vmcnt0_drain_before_transpose_reads(asm):
                 if nxt and nxt[0].startswith("ds_read_b64_tr_b16"):
                     bad.append(name[:60])
     assert not bad, f"vmcnt(0) right before the transpose reads in: {bad}"
+
+
+def test_merge_kernels_use_no_scratch(asm):
+    """The split-merge kernels keep their batches in registers (a scratch-backed batch array made
+    every load a round trip through memory)."""
+    text = "\n".join(asm)
+    found = 0
+    for m in re.finditer(r"\.agpr_count:\s+\d+.*?\.name:\s+(\S+).*?\.private_segment_fixed_size:\s+(\d+)", text, re.S):
+        if "merge_kernel" in m.group(1):
+            found += 1
+            assert int(m.group(2)) == 0, f"{m.group(1)} uses {m.group(2)} bytes of scratch"
+    assert found >= 4
