@@ -19,7 +19,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = 8;                        // elements per thread per load group
 constexpr int kSegQuantum = kThreads * kChunk;   // segment lengths are multiples of this
-constexpr int kTargetBlocks = 1024;
+constexpr int kTargetBlocks = 2048;
+constexpr int kSplitQuanta = 8;                  // a split of few rows: 8 quanta, one load batch per thread
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 typedef short ss2 __attribute__((ext_vector_type(2)));
@@ -101,16 +102,20 @@ __global__ __launch_bounds__(kThreads) void node_argmax_kernel(const ArgmaxArgs 
                 }
             }
         };
-        // main body: four 16-byte loads in flight per thread
+        // main body: eight 16-byte loads in flight per thread (a split of 8 quanta is one round trip)
+        for (; base + 7 * kSegQuantum + kChunk <= v1; base += 8 * kSegQuantum) {
+            u32x4_t w[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) w[k] = ev::ld16_stream(rp + base + k * kSegQuantum);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) consume(w[k], base + k * kSegQuantum);
+        }
         for (; base + 3 * kSegQuantum + kChunk <= v1; base += 4 * kSegQuantum) {
-            const u32x4_t w0 = ev::ld16_stream(rp + base);
-            const u32x4_t w1 = ev::ld16_stream(rp + base + kSegQuantum);
-            const u32x4_t w2 = ev::ld16_stream(rp + base + 2 * kSegQuantum);
-            const u32x4_t w3 = ev::ld16_stream(rp + base + 3 * kSegQuantum);
-            consume(w0, base);
-            consume(w1, base + kSegQuantum);
-            consume(w2, base + 2 * kSegQuantum);
-            consume(w3, base + 3 * kSegQuantum);
+            u32x4_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = ev::ld16_stream(rp + base + k * kSegQuantum);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) consume(w[k], base + k * kSegQuantum);
         }
         for (; base + kChunk <= v1; base += kSegQuantum) consume(ev::ld16_stream(rp + base), base);
         if (base < v1) {  // ragged end of the row: element by element
@@ -174,7 +179,7 @@ struct ArgmaxPlan {
 ArgmaxPlan make_plan(int32_t rows, int32_t vocab) {
     ArgmaxPlan p{};
     int splits = rows >= kTargetBlocks ? 1 : (kTargetBlocks + rows - 1) / rows;
-    const int max_by_len = (vocab + 4 * kSegQuantum - 1) / (4 * kSegQuantum);  // >= 4 quanta each
+    const int max_by_len = (vocab + kSplitQuanta * kSegQuantum - 1) / (kSplitQuanta * kSegQuantum);
     if (splits > max_by_len) splits = max_by_len;
     if (splits < 1) splits = 1;
     int seg = (vocab + splits - 1) / splits;

@@ -1391,7 +1391,9 @@ __global__ __launch_bounds__(2 * D, 2) void tree_attention_merge_kernel(const At
         const int u = it / (RT * 2), t = (it / 2) % RT, half = it % 2;
         const int w1 = s_idx[u];
         const int4 e = a.table[w1];
-        if (e.x <= 8) merge_item<D, 8, F32OUT>(a, R, w1, e, t, half);
+        if (e.x <= 2) merge_item<D, 2, F32OUT>(a, R, w1, e, t, half);
+        else if (e.x <= 4) merge_item<D, 4, F32OUT>(a, R, w1, e, t, half);
+        else if (e.x <= 8) merge_item<D, 8, F32OUT>(a, R, w1, e, t, half);
         else if (e.x <= 16) merge_item<D, 16, F32OUT>(a, R, w1, e, t, half);
         else merge_item<D, 32, F32OUT>(a, R, w1, e, t, half);
     }
