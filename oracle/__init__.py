@@ -65,6 +65,15 @@ def _bind(lib):
     lib.oracle_tree_attention_rows.restype = None
     lib.oracle_tree_attention_rows.argtypes = [_P, _P, _P, _I32, _P, _P, _P, _P, _I32, _I32, _I64, _I32,
                                                _I32, _I32, _D, _P, _I64, _P, _P]
+    lib.oracle_tree_attention_ex.restype = None
+    lib.oracle_tree_attention_ex.argtypes = [_P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                             _I64, _I32, _I32, _I32, _D, _P, _P, _P]
+    lib.oracle_tree_attention_rows_ex.restype = None
+    lib.oracle_tree_attention_rows_ex.argtypes = [_P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                                  _I32, _I64, _I32, _I32, _I32, _D, _P, _I64, _P, _P]
+    lib.oracle_compact_kv_paged.restype = None
+    lib.oracle_compact_kv_paged.argtypes = [_P, _P, _P, _P, _I32, _I32, _I64, _P, _I32, _I32, _P, _P, _P, _I32,
+                                            _I32, _I64, _I32, _I32, _P, _P]
     lib.oracle_node_argmax.restype = None
     lib.oracle_node_argmax.argtypes = [_P, _I32, _I64, _I32, _I32, _P, _P]
     lib.oracle_greedy_accept.restype = None
@@ -108,16 +117,29 @@ def ancestor_path(parent, i: int, lib=None) -> np.ndarray:
     return out[:n].copy()
 
 
+def _layout(kv_start, block_table, page_size):
+    """(kv_start, block_table, bt_stride, page_size) arguments of the C oracle."""
+    if block_table is None:
+        return _i32(kv_start), None, 0, 0
+    bt = _i32(block_table)
+    assert bt.ndim == 2 and page_size >= 1
+    ks = _i32(kv_start) if kv_start is not None else np.zeros(bt.shape[0], np.int32)
+    return ks, bt, bt.shape[1], int(page_size)
+
+
 def tree_attention(q, k, v, node_start, parent, kv_start, prefix_len, *, num_q_heads: int,
                    num_kv_heads: int, head_dim: int, sm_scale: float, total_slots: int,
-                   max_nodes: int = None, lib=None):
+                   max_nodes: int = None, window: int = 0, block_table=None, page_size: int = 0, lib=None):
     """Every row.  Returns (out [T, Hq, D] float64, lse [T, Hq] float64, seq_err [B] int32).
-    Rows of sequences with data errors hold NaN."""
+    Rows of sequences with data errors hold NaN.  window > 0: only the last `window` prefix tokens
+    are visible.  block_table [B, pages] with page_size: paged caches ([rows, Hkv, D], token t of
+    sequence b at row block_table[b, t // page_size] * page_size + t % page_size; kv_start unused)."""
     lib = lib or load()
     q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
     dt = _dtype_of(q)
     assert _dtype_of(k) == dt and _dtype_of(v) == dt
-    node_start, parent, kv_start, prefix_len = map(_i32, (node_start, parent, kv_start, prefix_len))
+    node_start, parent, prefix_len = map(_i32, (node_start, parent, prefix_len))
+    kv_start, bt, bts, pgs = _layout(kv_start, block_table, page_size)
     B = len(prefix_len)
     T = int(node_start[-1]) if len(node_start) else 0
     if max_nodes is None:
@@ -126,21 +148,23 @@ def tree_attention(q, k, v, node_start, parent, kv_start, prefix_len, *, num_q_h
     out = np.full((T, num_q_heads, head_dim), np.nan)
     lse = np.full((T, num_q_heads), np.nan)
     err = np.zeros(max(B, 1), dtype=np.int32)
-    lib.oracle_tree_attention(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(node_start), _ptr(parent), _ptr(kv_start),
-                              _ptr(prefix_len), B, max_nodes, int(total_slots), num_q_heads, num_kv_heads,
-                              head_dim, float(sm_scale), _ptr(out), _ptr(lse), _ptr(err))
+    lib.oracle_tree_attention_ex(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(node_start), _ptr(parent), _ptr(kv_start),
+                                 _ptr(prefix_len), _ptr(bt) if bt is not None else None, bts, pgs, int(window), B,
+                                 max_nodes, int(total_slots), num_q_heads, num_kv_heads, head_dim, float(sm_scale),
+                                 _ptr(out), _ptr(lse), _ptr(err))
     return out, lse, err[:B]
 
 
 def tree_attention_rows(q, k, v, node_start, parent, kv_start, prefix_len, rows, *, num_q_heads: int,
                         num_kv_heads: int, head_dim: int, sm_scale: float, total_slots: int,
-                        max_nodes: int = None, lib=None):
+                        max_nodes: int = None, window: int = 0, block_table=None, page_size: int = 0, lib=None):
     """Selected rows only: ``rows`` is an int array [R, 2] of (global node, q head).
     Returns (out [R, D] float64, lse [R] float64)."""
     lib = lib or load()
     q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
     dt = _dtype_of(q)
-    node_start, parent, kv_start, prefix_len = map(_i32, (node_start, parent, kv_start, prefix_len))
+    node_start, parent, prefix_len = map(_i32, (node_start, parent, prefix_len))
+    kv_start, bt, bts, pgs = _layout(kv_start, block_table, page_size)
     rows = _i32(rows).reshape(-1, 2)
     B = len(prefix_len)
     if max_nodes is None:
@@ -148,10 +172,10 @@ def tree_attention_rows(q, k, v, node_start, parent, kv_start, prefix_len, rows,
     R = rows.shape[0]
     out = np.full((R, head_dim), np.nan)
     lse = np.full(R, np.nan)
-    lib.oracle_tree_attention_rows(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(node_start), _ptr(parent),
-                                   _ptr(kv_start), _ptr(prefix_len), B, max_nodes, int(total_slots),
-                                   num_q_heads, num_kv_heads, head_dim, float(sm_scale), _ptr(rows), R,
-                                   _ptr(out), _ptr(lse))
+    lib.oracle_tree_attention_rows_ex(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(node_start), _ptr(parent),
+                                      _ptr(kv_start), _ptr(prefix_len), _ptr(bt) if bt is not None else None, bts,
+                                      pgs, int(window), B, max_nodes, int(total_slots), num_q_heads, num_kv_heads,
+                                      head_dim, float(sm_scale), _ptr(rows), R, _ptr(out), _ptr(lse))
     return out, lse
 
 
@@ -208,4 +232,28 @@ def compact_kv(k, v, kv_start, prefix_len, accept_len, accept_path, *, num_layer
     lib.oracle_compact_kv(_ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out), elem, num_layers, layer_stride,
                           _ptr(kv_start), _ptr(prefix_len), _ptr(accept_len), _ptr(accept_path), B, max_nodes,
                           int(total_slots), num_kv_heads, head_dim, _ptr(new_len), _ptr(err))
+    return k_out, v_out, new_len[:B], err[:B]
+
+
+def compact_kv_paged(k, v, block_table, page_size: int, prefix_len, accept_len, accept_path, *, num_layers: int,
+                     total_rows: int, num_kv_heads: int, head_dim: int, lib=None):
+    """Out-of-place compaction of paged caches shaped [layers, total_rows, Hkv, D]: token t of sequence
+    b sits at row block_table[b, t // page_size] * page_size + t % page_size.
+    Returns (k_out, v_out, new_len [B], seq_err [B])."""
+    lib = lib or load()
+    k, v = np.ascontiguousarray(k), np.ascontiguousarray(v)
+    bt = _i32(block_table)
+    prefix_len, accept_len = map(_i32, (prefix_len, accept_len))
+    accept_path = _i32(accept_path)
+    B = len(prefix_len)
+    max_nodes = accept_path.shape[1] if accept_path.ndim == 2 else 1
+    elem = k.dtype.itemsize
+    layer_stride = total_rows * num_kv_heads * head_dim * elem
+    assert k.nbytes == num_layers * layer_stride and v.nbytes == k.nbytes
+    k_out, v_out = np.empty_like(k), np.empty_like(v)
+    new_len = np.zeros(max(B, 1), np.int32)
+    err = np.zeros(max(B, 1), np.int32)
+    lib.oracle_compact_kv_paged(_ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out), elem, num_layers, layer_stride, _ptr(bt),
+                                bt.shape[1], int(page_size), _ptr(prefix_len), _ptr(accept_len), _ptr(accept_path), B,
+                                max_nodes, int(total_rows), num_kv_heads, head_dim, _ptr(new_len), _ptr(err))
     return k_out, v_out, new_len[:B], err[:B]

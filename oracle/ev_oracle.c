@@ -77,43 +77,79 @@ int32_t oracle_ancestor_path(const int32_t *parent, int32_t i, int32_t *path) {
     return n;
 }
 
-static int32_t seq_layout_errors(const int32_t *kv_start, const int32_t *prefix_len, int32_t b,
-                                 int32_t n, int64_t total_slots) {
-    if (kv_start[b] < 0 || prefix_len[b] < 0) return 8;
-    if ((int64_t)kv_start[b] + prefix_len[b] + n > total_slots) return 8;
+/* Cache row of logical token t of sequence b (token t = prefix position t; tree node j sits at
+   t = L + j).  Contiguous caches: row kv_start[b] + t.  Paged caches (block_table != NULL):
+   page block_table[b * bt_stride + t / page_size], row t % page_size inside it. */
+static int64_t token_slot(const int32_t *kv_start, const int32_t *block_table, int32_t bt_stride,
+                          int32_t page_size, int32_t b, int64_t t) {
+    if (block_table)
+        return (int64_t)block_table[(int64_t)b * bt_stride + t / page_size] * page_size + t % page_size;
+    return (int64_t)kv_start[b] + t;
+}
+
+/* First prefix token a query sees: the last `window` tokens only when a window is set. */
+static int32_t first_visible(int32_t L, int32_t window) { return (window > 0 && L > window) ? L - window : 0; }
+
+static int32_t seq_layout_errors(const int32_t *kv_start, const int32_t *prefix_len, const int32_t *block_table,
+                                 int32_t bt_stride, int32_t page_size, int32_t window, int32_t b, int32_t n,
+                                 int64_t total_slots) {
+    if (prefix_len[b] < 0) return 8;
+    if (!block_table) {
+        if (kv_start[b] < 0) return 8;
+        if ((int64_t)kv_start[b] + prefix_len[b] + n > total_slots) return 8;
+        return 0;
+    }
+    /* every page the visible tokens and the tree use must exist */
+    const int64_t t_end = (int64_t)prefix_len[b] + n;
+    if ((t_end + page_size - 1) / page_size > bt_stride) return 8;
+    for (int64_t t = first_visible(prefix_len[b], window); t < t_end; ++t) {
+        const int32_t pg = block_table[(int64_t)b * bt_stride + t / page_size];
+        if (pg < 0 || (int64_t)pg * page_size >= total_slots) return 8;
+    }
     return 0;
 }
 
 /* Per-sequence validity for attention: tree rule and slot range. */
-void oracle_attention_errors(const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
-                             const int32_t *prefix_len, int32_t batch, int32_t max_nodes,
+static void attention_errors(const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                             const int32_t *prefix_len, const int32_t *block_table, int32_t bt_stride,
+                             int32_t page_size, int32_t window, int32_t batch, int32_t max_nodes,
                              int64_t total_slots, int32_t *seq_err) {
     for (int32_t b = 0; b < batch; ++b) {
         int32_t n = node_start[b + 1] - node_start[b];
         int32_t e = oracle_tree_errors(parent + node_start[b], n, max_nodes);
-        if (!(e & 2)) e |= seq_layout_errors(kv_start, prefix_len, b, n, total_slots);
+        if (!(e & 2))
+            e |= seq_layout_errors(kv_start, prefix_len, block_table, bt_stride, page_size, window, b, n, total_slots);
         seq_err[b] = e;
     }
 }
 
+void oracle_attention_errors(const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                             const int32_t *prefix_len, int32_t batch, int32_t max_nodes,
+                             int64_t total_slots, int32_t *seq_err) {
+    attention_errors(node_start, parent, kv_start, prefix_len, NULL, 0, 0, 0, batch, max_nodes, total_slots,
+                     seq_err);
+}
+
 /* Attention of one (sequence b, local node i, q head h) row.
-   Visible keys: prefix slots s0 + t for 0 <= t < L, then tree slots s0 + L + j for every j in
-   anc(i).  scores = sm_scale * <q, k>;  out = sum_t e^{s_t - m} v_t / sum_t e^{s_t - m};
+   Visible keys: the prefix tokens t0 <= t < L (t0 = 0, or L - window with a sliding window of the
+   drafter's kind), then the tree tokens L + j for every j in anc(i), each at its cache row
+   (token_slot).  scores = sm_scale * <q, k>;  out = sum_t e^{s_t - m} v_t / sum_t e^{s_t - m};
    lse = m + ln sum_t e^{s_t - m}. */
 static void attention_row(const void *q, const void *k, const void *v, int dtype, const int32_t *node_start,
                           const int32_t *parent, const int32_t *kv_start, const int32_t *prefix_len,
+                          const int32_t *bt, int32_t bt_stride, int32_t page, int32_t window,
                           int32_t b, int32_t i, int32_t h, int32_t hq, int32_t hkv, int32_t d,
                           double sm_scale, double *out, double *lse, double *scratch, int64_t *slots) {
     const int32_t G = hq / hkv;
     const int32_t g = h / G;
     const int32_t L = prefix_len[b];
-    const int64_t s0 = kv_start[b];
+    const int32_t t0 = first_visible(L, window);
     const int32_t *par = parent + node_start[b];
     int32_t path[1024];
     int32_t np = oracle_ancestor_path(par, i, path);
     int64_t nvis = 0;
-    for (int32_t t = 0; t < L; ++t) slots[nvis++] = s0 + t;
-    for (int32_t t = 0; t < np; ++t) slots[nvis++] = s0 + L + path[t];
+    for (int32_t t = t0; t < L; ++t) slots[nvis++] = token_slot(kv_start, bt, bt_stride, page, b, t);
+    for (int32_t t = 0; t < np; ++t) slots[nvis++] = token_slot(kv_start, bt, bt_stride, page, b, L + path[t]);
 
     const size_t qrow = ((size_t)(node_start[b] + i) * hq + h) * d;
     double m = -INFINITY;
@@ -139,14 +175,18 @@ static void attention_row(const void *q, const void *k, const void *v, int dtype
 }
 
 /* A list of rows: rows[2r] = global node index, rows[2r+1] = q head.  out [nrows, d], lse [nrows].
-   Rows of sequences with data errors are left untouched. */
-void oracle_tree_attention_rows(const void *q, const void *k, const void *v, int32_t dtype,
-                                const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
-                                const int32_t *prefix_len, int32_t batch, int32_t max_nodes,
-                                int64_t total_slots, int32_t hq, int32_t hkv, int32_t d, double sm_scale,
-                                const int32_t *rows, int64_t nrows, double *out, double *lse) {
+   Rows of sequences with data errors are left untouched.  block_table == NULL: contiguous caches
+   (kv_start used); else paged caches of page_size rows per page (kv_start unused); total_slots =
+   rows of the cache.  window > 0: the sliding window. */
+void oracle_tree_attention_rows_ex(const void *q, const void *k, const void *v, int32_t dtype,
+                                   const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                                   const int32_t *prefix_len, const int32_t *block_table, int32_t bt_stride,
+                                   int32_t page_size, int32_t window, int32_t batch, int32_t max_nodes,
+                                   int64_t total_slots, int32_t hq, int32_t hkv, int32_t d, double sm_scale,
+                                   const int32_t *rows, int64_t nrows, double *out, double *lse) {
     int32_t *seq_err = (int32_t *)calloc(batch > 0 ? batch : 1, sizeof(int32_t));
-    oracle_attention_errors(node_start, parent, kv_start, prefix_len, batch, max_nodes, total_slots, seq_err);
+    attention_errors(node_start, parent, kv_start, prefix_len, block_table, bt_stride, page_size, window, batch,
+                     max_nodes, total_slots, seq_err);
     int32_t maxvis = 0;
     for (int32_t b = 0; b < batch; ++b) {
         int32_t n = node_start[b + 1] - node_start[b];
@@ -162,8 +202,9 @@ void oracle_tree_attention_rows(const void *q, const void *k, const void *v, int
             int32_t b = 0;
             while (b + 1 <= batch && node_start[b + 1] <= node) ++b;
             if (seq_err[b]) continue;
-            attention_row(q, k, v, dtype, node_start, parent, kv_start, prefix_len, b, node - node_start[b], h,
-                          hq, hkv, d, sm_scale, out + (size_t)r * d, lse + r, scratch, slots);
+            attention_row(q, k, v, dtype, node_start, parent, kv_start, prefix_len, block_table, bt_stride,
+                          page_size, window, b, node - node_start[b], h, hq, hkv, d, sm_scale,
+                          out + (size_t)r * d, lse + r, scratch, slots);
         }
         free(scratch);
         free(slots);
@@ -171,22 +212,43 @@ void oracle_tree_attention_rows(const void *q, const void *k, const void *v, int
     free(seq_err);
 }
 
+void oracle_tree_attention_rows(const void *q, const void *k, const void *v, int32_t dtype,
+                                const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                                const int32_t *prefix_len, int32_t batch, int32_t max_nodes,
+                                int64_t total_slots, int32_t hq, int32_t hkv, int32_t d, double sm_scale,
+                                const int32_t *rows, int64_t nrows, double *out, double *lse) {
+    oracle_tree_attention_rows_ex(q, k, v, dtype, node_start, parent, kv_start, prefix_len, NULL, 0, 0, 0, batch,
+                                  max_nodes, total_slots, hq, hkv, d, sm_scale, rows, nrows, out, lse);
+}
+
 /* Every row: out [total_nodes, hq, d], lse [total_nodes, hq]. */
-void oracle_tree_attention(const void *q, const void *k, const void *v, int32_t dtype,
-                           const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
-                           const int32_t *prefix_len, int32_t batch, int32_t max_nodes, int64_t total_slots,
-                           int32_t hq, int32_t hkv, int32_t d, double sm_scale, double *out, double *lse,
-                           int32_t *seq_err) {
-    oracle_attention_errors(node_start, parent, kv_start, prefix_len, batch, max_nodes, total_slots, seq_err);
+void oracle_tree_attention_ex(const void *q, const void *k, const void *v, int32_t dtype,
+                              const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                              const int32_t *prefix_len, const int32_t *block_table, int32_t bt_stride,
+                              int32_t page_size, int32_t window, int32_t batch, int32_t max_nodes,
+                              int64_t total_slots, int32_t hq, int32_t hkv, int32_t d, double sm_scale, double *out,
+                              double *lse, int32_t *seq_err) {
+    attention_errors(node_start, parent, kv_start, prefix_len, block_table, bt_stride, page_size, window, batch,
+                     max_nodes, total_slots, seq_err);
     const int64_t total = (int64_t)node_start[batch] * hq;
     int32_t *rows = (int32_t *)malloc(sizeof(int32_t) * 2 * (total > 0 ? total : 1));
     for (int64_t r = 0; r < total; ++r) {
         rows[2 * r] = (int32_t)(r / hq);
         rows[2 * r + 1] = (int32_t)(r % hq);
     }
-    oracle_tree_attention_rows(q, k, v, dtype, node_start, parent, kv_start, prefix_len, batch, max_nodes,
-                               total_slots, hq, hkv, d, sm_scale, rows, total, out, lse);
+    oracle_tree_attention_rows_ex(q, k, v, dtype, node_start, parent, kv_start, prefix_len, block_table, bt_stride,
+                                  page_size, window, batch, max_nodes, total_slots, hq, hkv, d, sm_scale, rows,
+                                  total, out, lse);
     free(rows);
+}
+
+void oracle_tree_attention(const void *q, const void *k, const void *v, int32_t dtype,
+                           const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                           const int32_t *prefix_len, int32_t batch, int32_t max_nodes, int64_t total_slots,
+                           int32_t hq, int32_t hkv, int32_t d, double sm_scale, double *out, double *lse,
+                           int32_t *seq_err) {
+    oracle_tree_attention_ex(q, k, v, dtype, node_start, parent, kv_start, prefix_len, NULL, 0, 0, 0, batch,
+                             max_nodes, total_slots, hq, hkv, d, sm_scale, out, lse, seq_err);
 }
 
 /* Greedy target token of every logits row: the lowest index holding the row maximum.
@@ -292,5 +354,53 @@ void oracle_compact_kv(const void *k_in, const void *v_in, void *k_out, void *v_
             }
         }
         new_len[b] = prefix_len[b] + len;
+    }
+}
+
+/* Paged KV compaction, out of place: caches [layers][total_rows][hkv][d] where a sequence's token
+   t sits at page block_table[b * bt_stride + t / page_size], row t % page_size; for every layer and
+   0 <= d < len, token L + d of the output takes token L + path[d] of the INPUT (the pages may
+   differ).  new_len = L + len.  A sequence with len <= 0 is left alone (new_len = L). */
+void oracle_compact_kv_paged(const void *k_in, const void *v_in, void *k_out, void *v_out, int32_t elem_bytes,
+                             int32_t num_layers, int64_t layer_stride_bytes, const int32_t *block_table,
+                             int32_t bt_stride, int32_t page_size, const int32_t *prefix_len,
+                             const int32_t *accept_len, const int32_t *accept_path, int32_t batch,
+                             int32_t max_nodes, int64_t total_rows, int32_t hkv, int32_t d, int32_t *new_len,
+                             int32_t *seq_err) {
+    const size_t bytes = (size_t)num_layers * (size_t)layer_stride_bytes;
+    memcpy(k_out, k_in, bytes);
+    memcpy(v_out, v_in, bytes);
+    const size_t row = (size_t)hkv * d * elem_bytes; /* one token: all KV heads */
+    for (int32_t b = 0; b < batch; ++b) {
+        const int32_t len = accept_len[b];
+        const int32_t *path = accept_path + (size_t)b * max_nodes;
+        int32_t err = 0;
+        new_len[b] = prefix_len[b];
+        if (len <= 0) { seq_err[b] = 0; continue; }
+        if (len > max_nodes || path[0] != 0) err |= 16;
+        for (int32_t t = 1; t < len && !err; ++t)
+            if (path[t] <= path[t - 1]) err |= 16;
+        if (!err && prefix_len[b] < 0) err |= 8;
+        if (!err && ((int64_t)prefix_len[b] + path[len - 1]) / page_size >= bt_stride) err |= 8;
+        for (int32_t t = 0; t < len && !err; ++t) {
+            const int64_t tok[2] = {(int64_t)prefix_len[b] + t, (int64_t)prefix_len[b] + path[t]};
+            for (int u = 0; u < 2; ++u) {
+                const int32_t pg = block_table[(int64_t)b * bt_stride + tok[u] / page_size];
+                if (pg < 0 || (int64_t)pg * page_size >= total_rows) err |= 8;
+            }
+        }
+        seq_err[b] = err;
+        if (err) continue;
+        const int64_t L = prefix_len[b];
+        for (int32_t l = 0; l < num_layers; ++l) {
+            const size_t lo = (size_t)l * layer_stride_bytes;
+            for (int32_t t = 0; t < len; ++t) {
+                const size_t dst = lo + (size_t)token_slot(NULL, block_table, bt_stride, page_size, b, L + t) * row;
+                const size_t src = lo + (size_t)token_slot(NULL, block_table, bt_stride, page_size, b, L + path[t]) * row;
+                memcpy((char *)k_out + dst, (const char *)k_in + src, row);
+                memcpy((char *)v_out + dst, (const char *)v_in + src, row);
+            }
+        }
+        new_len[b] = (int32_t)(L + len);
     }
 }

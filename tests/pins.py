@@ -7,6 +7,7 @@ mistake (dropped term, wrong sign or index, swapped operand, wrong tie-break) fa
 """
 from __future__ import annotations
 
+import copy
 import math
 import os
 
@@ -275,3 +276,136 @@ def pin_tree_rules(lib):
 
 
 ALL_PINS = (pin_attention, pin_argmax, pin_accept, pin_compact, pin_tree_rules)
+
+
+def _window_attn(w, lib, window, **kw):
+    return oracle.tree_attention(w.q, w.k, w.v, w.node_start, w.parent, w.kv_start, w.prefix_len,
+                                 num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                                 sm_scale=w.sm_scale, total_slots=w.total_slots, max_nodes=max(w.max_nodes, 1),
+                                 window=window, lib=lib, **kw)
+
+
+def pin_window(lib):
+    """Sliding-window attention (only the last W prefix tokens are visible, plus the node's own
+    ancestors): SDPA with the explicit mask, the plain oracle on a prefix truncated to its last W
+    tokens, and W >= L equal to no window."""
+    w = small_tree_workload(61, dtype=BF16, prefix=(0, 3, 40, 97), nodes=(6, 16, 9, 12), sm_scale=0.7)
+    base, base_lse, _ = _attn(w, lib)
+    same, same_lse, _ = _window_attn(w, lib, 97)
+    assert np.array_equal(same, base) and np.array_equal(same_lse, base_lse), "window >= L changed results"
+    for W in (1, 5, 32):
+        out, lse, err = _window_attn(w, lib, W)
+        assert (err == 0).all()
+        for b in range(w.batch):
+            s, e = int(w.node_start[b]), int(w.node_start[b + 1])
+            L = int(w.prefix_len[b])
+            mask = bf.visible_mask(w.parent[s:e], L)
+            mask[:, :max(0, L - W)] = False
+            _close(out[s:e], bf.attention_seq_sdpa(w, b, mask=mask), rtol=1e-8, atol=1e-10, what=f"window {W} sdpa")
+        # the same rows from a cache whose prefix starts W tokens before the tree
+        cut = copy.deepcopy(w)
+        Lf = cut.prefix_len.copy()
+        cut.prefix_len = np.minimum(Lf, W).astype(np.int32)
+        cut.kv_start = (cut.kv_start + (Lf - cut.prefix_len)).astype(np.int32)
+        ref, ref_lse, _ = _attn(cut, lib)
+        assert np.array_equal(out, ref) and np.array_equal(lse, ref_lse), f"window {W} != truncated prefix"
+
+
+def paged_copy(w, page_size: int, seed: int, spare_pages: int = 3):
+    """The workload's caches scattered over randomly placed pages: returns (k_pool, v_pool,
+    block_table [B, pages]).  Token t of sequence b lands at row bt[b, t // P] * P + t % P."""
+    rng = np.random.default_rng(seed)
+    need = [(int(w.prefix_len[b]) + int(w.node_start[b + 1] - w.node_start[b]) + page_size - 1) // page_size
+            for b in range(w.batch)]
+    total = sum(need) + spare_pages
+    order = rng.permutation(total)
+    width = max(need) + 1
+    bt = np.full((w.batch, width), -7, np.int32)          # unused entries hold garbage
+    pool_k = np.zeros((total * page_size,) + w.k.shape[1:], w.k.dtype)
+    pool_v = np.zeros_like(pool_k)
+    pool_k[:] = rng.integers(0, 1 << 14, pool_k.shape).astype(w.k.dtype)
+    pool_v[:] = rng.integers(0, 1 << 14, pool_v.shape).astype(w.v.dtype)
+    nxt = 0
+    for b in range(w.batch):
+        s0 = int(w.kv_start[b])
+        ntok = int(w.prefix_len[b]) + int(w.node_start[b + 1] - w.node_start[b])
+        for p in range(need[b]):
+            bt[b, p] = order[nxt]
+            nxt += 1
+        for t in range(ntok):
+            row = bt[b, t // page_size] * page_size + t % page_size
+            pool_k[row] = w.k[s0 + t]
+            pool_v[row] = w.v[s0 + t]
+    return pool_k, pool_v, bt
+
+
+def pin_paged(lib):
+    """Paged caches: scattering a workload's tokens over random pages changes nothing (bit for
+    bit, with and without a window), and a page index outside the pool is a data error."""
+    for seed, dtype, P in ((71, BF16, 4), (72, F32, 16), (73, BF16, 1)):
+        w = small_tree_workload(seed, dtype=dtype, prefix=(0, 5, 33, 64), nodes=(7, 16, 3, 11))
+        pk, pv, bt = paged_copy(w, P, seed)
+        for W in (0, 9):
+            ref, ref_lse, _ = _window_attn(w, lib, W)
+            out, lse, err = oracle.tree_attention(w.q, pk, pv, w.node_start, w.parent, None, w.prefix_len,
+                                                  num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                                                  head_dim=w.head_dim, sm_scale=w.sm_scale, total_slots=pk.shape[0],
+                                                  max_nodes=max(w.max_nodes, 1), window=W, block_table=bt,
+                                                  page_size=P, lib=lib)
+            assert (err == 0).all()
+            assert np.array_equal(out, ref) and np.array_equal(lse, ref_lse), f"paged P={P} W={W}"
+        bad = bt.copy()
+        bad[2, 0] = pk.shape[0] // P                         # one past the pool
+        _, _, err = oracle.tree_attention(w.q, pk, pv, w.node_start, w.parent, None, w.prefix_len,
+                                          num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                                          sm_scale=w.sm_scale, total_slots=pk.shape[0], max_nodes=max(w.max_nodes, 1),
+                                          block_table=bad, page_size=P, lib=lib)
+        assert err[2] == 8 and (err[[0, 1, 3]] == 0).all(), err
+
+
+def pin_paged_compact(lib):
+    """Paged compaction moves the same bytes as contiguous compaction of the same logical data:
+    read back through the block table, every sequence's tokens agree; overlapping paths (a source
+    that is also a later destination) and pages crossed both ways included."""
+    rng = np.random.default_rng(81)
+    for P in (2, 3, 8):
+        w = small_tree_workload(81 + P, dtype=BF16, prefix=(4, 0, 13, 6), nodes=(6, 5, 16, 9))
+        B = w.batch
+        maxn = int(w.max_nodes)
+        paths = np.full((B, maxn), -1, np.int32)
+        lens = np.zeros(B, np.int32)
+        for b, path in enumerate(([0, 1, 3, 4], [0], [0, 2, 3, 7, 8, 15], [0, 1, 2, 3, 4, 5, 6, 7, 8])):
+            paths[b, :len(path)] = path
+            lens[b] = len(path)
+        pk, pv, bt = paged_copy(w, P, 90 + P)
+        layers = 2
+        k2 = np.stack([pk, rng.integers(0, 1 << 15, pk.shape).astype(pk.dtype)])
+        v2 = np.stack([pv, rng.integers(0, 1 << 15, pv.shape).astype(pv.dtype)])
+        kc = np.stack([w.k, np.zeros_like(w.k)])
+        vc = np.stack([w.v, np.zeros_like(w.v)])
+        for b in range(B):                                   # layer 1: the same tokens in both layouts
+            s0 = int(w.kv_start[b])
+            for t in range(int(w.prefix_len[b]) + int(w.node_start[b + 1] - w.node_start[b])):
+                row = bt[b, t // P] * P + t % P
+                kc[1, s0 + t] = k2[1, row]
+                vc[1, s0 + t] = v2[1, row]
+        ko, vo, nl, err = oracle.compact_kv_paged(k2, v2, bt, P, w.prefix_len, lens, paths, num_layers=layers,
+                                                  total_rows=pk.shape[0], num_kv_heads=w.num_kv_heads,
+                                                  head_dim=w.head_dim, lib=lib)
+        kr, vr, nl2, err2 = oracle.compact_kv(kc, vc, w.kv_start, w.prefix_len, lens, paths, num_layers=layers,
+                                              total_slots=w.total_slots, num_kv_heads=w.num_kv_heads,
+                                              head_dim=w.head_dim, lib=lib)
+        assert (err == 0).all() and (err2 == 0).all() and np.array_equal(nl, nl2)
+        touched = np.zeros(pk.shape[0], bool)
+        for b in range(B):
+            s0 = int(w.kv_start[b])
+            for t in range(int(w.prefix_len[b]) + int(w.node_start[b + 1] - w.node_start[b])):
+                row = bt[b, t // P] * P + t % P
+                touched[row] = True
+                for l in range(layers):
+                    assert np.array_equal(ko[l, row], kr[l, s0 + t]) and np.array_equal(vo[l, row], vr[l, s0 + t]), \
+                        f"P={P} seq {b} token {t} layer {l}"
+        assert np.array_equal(ko[:, ~touched], k2[:, ~touched]) and np.array_equal(vo[:, ~touched], v2[:, ~touched])
+
+
+ALL_PINS = ALL_PINS + (pin_window, pin_paged, pin_paged_compact)

@@ -17,8 +17,22 @@ MUTANTS = {
                               "for (int32_t j = parent[i]; j >= 0; j = parent[j]) rev[n++] = j;\n"
                               "    if (n == 0) rev[n++] = i;"),
     "gqa_modulo_mapping": ("const int32_t g = h / G;", "const int32_t g = h % hkv;"),
-    "prefix_off_by_one": ("for (int32_t t = 0; t < L; ++t) slots[nvis++] = s0 + t;",
-                          "for (int32_t t = 1; t < L; ++t) slots[nvis++] = s0 + t;"),
+    "prefix_off_by_one": ("for (int32_t t = t0; t < L; ++t) slots[nvis++] = token_slot(",
+                          "for (int32_t t = t0 + 1; t < L; ++t) slots[nvis++] = token_slot("),
+    "window_keeps_one_more": ("return (window > 0 && L > window) ? L - window : 0;",
+                              "return (window > 0 && L > window) ? L - window - 1 : 0;"),
+    "page_row_from_page_index": ("* page_size + t % page_size;", "* page_size + t / page_size;"),
+    "paged_compact_descending_in_place": (
+        "            for (int32_t t = 0; t < len; ++t) {\n"
+        "                const size_t dst = lo + (size_t)token_slot(NULL, block_table, bt_stride, page_size, b, L + t) * row;\n"
+        "                const size_t src = lo + (size_t)token_slot(NULL, block_table, bt_stride, page_size, b, L + path[t]) * row;\n"
+        "                memcpy((char *)k_out + dst, (const char *)k_in + src, row);\n"
+        "                memcpy((char *)v_out + dst, (const char *)v_in + src, row);",
+        "            for (int32_t t = len - 1; t >= 0; --t) {\n"
+        "                const size_t dst = lo + (size_t)token_slot(NULL, block_table, bt_stride, page_size, b, L + t) * row;\n"
+        "                const size_t src = lo + (size_t)token_slot(NULL, block_table, bt_stride, page_size, b, L + path[t]) * row;\n"
+        "                memcpy((char *)k_out + dst, (const char *)k_out + src, row);\n"
+        "                memcpy((char *)v_out + dst, (const char *)v_out + src, row);"),
     "softmax_sign": ("scratch[t] = exp(scratch[t] - m);", "scratch[t] = exp(m - scratch[t]);"),
     "scale_dropped": ("scratch[t] = sm_scale * dot;", "scratch[t] = dot;"),
     "k_v_swapped": ("dot += elem(q, dtype, qrow + c) * elem(k, dtype, krow + c);",
