@@ -58,6 +58,7 @@ struct AttnArgs {
     const int32_t *prefix_len;
     int64_t total_slots;
     int32_t batch, total_nodes, max_nodes, hq, hkv, group, row_groups;
+    int32_t window;    // > 0: only the last `window` prefix tokens are visible (sliding window)
     float scale_log2;  // sm_scale * log2(e) > 0: scores live in the base-2 domain
     int4 *table;       // [grid] per logical workgroup: {pieces, first node, nodes, unit index} of the
                        // split unit whose first piece it holds (pieces = 0: none)
@@ -185,6 +186,15 @@ __device__ __forceinline__ int wg_of(int64_t x, int64_t S, int P) {
     return static_cast<int>(((x + 1) * P - 1) / S);
 }
 
+// The visible prefix of sequence b: its last `window` tokens when a window is set (the
+// drafter's sliding window over its append-only cache), else all of it.  L is the visible
+// length and s0 the cache slot of its first token; the tree slots follow at s0 + L.
+__device__ __forceinline__ void visible_prefix(const AttnArgs &a, int b, int &L, int64_t &s0) {
+    const int Lf = a.prefix_len[b];
+    L = (a.window > 0 && Lf > a.window) ? a.window : Lf;
+    s0 = static_cast<int64_t>(a.kv_start[b]) + (Lf - L);
+}
+
 // Partial-result slot of piece `piece` of the split unit whose first piece is held by logical
 // workgroup w1: a workgroup holds at most two split pieces, the last piece of a unit begun
 // earlier (slot 2w) and the first piece of a unit that continues past it (slot 2w + 1).
@@ -220,7 +230,8 @@ __device__ __forceinline__ int64_t schedule_scan(const AttnArgs &a, int32_t *s_c
             if (err) {
                 if (blockIdx.x == 0) ev::flag_error(a.err_flag, err);
             } else {
-                work = a.hkv * ((n * G + R - 1) / R) * ((L + n + KST - 1) / KST);
+                const int Lv = (a.window > 0 && L > a.window) ? a.window : L;
+                work = a.hkv * ((n * G + R - 1) / R) * ((Lv + n + KST - 1) / KST);
             }
         }
         int x = work;
@@ -294,8 +305,9 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
         const int64_t seq_base = b ? s_cum[b - 1] : 0;
         const int ns0 = a.node_start[b];
         const int n = a.node_start[b + 1] - ns0;
-        const int L = a.prefix_len[b];
-        const int64_t s0 = a.kv_start[b];
+        int L;
+        int64_t s0;
+        visible_prefix(a, b, L, s0);
         const int stages = (L + n + KST - 1) / KST;
         const int ui = static_cast<int>((pos - seq_base) / stages);
         const int rg = ui / a.hkv, g = ui % a.hkv;
@@ -927,8 +939,9 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
         const int64_t seq_base = b ? s_cum[b - 1] : 0;
         const int ns0 = a.node_start[b];
         const int n = a.node_start[b + 1] - ns0;
-        const int L = a.prefix_len[b];
-        const int64_t s0 = a.kv_start[b];
+        int L;
+        int64_t s0;
+        visible_prefix(a, b, L, s0);
         const int stages = (L + n + KST - 1) / KST;
         const int ui = static_cast<int>((pos - seq_base) / stages);
         const int rg = ui / a.hkv, g = ui % a.hkv;
@@ -1467,13 +1480,13 @@ extern "C" size_t ev_tree_attention_workspace_size(int32_t batch, int32_t max_no
     return make_plan(batch, max_nodes, num_q_heads, num_kv_heads, head_dim).bytes;
 }
 
-extern "C" ev_status ev_tree_attention(const void *q, const void *k_cache, const void *v_cache, void *out, float *lse,
-                                       const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
-                                       const int32_t *prefix_len, int32_t batch, int32_t total_nodes,
-                                       int32_t max_nodes, int64_t total_slots, int32_t num_q_heads,
-                                       int32_t num_kv_heads, int32_t head_dim, ev_dtype dtype, float sm_scale,
-                                       void *workspace, size_t workspace_bytes, int32_t *err_flag,
-                                       hipStream_t stream) {
+namespace {
+ev_status launch_attention(const void *q, const void *k_cache, const void *v_cache, void *out, float *lse,
+                           const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                           const int32_t *prefix_len, int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                           int64_t total_slots, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           ev_dtype dtype, float sm_scale, int32_t window, void *workspace, size_t workspace_bytes,
+                           int32_t *err_flag, hipStream_t stream) {
     if (!q || !k_cache || !v_cache || !out || !node_start || !parent || !kv_start || !prefix_len)
         return EV_ERR_NULL;
     if (batch < 0 || batch > EV_MAX_BATCH || total_nodes < 0 || max_nodes < 1 || max_nodes > EV_MAX_NODES ||
@@ -1522,6 +1535,7 @@ extern "C" ev_status ev_tree_attention(const void *q, const void *k_cache, const
     args.hkv = num_kv_heads;
     args.group = num_q_heads / num_kv_heads;
     args.row_groups = plan.RG;
+    args.window = window;
     args.scale_log2 = sm_scale * kLog2e;
     args.table = static_cast<int4 *>(workspace);
     args.part = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + plan.table_bytes);
@@ -1539,4 +1553,30 @@ extern "C" ev_status ev_tree_attention(const void *q, const void *k_cache, const
         }
     }
     return ev::launch_status();
+}
+}  // namespace
+
+extern "C" ev_status ev_tree_attention(const void *q, const void *k_cache, const void *v_cache, void *out, float *lse,
+                                       const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                                       const int32_t *prefix_len, int32_t batch, int32_t total_nodes,
+                                       int32_t max_nodes, int64_t total_slots, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, ev_dtype dtype, float sm_scale,
+                                       void *workspace, size_t workspace_bytes, int32_t *err_flag,
+                                       hipStream_t stream) {
+    return launch_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
+                            total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype,
+                            sm_scale, 0, workspace, workspace_bytes, err_flag, stream);
+}
+
+extern "C" ev_status ev_tree_attention_window(const void *q, const void *k_cache, const void *v_cache, void *out,
+                                              float *lse, const int32_t *node_start, const int32_t *parent,
+                                              const int32_t *kv_start, const int32_t *prefix_len, int32_t batch,
+                                              int32_t total_nodes, int32_t max_nodes, int64_t total_slots,
+                                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                              ev_dtype dtype, float sm_scale, int32_t window, void *workspace,
+                                              size_t workspace_bytes, int32_t *err_flag, hipStream_t stream) {
+    if (window < 1) return EV_ERR_SHAPE;
+    return launch_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
+                            total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype,
+                            sm_scale, window, workspace, workspace_bytes, err_flag, stream);
 }

@@ -25,7 +25,8 @@ MAX_NODES = 64
 MAX_BATCH = 2048
 
 EXPORTS = ("ev_status_string", "ev_tree_attention_workspace_size", "ev_tree_attention",
-           "ev_node_argmax_workspace_size", "ev_node_argmax", "ev_greedy_accept", "ev_compact_kv")
+           "ev_tree_attention_window", "ev_node_argmax_workspace_size", "ev_node_argmax", "ev_greedy_accept",
+           "ev_compact_kv")
 
 _lib = None
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -53,6 +54,9 @@ def load(path: str = LIB_PATH):
     lib.ev_tree_attention.restype = ctypes.c_int
     lib.ev_tree_attention.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
                                       _I32, ctypes.c_int, _F, _P, _SZ, _P, _P]
+    lib.ev_tree_attention_window.restype = ctypes.c_int
+    lib.ev_tree_attention_window.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32,
+                                             _I32, _I32, ctypes.c_int, _F, _I32, _P, _SZ, _P, _P]
     lib.ev_node_argmax_workspace_size.restype = _SZ
     lib.ev_node_argmax_workspace_size.argtypes = [_I32, _I32]
     lib.ev_node_argmax.restype = ctypes.c_int
@@ -82,6 +86,15 @@ def ev_tree_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_star
     return load().ev_tree_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
                                     total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype,
                                     sm_scale, workspace, workspace_bytes, err_flag, stream)
+
+
+def ev_tree_attention_window(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
+                             total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype,
+                             sm_scale, window, workspace, workspace_bytes, err_flag, stream) -> int:
+    return load().ev_tree_attention_window(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len,
+                                           batch, total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads,
+                                           head_dim, dtype, sm_scale, window, workspace, workspace_bytes, err_flag,
+                                           stream)
 
 
 def ev_node_argmax_workspace_size(num_rows, vocab) -> int:
@@ -163,9 +176,11 @@ class Workspace:
 
 
 def tree_attention(q, k_cache, v_cache, node_start, parent, kv_start, prefix_len, *, max_nodes: int,
-                   sm_scale: float, out=None, lse=None, workspace: Workspace = None, err_flag=None, stream=None):
-    """Tree-masked GQA attention (ev_tree_attention).  q [T, Hq, D]; caches [slots, Hkv, D]; metadata int32.
-    Returns (out, lse, workspace)."""
+                   sm_scale: float, window: int = None, out=None, lse=None, workspace: Workspace = None,
+                   err_flag=None, stream=None):
+    """Tree-masked GQA attention (ev_tree_attention; ev_tree_attention_window when `window` is given:
+    only the last `window` prefix tokens are visible).  q [T, Hq, D]; caches [slots, Hkv, D];
+    metadata int32.  Returns (out, lse, workspace)."""
     torch = _torch()
     _need(q, "q", ndim=3)
     _need(k_cache, "k_cache", q.dtype, 3)
@@ -187,11 +202,13 @@ def tree_attention(q, k_cache, v_cache, node_start, parent, kv_start, prefix_len
     need = ev_tree_attention_workspace_size(B, max_nodes, Hq, Hkv, D)
     if workspace is None or workspace.nbytes < need:
         workspace = Workspace(need, q.device)
-    st = ev_tree_attention(_addr(q), _addr(k_cache), _addr(v_cache), _addr(out), _addr(lse), _addr(node_start),
-                           _addr(parent), _addr(kv_start), _addr(prefix_len), B, T, max_nodes, slots, Hq, Hkv, D,
-                           _dtype_code(q), float(sm_scale), workspace.ptr, workspace.nbytes, _addr(err_flag),
-                           _stream(stream))
-    _check(st, "ev_tree_attention")
+    ptrs = (_addr(q), _addr(k_cache), _addr(v_cache), _addr(out), _addr(lse), _addr(node_start), _addr(parent),
+            _addr(kv_start), _addr(prefix_len), B, T, max_nodes, slots, Hq, Hkv, D, _dtype_code(q), float(sm_scale))
+    tail = (workspace.ptr, workspace.nbytes, _addr(err_flag), _stream(stream))
+    if window is None:
+        _check(ev_tree_attention(*ptrs, *tail), "ev_tree_attention")
+    else:
+        _check(ev_tree_attention_window(*ptrs, int(window), *tail), "ev_tree_attention_window")
     return out, lse, workspace
 
 

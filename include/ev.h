@@ -115,6 +115,28 @@ ev_status ev_tree_attention(const void *q, const void *k_cache, const void *v_ca
                             int32_t *err_flag, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * ev_tree_attention_window
+ *
+ * ev_tree_attention with a sliding window over the prefix: the EAGLE-4 drafter's layers attend
+ * only to the most recent stretch of an append-only cache, which keeps long documents cheap
+ * (aiposthub.com analysis, section "EAGLE-4 是什麼？先看推測解碼為什麼能變快"; arex-research.com
+ * release note, section "投机树多大，由实测成本决定").  Read here as: the last `window` prefix
+ * tokens stay visible, every tree ancestor (and the node itself) stays visible whatever the
+ * window, i.e. with Lf = prefix_len[b] and L = min(Lf, window)
+ *   S(i) = { kv_start[b] + Lf - L + t : 0 <= t < L }  U  { kv_start[b] + Lf + j : j anc. of i or i }
+ * All other arguments, layouts, arithmetic and error behaviour are those of ev_tree_attention,
+ * and the same workspace size applies.  window >= 1 (EV_ERR_SHAPE otherwise); window >= Lf
+ * gives ev_tree_attention's result for that sequence.
+ * -------------------------------------------------------------------------------------------*/
+ev_status ev_tree_attention_window(const void *q, const void *k_cache, const void *v_cache, void *out,
+                                   float *lse, const int32_t *node_start, const int32_t *parent,
+                                   const int32_t *kv_start, const int32_t *prefix_len, int32_t batch,
+                                   int32_t total_nodes, int32_t max_nodes, int64_t total_slots,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, ev_dtype dtype,
+                                   float sm_scale, int32_t window, void *workspace, size_t workspace_bytes,
+                                   int32_t *err_flag, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * ev_node_argmax
  *
  * target_token[r] = the LOWEST index v in [0, vocab) holding the maximum of logits row r (the

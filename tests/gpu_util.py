@@ -57,26 +57,27 @@ def cached_config(name: str):
     return synth.make_config(name)
 
 
-def gpu_attention(w, d, sm_scale=None, err=None):
+def gpu_attention(w, d, sm_scale=None, err=None, window=None):
     from draft_tree_verification_amd import ev
     out, lse, _ = ev.tree_attention(d["q"], d["k"], d["v"], d["node_start"], d["parent"], d["kv_start"],
                                     d["prefix_len"], max_nodes=max(w.max_nodes, 1),
-                                    sm_scale=w.sm_scale if sm_scale is None else sm_scale, err_flag=err)
+                                    sm_scale=w.sm_scale if sm_scale is None else sm_scale, window=window,
+                                    err_flag=err)
     return out, lse
 
 
-def oracle_attention(w, sm_scale=None):
+def oracle_attention(w, sm_scale=None, window=0):
     return oracle.tree_attention(w.q, w.k, w.v, w.node_start, w.parent, w.kv_start, w.prefix_len,
                                  num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                                  sm_scale=w.sm_scale if sm_scale is None else sm_scale, total_slots=w.total_slots,
-                                 max_nodes=max(w.max_nodes, 1))
+                                 max_nodes=max(w.max_nodes, 1), window=window)
 
 
-def oracle_rows(w, rows, sm_scale=None):
+def oracle_rows(w, rows, sm_scale=None, window=0):
     return oracle.tree_attention_rows(w.q, w.k, w.v, w.node_start, w.parent, w.kv_start, w.prefix_len, rows,
                                       num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                                       head_dim=w.head_dim, sm_scale=w.sm_scale if sm_scale is None else sm_scale,
-                                      total_slots=w.total_slots, max_nodes=max(w.max_nodes, 1))
+                                      total_slots=w.total_slots, max_nodes=max(w.max_nodes, 1), window=window)
 
 
 def check_attention(gpu_out, ref_out, gpu_lse=None, ref_lse=None, vmax=None, what="", tight=True):
