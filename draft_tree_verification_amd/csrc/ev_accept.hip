@@ -94,46 +94,70 @@ struct CompactArgs {
     unsigned char *k, *v;
     int64_t layer_stride;
     const int32_t *kv_start, *prefix_len, *accept_len, *accept_path;
+    const int32_t *block_table;       // paged caches (else NULL): [batch][bt_stride] pool pages
+    int32_t bt_stride, page_size;
     int32_t batch, max_nodes, row16;  // row16: 16-byte chunks per slot row
-    int64_t total_slots, row_bytes;
+    int64_t total_slots, row_bytes;   // paged: total_slots = pool pages * page_size
     int32_t *new_len, *err_flag;
 };
 
 constexpr int kCompactThreads = 256;
 constexpr int kBatchRows = 8;
 
-// Block (b, layer).  Rows move in increasing d; a destination slot L+d can only be the source of
-// some d' <= d (path[d'] >= d' since the path strictly increases from 0), so every source is read
-// before anything overwrites it even though each thread streams its own columns independently.
+// Block (b, layer).  Rows move in increasing d; a destination token L+d can only be the source
+// of some d' <= d (path[d'] >= d' since the path strictly increases from 0), so every source is
+// read before anything overwrites it even though each thread streams its own columns
+// independently.  With a block table the same holds row by row as long as the sequence's pages
+// are distinct (tokens then map to distinct rows).
 __global__ __launch_bounds__(kCompactThreads) void compact_kv_kernel(const CompactArgs a) {
     const int b = blockIdx.x;
     const int layer = blockIdx.y;
     const int tid = threadIdx.x;
-    __shared__ int s_path[EV_MAX_NODES];
+    __shared__ int64_t s_src[EV_MAX_NODES], s_dst[EV_MAX_NODES];
     const int len = a.accept_len[b];
     const int L = a.prefix_len[b];
-    const int s0 = a.kv_start[b];
-    int err = 0;
+    int err = 0, p = 0;
     if (len > 0) {
         if (len > a.max_nodes) err = EV_DATA_BAD_PATH;
         if (!err && tid < len) {
-            const int p = a.accept_path[static_cast<size_t>(b) * a.max_nodes + tid];
-            s_path[tid] = p;
+            p = a.accept_path[static_cast<size_t>(b) * a.max_nodes + tid];
             const int prev = tid ? a.accept_path[static_cast<size_t>(b) * a.max_nodes + tid - 1] : -1;
             if (tid == 0 ? p != 0 : p <= prev) err = EV_DATA_BAD_PATH;
         }
     }
     err = __syncthreads_or(err) ? EV_DATA_BAD_PATH : 0;
     if (len > 0 && !err) {
-        const int last = s_path[len - 1];
-        if (s0 < 0 || L < 0 || static_cast<int64_t>(s0) + L + last >= a.total_slots) err = EV_DATA_BAD_SLOTS;
+        const int last = a.accept_path[static_cast<size_t>(b) * a.max_nodes + len - 1];
+        if (!a.block_table) {
+            const int s0 = a.kv_start[b];
+            if (s0 < 0 || L < 0 || static_cast<int64_t>(s0) + L + last >= a.total_slots) err = EV_DATA_BAD_SLOTS;
+            else if (tid < len) {
+                s_src[tid] = static_cast<int64_t>(s0) + L + p;
+                s_dst[tid] = static_cast<int64_t>(s0) + L + tid;
+            }
+        } else if (L < 0 || (static_cast<int64_t>(L) + last) / a.page_size >= a.bt_stride) {
+            err = EV_DATA_BAD_SLOTS;
+        } else {
+            int bad = 0;
+            if (tid < len) {
+                const int32_t *bt = a.block_table + static_cast<size_t>(b) * a.bt_stride;
+                const int64_t num_pages = a.total_slots / a.page_size;
+                const int64_t ts = static_cast<int64_t>(L) + p, td = static_cast<int64_t>(L) + tid;
+                const int ps = bt[ts / a.page_size], pd = bt[td / a.page_size];
+                bad = ps < 0 || ps >= num_pages || pd < 0 || pd >= num_pages;
+                s_src[tid] = static_cast<int64_t>(ps) * a.page_size + ts % a.page_size;
+                s_dst[tid] = static_cast<int64_t>(pd) * a.page_size + td % a.page_size;
+            }
+            err = __syncthreads_or(bad) ? EV_DATA_BAD_SLOTS : 0;
+        }
     }
     if (layer == 0 && tid == 0) {
         a.new_len[b] = (len > 0 && !err) ? L + len : L;
         ev::flag_error(a.err_flag, err);
     }
     if (len <= 1 || err) return;
-    const int64_t base = static_cast<int64_t>(layer) * a.layer_stride + (static_cast<int64_t>(s0) + L) * a.row_bytes;
+    __syncthreads();  // the row indices are in LDS
+    const int64_t base = static_cast<int64_t>(layer) * a.layer_stride;
     for (int c = tid; c < 2 * a.row16; c += kCompactThreads) {
         unsigned char *buf = (c < a.row16 ? a.k : a.v) + base + static_cast<int64_t>(c % a.row16) * 16;
         for (int d0 = 1; d0 < len; d0 += kBatchRows) {
@@ -141,13 +165,13 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kv_kernel(const Compa
 #pragma unroll
             for (int i = 0; i < kBatchRows; ++i) {
                 const int d = d0 + i;
-                if (d < len && s_path[d] != d) rows[i] = ev::ld16(buf + static_cast<int64_t>(s_path[d]) * a.row_bytes);
+                if (d < len && s_src[d] != s_dst[d]) rows[i] = ev::ld16(buf + s_src[d] * a.row_bytes);
             }
 #pragma unroll
             for (int i = 0; i < kBatchRows; ++i) {
                 const int d = d0 + i;
-                if (d < len && s_path[d] != d)
-                    *reinterpret_cast<u32x4_t *>(buf + static_cast<int64_t>(d) * a.row_bytes) = rows[i];
+                if (d < len && s_src[d] != s_dst[d])
+                    *reinterpret_cast<u32x4_t *>(buf + s_dst[d] * a.row_bytes) = rows[i];
             }
         }
     }
@@ -173,12 +197,15 @@ extern "C" ev_status ev_greedy_accept(const int32_t *node_start, const int32_t *
     return ev::launch_status();
 }
 
-extern "C" ev_status ev_compact_kv(void *k_cache, void *v_cache, int32_t elem_bytes, int32_t num_layers,
-                                   int64_t layer_stride_bytes, const int32_t *kv_start, const int32_t *prefix_len,
-                                   const int32_t *accept_len, const int32_t *accept_path, int32_t batch,
-                                   int32_t max_nodes, int64_t total_slots, int32_t num_kv_heads, int32_t head_dim,
-                                   int32_t *new_len, int32_t *err_flag, hipStream_t stream) {
-    if (!k_cache || !v_cache || !kv_start || !prefix_len || !accept_len || !accept_path || !new_len)
+namespace {
+ev_status launch_compact(void *k_cache, void *v_cache, int32_t elem_bytes, int32_t num_layers,
+                         int64_t layer_stride_bytes, const int32_t *kv_start, const int32_t *block_table,
+                         int32_t bt_stride, int32_t page_size, const int32_t *prefix_len, const int32_t *accept_len,
+                         const int32_t *accept_path, int32_t batch, int32_t max_nodes, int64_t total_slots,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t *new_len, int32_t *err_flag,
+                         hipStream_t stream) {
+    if (!k_cache || !v_cache || !prefix_len || !accept_len || !accept_path || !new_len ||
+        (block_table ? false : !kv_start))
         return EV_ERR_NULL;
     if (batch < 0 || num_layers < 1 || max_nodes < 1 || max_nodes > EV_MAX_NODES || total_slots < 0 ||
         num_kv_heads < 1 || head_dim < 1)
@@ -200,6 +227,9 @@ extern "C" ev_status ev_compact_kv(void *k_cache, void *v_cache, int32_t elem_by
     args.prefix_len = prefix_len;
     args.accept_len = accept_len;
     args.accept_path = accept_path;
+    args.block_table = block_table;
+    args.bt_stride = bt_stride;
+    args.page_size = page_size;
     args.batch = batch;
     args.max_nodes = max_nodes;
     args.row16 = static_cast<int32_t>(row_bytes / 16);
@@ -209,4 +239,29 @@ extern "C" ev_status ev_compact_kv(void *k_cache, void *v_cache, int32_t elem_by
     args.err_flag = err_flag;
     hipLaunchKernelGGL(compact_kv_kernel, dim3(batch, num_layers), dim3(kCompactThreads), 0, stream, args);
     return ev::launch_status();
+}
+}  // namespace
+
+extern "C" ev_status ev_compact_kv(void *k_cache, void *v_cache, int32_t elem_bytes, int32_t num_layers,
+                                   int64_t layer_stride_bytes, const int32_t *kv_start, const int32_t *prefix_len,
+                                   const int32_t *accept_len, const int32_t *accept_path, int32_t batch,
+                                   int32_t max_nodes, int64_t total_slots, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t *new_len, int32_t *err_flag, hipStream_t stream) {
+    return launch_compact(k_cache, v_cache, elem_bytes, num_layers, layer_stride_bytes, kv_start, nullptr, 0, 0,
+                          prefix_len, accept_len, accept_path, batch, max_nodes, total_slots, num_kv_heads, head_dim,
+                          new_len, err_flag, stream);
+}
+
+extern "C" ev_status ev_compact_kv_paged(void *k_pages, void *v_pages, int32_t elem_bytes, int32_t num_layers,
+                                         int64_t layer_stride_bytes, const int32_t *block_table, int32_t bt_stride,
+                                         int32_t page_size, const int32_t *prefix_len, const int32_t *accept_len,
+                                         const int32_t *accept_path, int32_t batch, int32_t max_nodes,
+                                         int32_t num_pages, int32_t num_kv_heads, int32_t head_dim, int32_t *new_len,
+                                         int32_t *err_flag, hipStream_t stream) {
+    if (!block_table) return EV_ERR_NULL;
+    if (page_size < 1 || bt_stride < 1 || num_pages < 0) return EV_ERR_SHAPE;
+    return launch_compact(k_pages, v_pages, elem_bytes, num_layers, layer_stride_bytes, nullptr, block_table,
+                          bt_stride, page_size, prefix_len, accept_len, accept_path, batch, max_nodes,
+                          static_cast<int64_t>(num_pages) * page_size, num_kv_heads, head_dim, new_len, err_flag,
+                          stream);
 }

@@ -59,6 +59,9 @@ struct AttnArgs {
     int64_t total_slots;
     int32_t batch, total_nodes, max_nodes, hq, hkv, group, row_groups;
     int32_t window;    // > 0: only the last `window` prefix tokens are visible (sliding window)
+    const int32_t *block_table;  // paged caches (else NULL): [batch][bt_stride] pool page of each
+                                 // run of 2^page_shift tokens; row = page * 2^page_shift + offset
+    int32_t bt_stride, page_shift, num_pages;
     float scale_log2;  // sm_scale * log2(e) > 0: scores live in the base-2 domain
     int4 *table;       // [grid] per logical workgroup: {pieces, first node, nodes, unit index} of the
                        // split unit whose first piece it holds (pieces = 0: none)
@@ -188,11 +191,27 @@ __device__ __forceinline__ int wg_of(int64_t x, int64_t S, int P) {
 
 // The visible prefix of sequence b: its last `window` tokens when a window is set (the
 // drafter's sliding window over its append-only cache), else all of it.  L is the visible
-// length and s0 the cache slot of its first token; the tree slots follow at s0 + L.
+// length and s0 the position of its first token: a cache slot (contiguous caches; the tree
+// slots follow at s0 + L) or a token index within the sequence (paged caches).
+template <bool PG>
 __device__ __forceinline__ void visible_prefix(const AttnArgs &a, int b, int &L, int64_t &s0) {
     const int Lf = a.prefix_len[b];
     L = (a.window > 0 && Lf > a.window) ? a.window : Lf;
-    s0 = static_cast<int64_t>(a.kv_start[b]) + (Lf - L);
+    s0 = (PG ? 0 : static_cast<int64_t>(a.kv_start[b])) + (Lf - L);
+}
+
+using const_i32_t = const __attribute__((address_space(4))) int32_t;
+
+// Paged caches: the first pool row of the page that holds token `tok` of the block-table row
+// `bt` (uniform arguments: one scalar load).  A page outside the pool raises EV_DATA_BAD_SLOTS
+// and page 0 is read instead, so no load leaves the pool.
+__device__ __forceinline__ int64_t page_row(const AttnArgs &a, const int32_t *bt, int tok) {
+    int pg = ((const_i32_t *)bt)[tok >> a.page_shift];
+    if (static_cast<unsigned>(pg) >= static_cast<unsigned>(a.num_pages)) {
+        ev::flag_error(a.err_flag, EV_DATA_BAD_SLOTS);
+        pg = 0;
+    }
+    return static_cast<int64_t>(pg) << a.page_shift;
 }
 
 // Partial-result slot of piece `piece` of the split unit whose first piece is held by logical
@@ -221,11 +240,12 @@ __device__ __forceinline__ int64_t schedule_scan(const AttnArgs &a, int32_t *s_c
         if (b < a.batch) {
             const int ns0 = a.node_start[b], ns1 = a.node_start[b + 1];
             const int n = ns1 - ns0;
-            const int L = a.prefix_len[b], s0 = a.kv_start[b];
+            const int L = a.prefix_len[b], s0 = a.block_table ? 0 : a.kv_start[b];
             int err = 0;
             if (ns0 < 0 || ns1 > a.total_nodes || n < 1 || n > a.max_nodes)
                 err = EV_DATA_BAD_NODES;
-            else if (L < 0 || s0 < 0 || static_cast<int64_t>(s0) + L + n > a.total_slots)
+            else if (a.block_table ? (L < 0 || ((static_cast<int64_t>(L) + n - 1) >> a.page_shift) >= a.bt_stride)
+                                   : (L < 0 || s0 < 0 || static_cast<int64_t>(s0) + L + n > a.total_slots))
                 err = EV_DATA_BAD_SLOTS;
             if (err) {
                 if (blockIdx.x == 0) ev::flag_error(a.err_flag, err);
@@ -253,8 +273,9 @@ __device__ __forceinline__ int64_t schedule_scan(const AttnArgs &a, int32_t *s_c
     return carry;
 }
 
-template <int D, int RT, bool F32IN>
+template <int D, int RT, bool F32IN, bool PG>
 __device__ __forceinline__ void attention_body(const AttnArgs &a) {
+    static_assert(!(PG && F32IN), "paged caches hold bf16");
     using Lay = Layout<D, RT, F32IN>;
     constexpr bool X5 = Lay::X5;
     constexpr int KST = Lay::KST;
@@ -307,7 +328,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
         const int n = a.node_start[b + 1] - ns0;
         int L;
         int64_t s0;
-        visible_prefix(a, b, L, s0);
+        visible_prefix<PG>(a, b, L, s0);
         const int stages = (L + n + KST - 1) / KST;
         const int ui = static_cast<int>((pos - seq_base) / stages);
         const int rg = ui / a.hkv, g = ui % a.hkv;
@@ -375,7 +396,10 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
 
         const int kv_end = L + n;  // unit-relative key positions below this exist
         const size_t slot_stride = static_cast<size_t>(a.hkv) * D;  // elements between slots
-        const size_t head_off = static_cast<size_t>(s0) * slot_stride + static_cast<size_t>(g) * D;
+        // paged caches: rows are found per load through the block table, s0 is a token index
+        const size_t head_off = (PG ? 0 : static_cast<size_t>(s0) * slot_stride) + static_cast<size_t>(g) * D;
+        const int32_t *bt = nullptr;
+        if constexpr (PG) bt = a.block_table + static_cast<size_t>(__builtin_amdgcn_readfirstlane(b)) * a.bt_stride;
 
         // Online-softmax update of tile slot tt from raw scores (masked entries are -inf): the
         // running max moves to the stage's max (scaled), the exponent folds the scale into one
@@ -623,8 +647,23 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
                     const int p = lane % CPR;
                     const int kp = st * KST + row;
                     const int c = p ^ (isv ? fv(row) : fk(row));
-                    const int kpc = kp < kv_end ? kp : 0;          // rows past the unit: any finite row
-                    const uint16_t *src = (isv ? vbase : kbase) + static_cast<size_t>(kpc) * slot_stride + 8 * c;
+                    const uint16_t *src;
+                    if constexpr (PG) {
+                        // this load's RPI rows span at most two pages (pages hold >= 16 tokens);
+                        // rows past the unit read its last row
+                        const int kl = kv_end - 1, kf = st * KST + local * RPI;
+                        const int t0 = static_cast<int>(s0) + min(kf, kl);
+                        const int t1 = static_cast<int>(s0) + min(kf + RPI - 1, kl);
+                        const int64_t r0 = page_row(a, bt, __builtin_amdgcn_readfirstlane(t0));
+                        const int64_t r1 = page_row(a, bt, __builtin_amdgcn_readfirstlane(t1));
+                        const int t = static_cast<int>(s0) + min(kp, kl);
+                        const int64_t r = ((t >> a.page_shift) == (t0 >> a.page_shift) ? r0 : r1) +
+                                          (t & ((1 << a.page_shift) - 1));
+                        src = (isv ? vbase : kbase) + static_cast<size_t>(r) * slot_stride + 8 * c;
+                    } else {
+                        const int kpc = kp < kv_end ? kp : 0;      // rows past the unit: any finite row
+                        src = (isv ? vbase : kbase) + static_cast<size_t>(kpc) * slot_stride + 8 * c;
+                    }
                     __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(buf + (isv ? TB : 0) + local * 1024), 16, 0,
                                                      0);
                 }
@@ -764,14 +803,14 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
 }
 
 // Up to four row tiles: 32-key stages, two workgroups per CU.
-template <int D, int RT, bool F32IN>
+template <int D, int RT, bool F32IN, bool PG>
 __global__ __launch_bounds__(kThreads, 2) void tree_attention_kernel(const AttnArgs a) {
-    attention_body<D, RT, F32IN>(a);
+    attention_body<D, RT, F32IN, PG>(a);
 }
 // 80-row units: 64-key stages, one workgroup per CU (each wave holds 1.25 tiles).
 template <int D, bool F32IN>
 __global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel5(const AttnArgs a) {
-    attention_body<D, 5, F32IN>(a);
+    attention_body<D, 5, F32IN, false>(a);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -875,7 +914,7 @@ template <> struct ReadQ<64> {  // 16 rows = 2048 bytes
 
 constexpr float kRescaleSlack = 8.f;  // log2 of the largest probability allowed before a rescale
 
-template <int D>
+template <int D, bool PG>
 __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
     using Lay = LayKS<D>;
     constexpr int R = Lay::R;
@@ -941,7 +980,7 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
         const int n = a.node_start[b + 1] - ns0;
         int L;
         int64_t s0;
-        visible_prefix(a, b, L, s0);
+        visible_prefix<PG>(a, b, L, s0);
         const int stages = (L + n + KST - 1) / KST;
         const int ui = static_cast<int>((pos - seq_base) / stages);
         const int rg = ui / a.hkv, g = ui % a.hkv;
@@ -954,9 +993,12 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
         const int kv_end = L + n;
         const int nst = st1 - st0;
         const size_t slot_stride = static_cast<size_t>(a.hkv) * D;
-        const size_t head_off = static_cast<size_t>(s0) * slot_stride + static_cast<size_t>(g) * D;
+        // paged caches: rows are found per block through the block table, s0 is a token index
+        const size_t head_off = (PG ? 0 : static_cast<size_t>(s0) * slot_stride) + static_cast<size_t>(g) * D;
         const uint16_t *kbase = static_cast<const uint16_t *>(a.k) + head_off;
         const uint16_t *vbase = static_cast<const uint16_t *>(a.v) + head_off;
+        const int32_t *bt = nullptr;
+        if constexpr (PG) bt = a.block_table + static_cast<size_t>(__builtin_amdgcn_readfirstlane(b)) * a.bt_stride;
 
         // lane offsets of the operand reads inside one buffer: K operand step s = row lr, chunk
         // 4s + lq; V^T operand d tile dt = rows 4lq + lr/4, chunk 2dt + (lr&3)/2, half lr&1
@@ -986,7 +1028,38 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
         auto issue = [&](int st, int bi) {
             unsigned char *buf = wbuf + bi * WBUF;
             const int kp0 = st * KST + 16 * wave;
-            if (kp0 + 16 <= kv_end) {
+            if constexpr (PG) {
+                // the block's tokens (rows past the unit read its last row) span at most two pages
+                const int kl = kv_end - 1;
+                const int t0 = __builtin_amdgcn_readfirstlane(static_cast<int>(s0) + min(kp0, kl));
+                const int t1 = __builtin_amdgcn_readfirstlane(static_cast<int>(s0) + min(kp0 + 15, kl));
+                const int sh = a.page_shift;
+                const int64_t r0 = page_row(a, bt, t0);
+                if (kp0 + 16 <= kv_end && (t0 >> sh) == (t1 >> sh)) {
+                    // one page: a uniform block address plus the invariant lane offsets
+                    const size_t boff = static_cast<size_t>(r0 + (t0 & ((1 << sh) - 1))) * slot_bytes;
+#pragma unroll
+                    for (int i = 0; i < PERW; ++i) {
+                        const bool isv = i >= PERK;
+                        const char *src = (isv ? vb8 : kb8) + boff + doff[i];
+                        __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(buf + (isv ? SUB : 0) + (isv ? i - PERK : i) * 1024),
+                                                         16, 0, 0);
+                    }
+                } else {
+                    const int64_t r1 = page_row(a, bt, t1);
+#pragma unroll
+                    for (int i = 0; i < PERW; ++i) {
+                        const bool isv = i >= PERK;
+                        const int local = isv ? i - PERK : i;
+                        const int row = local * RPI + lane / CPR;
+                        const int c = (lane % CPR) ^ (isv ? fv(row) : fk(row));
+                        const int t = static_cast<int>(s0) + min(kp0 + row, kl);
+                        const int64_t r = ((t >> sh) == (t0 >> sh) ? r0 : r1) + (t & ((1 << sh) - 1));
+                        const char *src = (isv ? vb8 : kb8) + static_cast<size_t>(r) * slot_bytes + 16 * c;
+                        __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(buf + (isv ? SUB : 0) + local * 1024), 16, 0, 0);
+                    }
+                }
+            } else if (kp0 + 16 <= kv_end) {
                 const size_t boff = static_cast<size_t>(kp0) * slot_bytes;
 #pragma unroll
                 for (int i = 0; i < PERW; ++i) {
@@ -1306,9 +1379,9 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
     }
 }
 
-template <int D>
+template <int D, bool PG>
 __global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel_ks(const AttnArgs a) {
-    attention_ks_body<D>(a);
+    attention_ks_body<D, PG>(a);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1435,27 +1508,31 @@ Plan make_plan(int32_t batch, int32_t max_nodes, int32_t hq, int32_t hkv, int32_
 
 using KernelFn = void (*)(AttnArgs);
 
-template <int D, bool F32IN>
+template <int D, bool F32IN, bool PG>
 KernelFn pick_rt(int rt) {
     switch (rt) {
-        case 1: return tree_attention_kernel<D, 1, F32IN>;
-        case 2: return tree_attention_kernel<D, 2, F32IN>;
-        case 3: return tree_attention_kernel<D, 3, F32IN>;
-        case 4: return tree_attention_kernel<D, 4, F32IN>;
-        default: return tree_attention_kernel5<D, F32IN>;
+        case 1: return tree_attention_kernel<D, 1, F32IN, PG>;
+        case 2: return tree_attention_kernel<D, 2, F32IN, PG>;
+        case 3: return tree_attention_kernel<D, 3, F32IN, PG>;
+        case 4: return tree_attention_kernel<D, 4, F32IN, PG>;
+        default: return tree_attention_kernel5<D, F32IN>;  // fp32 only: bf16 80-row units go key-split
     }
 }
 
-KernelFn pick_kernel(int head_dim, int rt, bool f32) {
-    if (rt == kMaxRowTiles && !f32) return head_dim == 64 ? tree_attention_kernel_ks<64> : tree_attention_kernel_ks<128>;
-    if (head_dim == 64) return f32 ? pick_rt<64, true>(rt) : pick_rt<64, false>(rt);
-    return f32 ? pick_rt<128, true>(rt) : pick_rt<128, false>(rt);
+KernelFn pick_kernel(int head_dim, int rt, bool f32, bool pg) {
+    if (rt == kMaxRowTiles && !f32) {
+        if (head_dim == 64) return pg ? tree_attention_kernel_ks<64, true> : tree_attention_kernel_ks<64, false>;
+        return pg ? tree_attention_kernel_ks<128, true> : tree_attention_kernel_ks<128, false>;
+    }
+    if (pg) return head_dim == 64 ? pick_rt<64, false, true>(rt) : pick_rt<128, false, true>(rt);
+    if (head_dim == 64) return f32 ? pick_rt<64, true, false>(rt) : pick_rt<64, false, false>(rt);
+    return f32 ? pick_rt<128, true, false>(rt) : pick_rt<128, false, false>(rt);
 }
 
 // Resident workgroups per CU for a kernel variant, cached per (device, variant).
 int blocks_per_cu(KernelFn fn, int variant) {
     static std::mutex mu;
-    static int cache[16][32] = {};
+    static int cache[16][64] = {};
     const int dev = ev::current_device();
     std::lock_guard<std::mutex> lock(mu);
     if (dev < 0 || dev >= 16) return 1;
@@ -1485,30 +1562,36 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
                            const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
                            const int32_t *prefix_len, int32_t batch, int32_t total_nodes, int32_t max_nodes,
                            int64_t total_slots, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                           ev_dtype dtype, float sm_scale, int32_t window, void *workspace, size_t workspace_bytes,
+                           ev_dtype dtype, float sm_scale, int32_t window, const int32_t *block_table,
+                           int32_t bt_stride, int32_t page_size, void *workspace, size_t workspace_bytes,
                            int32_t *err_flag, hipStream_t stream) {
-    if (!q || !k_cache || !v_cache || !out || !node_start || !parent || !kv_start || !prefix_len)
+    const bool pg = page_size > 0;  // paged caches: total_slots = pool pages * page_size
+    if (!q || !k_cache || !v_cache || !out || !node_start || !parent || !prefix_len || (pg ? !block_table : !kv_start))
         return EV_ERR_NULL;
     if (batch < 0 || batch > EV_MAX_BATCH || total_nodes < 0 || max_nodes < 1 || max_nodes > EV_MAX_NODES ||
         total_slots < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads ||
-        (head_dim != 64 && head_dim != 128) || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
+        (head_dim != 64 && head_dim != 128) || !std::isfinite(sm_scale) || !(sm_scale > 0.f) || window < 0)
         return EV_ERR_SHAPE;
     if (dtype != EV_BF16 && dtype != EV_F32) return EV_ERR_DTYPE;
+    if (pg && dtype != EV_BF16) return EV_ERR_DTYPE;
     if (!ev::aligned16(q) || !ev::aligned16(k_cache) || !ev::aligned16(v_cache) || !ev::aligned16(out))
         return EV_ERR_ALIGN;
     const Plan plan = make_plan(batch, max_nodes, num_q_heads, num_kv_heads, head_dim);
     if (!workspace || workspace_bytes < plan.bytes) return EV_ERR_WORKSPACE;
     if (!ev::aligned16(workspace)) return EV_ERR_ALIGN;
-    // stage counts are 32-bit in the kernel (32-key stages bound them from above)
-    const int64_t max_stages = static_cast<int64_t>(num_kv_heads) * plan.RG * (total_slots / 32 + 2 * batch);
+    // stage counts are 32-bit in the kernel (32-key stages bound them from above); token indices
+    // of paged sequences are 32-bit
+    const int64_t max_tokens = pg ? static_cast<int64_t>(bt_stride) * page_size * batch : total_slots;
+    const int64_t max_stages = static_cast<int64_t>(num_kv_heads) * plan.RG * (max_tokens / 32 + 2 * batch);
     if (max_stages >= (int64_t(1) << 31)) return EV_ERR_SHAPE;
+    if (pg && static_cast<int64_t>(bt_stride) * page_size >= (int64_t(1) << 31)) return EV_ERR_SHAPE;
     const ev_status dev = ev::check_device();
     if (dev != EV_OK) return dev;
     if (batch == 0 || total_nodes == 0) return EV_OK;
 
     const bool f32 = dtype == EV_F32;
-    KernelFn fn = pick_kernel(head_dim, plan.RT, f32);
-    const int variant = (head_dim == 64 ? 0 : 16) + (f32 ? 8 : 0) + plan.RT;
+    KernelFn fn = pick_kernel(head_dim, plan.RT, f32, pg);
+    const int variant = (head_dim == 64 ? 0 : 16) + (f32 ? 8 : 0) + plan.RT + (pg ? 32 : 0);
     const int resident = ev::device_cu_count() * blocks_per_cu(fn, variant);
     int64_t grid = resident;
     if (grid > kMaxGrid) grid = kMaxGrid;
@@ -1536,6 +1619,10 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
     args.group = num_q_heads / num_kv_heads;
     args.row_groups = plan.RG;
     args.window = window;
+    args.block_table = pg ? block_table : nullptr;
+    args.bt_stride = bt_stride;
+    args.page_shift = pg ? __builtin_ctz(static_cast<unsigned>(page_size)) : 0;
+    args.num_pages = pg ? static_cast<int32_t>(total_slots / page_size) : 0;
     args.scale_log2 = sm_scale * kLog2e;
     args.table = static_cast<int4 *>(workspace);
     args.part = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + plan.table_bytes);
@@ -1565,7 +1652,7 @@ extern "C" ev_status ev_tree_attention(const void *q, const void *k_cache, const
                                        hipStream_t stream) {
     return launch_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
                             total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype,
-                            sm_scale, 0, workspace, workspace_bytes, err_flag, stream);
+                            sm_scale, 0, nullptr, 0, 0, workspace, workspace_bytes, err_flag, stream);
 }
 
 extern "C" ev_status ev_tree_attention_window(const void *q, const void *k_cache, const void *v_cache, void *out,
@@ -1578,5 +1665,21 @@ extern "C" ev_status ev_tree_attention_window(const void *q, const void *k_cache
     if (window < 1) return EV_ERR_SHAPE;
     return launch_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
                             total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype,
-                            sm_scale, window, workspace, workspace_bytes, err_flag, stream);
+                            sm_scale, window, nullptr, 0, 0, workspace, workspace_bytes, err_flag, stream);
+}
+
+extern "C" ev_status ev_tree_attention_paged(const void *q, const void *k_pages, const void *v_pages, void *out,
+                                             float *lse, const int32_t *node_start, const int32_t *parent,
+                                             const int32_t *block_table, int32_t bt_stride, int32_t page_size,
+                                             const int32_t *prefix_len, int32_t batch, int32_t total_nodes,
+                                             int32_t max_nodes, int32_t num_pages, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim, ev_dtype dtype, float sm_scale,
+                                             int32_t window, void *workspace, size_t workspace_bytes,
+                                             int32_t *err_flag, hipStream_t stream) {
+    if (page_size < 16 || page_size > 65536 || (page_size & (page_size - 1)) || bt_stride < 1 || num_pages < 0)
+        return EV_ERR_SHAPE;
+    return launch_attention(q, k_pages, v_pages, out, lse, node_start, parent, nullptr, prefix_len, batch,
+                            total_nodes, max_nodes, static_cast<int64_t>(num_pages) * page_size, num_q_heads,
+                            num_kv_heads, head_dim, dtype, sm_scale, window, block_table, bt_stride, page_size,
+                            workspace, workspace_bytes, err_flag, stream);
 }

@@ -25,8 +25,8 @@ MAX_NODES = 64
 MAX_BATCH = 2048
 
 EXPORTS = ("ev_status_string", "ev_tree_attention_workspace_size", "ev_tree_attention",
-           "ev_tree_attention_window", "ev_node_argmax_workspace_size", "ev_node_argmax", "ev_greedy_accept",
-           "ev_compact_kv")
+           "ev_tree_attention_window", "ev_tree_attention_paged", "ev_node_argmax_workspace_size",
+           "ev_node_argmax", "ev_greedy_accept", "ev_compact_kv", "ev_compact_kv_paged")
 
 _lib = None
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -57,6 +57,9 @@ def load(path: str = LIB_PATH):
     lib.ev_tree_attention_window.restype = ctypes.c_int
     lib.ev_tree_attention_window.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32,
                                              _I32, _I32, ctypes.c_int, _F, _I32, _P, _SZ, _P, _P]
+    lib.ev_tree_attention_paged.restype = ctypes.c_int
+    lib.ev_tree_attention_paged.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _I32, _I32, _I32, _I32,
+                                            _I32, _I32, _I32, ctypes.c_int, _F, _I32, _P, _SZ, _P, _P]
     lib.ev_node_argmax_workspace_size.restype = _SZ
     lib.ev_node_argmax_workspace_size.argtypes = [_I32, _I32]
     lib.ev_node_argmax.restype = ctypes.c_int
@@ -66,6 +69,9 @@ def load(path: str = LIB_PATH):
     lib.ev_compact_kv.restype = ctypes.c_int
     lib.ev_compact_kv.argtypes = [_P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P,
                                   _P, _P]
+    lib.ev_compact_kv_paged.restype = ctypes.c_int
+    lib.ev_compact_kv_paged.argtypes = [_P, _P, _I32, _I32, _I64, _P, _I32, _I32, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                        _I32, _P, _P, _P]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -95,6 +101,23 @@ def ev_tree_attention_window(q, k_cache, v_cache, out, lse, node_start, parent, 
                                            batch, total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads,
                                            head_dim, dtype, sm_scale, window, workspace, workspace_bytes, err_flag,
                                            stream)
+
+
+def ev_tree_attention_paged(q, k_pages, v_pages, out, lse, node_start, parent, block_table, bt_stride, page_size,
+                            prefix_len, batch, total_nodes, max_nodes, num_pages, num_q_heads, num_kv_heads, head_dim,
+                            dtype, sm_scale, window, workspace, workspace_bytes, err_flag, stream) -> int:
+    return load().ev_tree_attention_paged(q, k_pages, v_pages, out, lse, node_start, parent, block_table, bt_stride,
+                                          page_size, prefix_len, batch, total_nodes, max_nodes, num_pages,
+                                          num_q_heads, num_kv_heads, head_dim, dtype, sm_scale, window, workspace,
+                                          workspace_bytes, err_flag, stream)
+
+
+def ev_compact_kv_paged(k_pages, v_pages, elem_bytes, num_layers, layer_stride_bytes, block_table, bt_stride,
+                        page_size, prefix_len, accept_len, accept_path, batch, max_nodes, num_pages, num_kv_heads,
+                        head_dim, new_len, err_flag, stream) -> int:
+    return load().ev_compact_kv_paged(k_pages, v_pages, elem_bytes, num_layers, layer_stride_bytes, block_table,
+                                      bt_stride, page_size, prefix_len, accept_len, accept_path, batch, max_nodes,
+                                      num_pages, num_kv_heads, head_dim, new_len, err_flag, stream)
 
 
 def ev_node_argmax_workspace_size(num_rows, vocab) -> int:
@@ -212,6 +235,40 @@ def tree_attention(q, k_cache, v_cache, node_start, parent, kv_start, prefix_len
     return out, lse, workspace
 
 
+def tree_attention_paged(q, k_pages, v_pages, node_start, parent, block_table, prefix_len, *, max_nodes: int,
+                         sm_scale: float, window: int = 0, out=None, lse=None, workspace: Workspace = None,
+                         err_flag=None, stream=None):
+    """Tree-masked GQA attention over a paged pool (ev_tree_attention_paged).  q [T, Hq, D] bf16;
+    pools [pages, page_size, Hkv, D] bf16; block_table [B, stride] int32.  Returns (out, lse, ws)."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_pages, "k_pages", torch.bfloat16, 4)
+    _need(v_pages, "v_pages", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    for name, t in (("node_start", node_start), ("parent", parent), ("prefix_len", prefix_len)):
+        _need(t, name, torch.int32, 1)
+    T, Hq, D = q.shape
+    pages, page_size, Hkv, Dk = k_pages.shape
+    if Dk != D or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("q / k_pages / v_pages shapes disagree")
+    B = prefix_len.shape[0]
+    if node_start.shape[0] != B + 1 or block_table.shape[0] != B or parent.shape[0] != T:
+        raise ValueError("metadata lengths disagree with batch / total nodes")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    need = ev_tree_attention_workspace_size(B, max_nodes, Hq, Hkv, D)
+    if workspace is None or workspace.nbytes < need:
+        workspace = Workspace(need, q.device)
+    st = ev_tree_attention_paged(_addr(q), _addr(k_pages), _addr(v_pages), _addr(out), _addr(lse), _addr(node_start),
+                                 _addr(parent), _addr(block_table), block_table.shape[1], page_size,
+                                 _addr(prefix_len), B, T, max_nodes, pages, Hq, Hkv, D, EV_BF16, float(sm_scale),
+                                 int(window), workspace.ptr, workspace.nbytes, _addr(err_flag), _stream(stream))
+    _check(st, "ev_tree_attention_paged")
+    return out, lse, workspace
+
+
 def node_argmax(logits, *, vocab: int = None, target=None, max_value=None, workspace: Workspace = None,
                 stream=None):
     """Greedy token per row (ev_node_argmax).  logits [R, stride] bf16/fp32.  Returns (target, max_value, ws)."""
@@ -279,6 +336,35 @@ def compact_kv(k_cache, v_cache, kv_start, prefix_len, accept_len, accept_path, 
                        _addr(prefix_len), _addr(accept_len), _addr(accept_path), B, max_nodes, slots, Hkv, D,
                        _addr(new_len), _addr(err_flag), _stream(stream))
     _check(st, "ev_compact_kv")
+    return new_len
+
+
+def compact_kv_paged(k_pages, v_pages, block_table, prefix_len, accept_len, accept_path, *, new_len=None,
+                     err_flag=None, stream=None):
+    """In-place KV compaction through a block table (ev_compact_kv_paged).  Pools
+    [pages, page_size, Hkv, D] or [layers, pages, page_size, Hkv, D]; block_table [B, stride] int32."""
+    torch = _torch()
+    _need(k_pages, "k_pages")
+    _need(v_pages, "v_pages", k_pages.dtype)
+    _need(block_table, "block_table", torch.int32, 2)
+    if k_pages.dim() == 4:
+        layers, (pages, page_size, Hkv, D) = 1, k_pages.shape
+    elif k_pages.dim() == 5:
+        layers, pages, page_size, Hkv, D = k_pages.shape
+    else:
+        raise ValueError("pools must be [pages, page_size, Hkv, D] or [layers, pages, page_size, Hkv, D]")
+    if tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("k_pages / v_pages shapes disagree")
+    B = prefix_len.shape[0]
+    max_nodes = accept_path.shape[1]
+    if new_len is None:
+        new_len = torch.empty(B, dtype=torch.int32, device=k_pages.device)
+    esz = k_pages.element_size()
+    st = ev_compact_kv_paged(_addr(k_pages), _addr(v_pages), esz, layers, pages * page_size * Hkv * D * esz,
+                             _addr(block_table), block_table.shape[1], page_size, _addr(prefix_len),
+                             _addr(accept_len), _addr(accept_path), B, max_nodes, pages, Hkv, D, _addr(new_len),
+                             _addr(err_flag), _stream(stream))
+    _check(st, "ev_compact_kv_paged")
     return new_len
 
 

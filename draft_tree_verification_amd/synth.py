@@ -237,6 +237,36 @@ def make_config(name: str, seed: Optional[int] = None) -> Workload:
     raise KeyError(name)
 
 
+def paged_layout(w: Workload, page_size: int, seed: int, spare_pages: int = 3):
+    """The workload's caches scattered over randomly placed pages of a pool: returns (k_pool,
+    v_pool, block_table [B, width] int32).  Sequence b's token t (prefix, then tree node t - L)
+    is copied to pool row block_table[b, t // page_size] * page_size + t % page_size; every page
+    is used by one sequence at most, unused pool rows and table entries hold garbage."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ntok = [int(w.prefix_len[b]) + int(w.node_start[b + 1] - w.node_start[b]) for b in range(w.batch)]
+    need = [(n + page_size - 1) // page_size for n in ntok]
+    total = sum(need) + spare_pages
+    order = rng.permutation(total).astype(np.int32)
+    width = max(need) + 1
+    bt = np.full((w.batch, width), -7, np.int32)
+    shape = (total * page_size,) + w.k.shape[1:]
+    if w.k.dtype == np.uint16:
+        pool_k = rng.integers(0, 1 << 14, shape, dtype=np.uint16)
+        pool_v = rng.integers(0, 1 << 14, shape, dtype=np.uint16)
+    else:
+        pool_k = rng.integers(0, 1 << 14, shape).astype(w.k.dtype)
+        pool_v = rng.integers(0, 1 << 14, shape).astype(w.v.dtype)
+    nxt = 0
+    for b in range(w.batch):
+        bt[b, :need[b]] = order[nxt:nxt + need[b]]
+        nxt += need[b]
+        t = np.arange(ntok[b], dtype=np.int64)
+        rows = bt[b, t // page_size].astype(np.int64) * page_size + t % page_size
+        pool_k[rows] = w.k[int(w.kv_start[b]) + t]
+        pool_v[rows] = w.v[int(w.kv_start[b]) + t]
+    return pool_k, pool_v, bt
+
+
 def describe(w: Workload) -> dict:
     return {"workload": w.name, "batch": w.batch, "tree_nodes": w.total_nodes,
             "prefix_tokens": int(w.prefix_len.sum()), "q_heads": w.num_q_heads,

@@ -18,6 +18,10 @@
  *                       name per-sequence acceptance lengths under continuous batching as the
  *                       main integration difficulty: same article, "Current Limitation")
  *
+ * plus variants of the same operations: ev_tree_attention_window (a sliding window over the
+ * prefix, as in the drafter's layers), ev_tree_attention_paged and ev_compact_kv_paged (KV
+ * held in a paged pool through a per-sequence block table).
+ *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer owned by the caller; the library allocates
  *     nothing and keeps no per-call state between calls (a small per-device cache of device
@@ -66,7 +70,8 @@ typedef enum { EV_BF16 = 0, EV_F32 = 1 } ev_dtype;
 #define EV_DATA_BAD_PARENT 1 /* parent[0] != -1 or parent[i] outside [0, i) */
 #define EV_DATA_BAD_NODES 2  /* N_b = node_start[b+1] - node_start[b] outside [1, max_nodes] */
 #define EV_DATA_BAD_TOKEN 4  /* a compared draft token or a target token outside [0, vocab) */
-#define EV_DATA_BAD_SLOTS 8  /* kv_start / prefix_len negative or slots past total_slots */
+#define EV_DATA_BAD_SLOTS 8  /* kv_start / prefix_len negative, slots past total_slots, or pages
+                               outside the block table or the pool */
 #define EV_DATA_BAD_PATH 16  /* accepted path not strictly increasing from node 0, or too long */
 
 #define EV_MAX_NODES 64
@@ -137,6 +142,40 @@ ev_status ev_tree_attention_window(const void *q, const void *k_cache, const voi
                                    int32_t *err_flag, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * ev_tree_attention_paged
+ *
+ * ev_tree_attention (optionally windowed) over a paged KV pool, the cache layout of the
+ * PagedAttention serving engines the verification kernel has to live in (kongchang.com English
+ * article, section "Current Limitation: Only Qwen3.8-27B Supported"; arex-research.com release
+ * note, section "eagle-harness 是插件，不改引擎本体", on tree verification in vLLM needing an
+ * unquantized KV cache).  Token t of sequence b (prefix tokens t < Lf = prefix_len[b], then tree
+ * node i at t = Lf + i) lives in pool row
+ *     row(b, t) = block_table[b * bt_stride + t / page_size] * page_size + t % page_size
+ * and the visible set of node i is { row(b, t) : Lf - L <= t < Lf } U { row(b, Lf + j) : j
+ * ancestor of i or j == i } with L = Lf (window == 0) or min(Lf, window).
+ *
+ *   k_pages, v_pages   bf16 [num_pages][page_size][num_kv_heads][head_dim] (read only)
+ *   block_table        int32 [batch][bt_stride]; entries 0 .. (Lf + N_b - 1) / page_size of row
+ *                      b are read, the rest are ignored
+ *   page_size          a power of two, 16 .. 65536;  bt_stride >= 1;  num_pages >= 0
+ *   window             0: no window;  >= 1: sliding window as in ev_tree_attention_window
+ * q, out, lse, node_start, parent, prefix_len, the sizes, sm_scale, workspace and err_flag are as
+ * in ev_tree_attention (same workspace size); kv_start does not exist here.  dtype must be
+ * EV_BF16 (EV_ERR_DTYPE otherwise).  Data errors: N_b outside [1, max_nodes] or a bad parent
+ * (EV_DATA_BAD_NODES / _PARENT) and Lf < 0 or (Lf + N_b - 1) / page_size >= bt_stride
+ * (EV_DATA_BAD_SLOTS) leave the sequence's rows unwritten as in ev_tree_attention; a block-table
+ * entry outside [0, num_pages) that the sequence reads raises EV_DATA_BAD_SLOTS while its rows
+ * are computed (their values are then unspecified: page 0 stands in, no load leaves the pool).
+ * -------------------------------------------------------------------------------------------*/
+ev_status ev_tree_attention_paged(const void *q, const void *k_pages, const void *v_pages, void *out, float *lse,
+                                  const int32_t *node_start, const int32_t *parent, const int32_t *block_table,
+                                  int32_t bt_stride, int32_t page_size, const int32_t *prefix_len, int32_t batch,
+                                  int32_t total_nodes, int32_t max_nodes, int32_t num_pages, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, ev_dtype dtype, float sm_scale,
+                                  int32_t window, void *workspace, size_t workspace_bytes, int32_t *err_flag,
+                                  hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * ev_node_argmax
  *
  * target_token[r] = the LOWEST index v in [0, vocab) holding the maximum of logits row r (the
@@ -197,6 +236,32 @@ ev_status ev_compact_kv(void *k_cache, void *v_cache, int32_t elem_bytes, int32_
                         const int32_t *accept_len, const int32_t *accept_path, int32_t batch, int32_t max_nodes,
                         int64_t total_slots, int32_t num_kv_heads, int32_t head_dim, int32_t *new_len,
                         int32_t *err_flag, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ev_compact_kv_paged
+ *
+ * ev_compact_kv through a block table (the per-sequence acceptance lengths of continuous
+ * batching over a paged pool: kongchang.com English article, "Current Limitation: Only
+ * Qwen3.8-27B Supported").  In place, for every layer l and 0 <= d < len = accept_len[b]:
+ *   row(b, L + d) of layer l  <-  the bytes row(b, L + path[d]) held BEFORE the call
+ * with row(b, t) = block_table[b * bt_stride + t / page_size] * page_size + t % page_size and
+ * L = prefix_len[b].  The pages a sequence uses must be distinct (so distinct tokens are
+ * distinct rows; the in-place move relies on it).  new_len[b] = L + len (L when len <= 0).
+ *
+ *   k_pages, v_pages     layer l starts at base + l * layer_stride_bytes and is
+ *                        [num_pages][page_size][num_kv_heads][head_dim] of elem_bytes (2 or 4)
+ *                        elements, alignment rules as in ev_compact_kv
+ *   block_table          int32 [batch][bt_stride];  page_size >= 1 (any);  num_pages >= 0
+ * Data errors: a bad path (EV_DATA_BAD_PATH) as in ev_compact_kv; L < 0,
+ * (L + path[len-1]) / page_size >= bt_stride or a source or destination page outside
+ * [0, num_pages) raise EV_DATA_BAD_SLOTS; such a sequence is left alone with new_len = L.
+ * -------------------------------------------------------------------------------------------*/
+ev_status ev_compact_kv_paged(void *k_pages, void *v_pages, int32_t elem_bytes, int32_t num_layers,
+                              int64_t layer_stride_bytes, const int32_t *block_table, int32_t bt_stride,
+                              int32_t page_size, const int32_t *prefix_len, const int32_t *accept_len,
+                              const int32_t *accept_path, int32_t batch, int32_t max_nodes, int32_t num_pages,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t *new_len, int32_t *err_flag,
+                              hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -311,40 +311,12 @@ def pin_window(lib):
         assert np.array_equal(out, ref) and np.array_equal(lse, ref_lse), f"window {W} != truncated prefix"
 
 
-def paged_copy(w, page_size: int, seed: int, spare_pages: int = 3):
-    """The workload's caches scattered over randomly placed pages: returns (k_pool, v_pool,
-    block_table [B, pages]).  Token t of sequence b lands at row bt[b, t // P] * P + t % P."""
-    rng = np.random.default_rng(seed)
-    need = [(int(w.prefix_len[b]) + int(w.node_start[b + 1] - w.node_start[b]) + page_size - 1) // page_size
-            for b in range(w.batch)]
-    total = sum(need) + spare_pages
-    order = rng.permutation(total)
-    width = max(need) + 1
-    bt = np.full((w.batch, width), -7, np.int32)          # unused entries hold garbage
-    pool_k = np.zeros((total * page_size,) + w.k.shape[1:], w.k.dtype)
-    pool_v = np.zeros_like(pool_k)
-    pool_k[:] = rng.integers(0, 1 << 14, pool_k.shape).astype(w.k.dtype)
-    pool_v[:] = rng.integers(0, 1 << 14, pool_v.shape).astype(w.v.dtype)
-    nxt = 0
-    for b in range(w.batch):
-        s0 = int(w.kv_start[b])
-        ntok = int(w.prefix_len[b]) + int(w.node_start[b + 1] - w.node_start[b])
-        for p in range(need[b]):
-            bt[b, p] = order[nxt]
-            nxt += 1
-        for t in range(ntok):
-            row = bt[b, t // page_size] * page_size + t % page_size
-            pool_k[row] = w.k[s0 + t]
-            pool_v[row] = w.v[s0 + t]
-    return pool_k, pool_v, bt
-
-
 def pin_paged(lib):
     """Paged caches: scattering a workload's tokens over random pages changes nothing (bit for
     bit, with and without a window), and a page index outside the pool is a data error."""
     for seed, dtype, P in ((71, BF16, 4), (72, F32, 16), (73, BF16, 1)):
         w = small_tree_workload(seed, dtype=dtype, prefix=(0, 5, 33, 64), nodes=(7, 16, 3, 11))
-        pk, pv, bt = paged_copy(w, P, seed)
+        pk, pv, bt = synth.paged_layout(w, P, seed)
         for W in (0, 9):
             ref, ref_lse, _ = _window_attn(w, lib, W)
             out, lse, err = oracle.tree_attention(w.q, pk, pv, w.node_start, w.parent, None, w.prefix_len,
@@ -377,7 +349,7 @@ def pin_paged_compact(lib):
         for b, path in enumerate(([0, 1, 3, 4], [0], [0, 2, 3, 7, 8, 15], [0, 1, 2, 3, 4, 5, 6, 7, 8])):
             paths[b, :len(path)] = path
             lens[b] = len(path)
-        pk, pv, bt = paged_copy(w, P, 90 + P)
+        pk, pv, bt = synth.paged_layout(w, P, 90 + P)
         layers = 2
         k2 = np.stack([pk, rng.integers(0, 1 << 15, pk.shape).astype(pk.dtype)])
         v2 = np.stack([pv, rng.integers(0, 1 << 15, pv.shape).astype(pv.dtype)])

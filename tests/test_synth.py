@@ -56,3 +56,17 @@ def test_planting_rule():
     hits = [w.draft[i] == greedy[w.node_start[b] + w.parent[i]]
             for b in range(w.batch) for i in range(w.node_start[b] + 1, w.node_start[b + 1])]
     assert abs(np.mean(hits) - 0.6) < 0.03
+
+
+def test_paged_layout_places_every_token():
+    w = synth.make_workload("pl", 4, prefix_lens=[0, 17, 40], nodes=[3, 16, 5], vocab=16)
+    pk, pv, bt = synth.paged_layout(w, 16, 9)
+    used = []
+    for b in range(w.batch):
+        n = int(w.prefix_len[b]) + int(w.node_start[b + 1] - w.node_start[b])
+        pages = bt[b, :(n + 15) // 16]
+        used += list(pages)
+        for t in range(n):
+            row = pages[t // 16] * 16 + t % 16
+            assert (pk[row] == w.k[w.kv_start[b] + t]).all() and (pv[row] == w.v[w.kv_start[b] + t]).all()
+    assert len(set(used)) == len(used) and min(used) >= 0 and max(used) < pk.shape[0] // 16
