@@ -222,6 +222,12 @@ __device__ __forceinline__ float *slot_of_piece(float *part, int w1, int piece, 
     return part + static_cast<size_t>(piece == 0 ? 2 * w + 1 : 2 * w) * slot_floats;
 }
 
+// Batches of at most kAlignedMaxBatch sequences also keep each sequence's stages per unit and
+// unit count in s_cum[kSeqStages + b] and s_cum[kSeqUnits + b] (for the unit-aligned split).
+constexpr int kAlignedMaxBatch = 64;
+constexpr int kSeqStages = EV_MAX_BATCH / 2;
+constexpr int kSeqUnits = EV_MAX_BATCH / 2 + kAlignedMaxBatch;
+
 // Per-sequence stage counts of the whole batch and their inclusive scan into s_cum (identical
 // in every workgroup); returns the total stage count.  Sequences with bad geometry get no stages
 // and raise their error bit once.
@@ -247,11 +253,18 @@ __device__ __forceinline__ int64_t schedule_scan(const AttnArgs &a, int32_t *s_c
             else if (a.block_table ? (L < 0 || ((static_cast<int64_t>(L) + n - 1) >> a.page_shift) >= a.bt_stride)
                                    : (L < 0 || s0 < 0 || static_cast<int64_t>(s0) + L + n > a.total_slots))
                 err = EV_DATA_BAD_SLOTS;
+            int st = 0, units = 0;
             if (err) {
                 if (blockIdx.x == 0) ev::flag_error(a.err_flag, err);
             } else {
                 const int Lv = (a.window > 0 && L > a.window) ? a.window : L;
-                work = a.hkv * ((n * G + R - 1) / R) * ((Lv + n + KST - 1) / KST);
+                st = (Lv + n + KST - 1) / KST;
+                units = a.hkv * ((n * G + R - 1) / R);
+                work = units * st;
+            }
+            if (a.batch <= kAlignedMaxBatch) {
+                s_cum[kSeqStages + b] = st;
+                s_cum[kSeqUnits + b] = units;
             }
         }
         int x = work;
@@ -271,6 +284,121 @@ __device__ __forceinline__ int64_t schedule_scan(const AttnArgs &a, int32_t *s_c
         __syncthreads();
     }
     return carry;
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Inclusive prefix over each 16-lane row with DPP row shifts (lanes shifted in from outside the
+// row read 0), then across the four rows through their last lanes; `total` = the wave's sum.
+// All values non-negative, so the same steps give a row-wise running maximum with op = max.
+template <bool MAX>
+__device__ __forceinline__ int wave_scan(int x, int &total) {
+    auto op = [](int u, int v) { return MAX ? max(u, v) : u + v; };
+    x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+    x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+    x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+    x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+    const int r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
+    const int row = (threadIdx.x & 63) >> 4;
+    if (row > 0) x = op(x, r0);
+    if (row > 1) x = op(x, r1);
+    if (row > 2) x = op(x, r2);
+    total = op(op(r0, r1), op(r2, r3));
+    return x;
+}
+__device__ __forceinline__ int wave_sum(int x) {
+    int t;
+    wave_scan<false>(x, t);
+    return t;
+}
+
+// The stage range of one logical workgroup.
+struct PieceMap {
+    int64_t begin, end;  // its stages in the batch's stage order
+    int P;               // logical workgroups with work
+    int k;               // unit-aligned split: pieces of this workgroup's unit (0: contiguous split)
+    int w1;              // unit-aligned split: logical workgroup of the unit's first piece
+};
+
+// Two ways to cut the batch's stages into per-workgroup ranges.
+//  * Unit-aligned (at most `grid` units, at most kAlignedMaxBatch sequences): unit u gets
+//    k_u = ceil(stages_u / C) pieces of near-equal length, C the smallest cap whose pieces fit the
+//    grid; each workgroup holds exactly one piece of one unit, so none restarts its load pipeline
+//    on a second unit, and the workgroups in use spread over all XCDs (logical = hardware index).
+//  * Contiguous (otherwise): equal ranges of the whole stage order; a range may cover the end of
+//    one unit and the start of the next (XCD-major logical order).
+// Every wave computes the map itself (lane = sequence), from the per-sequence counts in LDS.
+__device__ __forceinline__ PieceMap map_pieces(const AttnArgs &a, const int32_t *s_cum, int64_t S, int grid,
+                                               int &wl) {
+    PieceMap m{};
+    m.k = -1;
+    const int lane = threadIdx.x & 63;
+    if (a.batch <= kAlignedMaxBatch) {
+        const int st = lane < a.batch ? s_cum[kSeqStages + lane] : 0;
+        const int units = lane < a.batch ? s_cum[kSeqUnits + lane] : 0;
+        const int utot = wave_sum(units);
+        if (utot > 0 && utot <= grid) {
+            // C >= S / grid; C = max st_b fits (one piece per unit), and so does any C with
+            // S / C + utot <= grid (each unit rounds up by less than one piece)
+            int hi;
+            wave_scan<true>(st, hi);
+            int lo = static_cast<int>((S + grid - 1) / grid);
+            if (utot < grid) hi = min(hi, static_cast<int>((S + grid - utot - 1) / (grid - utot)));
+            lo = max(1, min(lo, hi));
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (wave_sum(units * ((st + mid - 1) / mid)) <= grid) hi = mid; else lo = mid + 1;
+            }
+            const int k = (st + lo - 1) / lo;
+            const int wk = units * k;
+            int P;
+            const int W = wave_scan<false>(wk, P) - wk;  // exclusive prefix
+            const int wb = blockIdx.x;
+            if (wb >= P) {
+                m.k = 0;
+                m.P = P;
+                wl = wb;
+            } else {
+                const uint64_t hit = __ballot(wk > 0 && W <= wb);
+                const int bs = hit ? 63 - __builtin_clzll(hit) : 0;
+                const int Wb = __builtin_amdgcn_readlane(W, bs), kb = __builtin_amdgcn_readlane(k, bs);
+                const int stb = __builtin_amdgcn_readlane(st, bs);
+                const int r = wb - Wb;
+                if (hit && kb > 0 && r >= 0) {
+                    const int ui = r / kb, j = r % kb;
+                    const int64_t ustart = (bs ? s_cum[bs - 1] : 0) + static_cast<int64_t>(ui) * stb;
+                    m.begin = ustart + static_cast<int64_t>(stb) * j / kb;
+                    m.end = ustart + static_cast<int64_t>(stb) * (j + 1) / kb;
+                    m.k = kb;
+                    m.w1 = Wb + ui * kb;
+                    m.P = P;
+                    wl = wb;
+                    // a map that fails these checks falls back to the contiguous split
+                    if (!(P <= grid && m.begin >= 0 && m.begin < m.end && m.end <= S)) m.k = -1;
+                }
+            }
+        }
+    }
+    if (m.k < 0) {
+        m.k = 0;
+        wl = (grid % 8 == 0) ? (blockIdx.x % 8) * (grid / 8) + blockIdx.x / 8 : blockIdx.x;
+        m.P = static_cast<int>(S < grid ? S : grid);  // never more than stages: every range non-empty
+        m.begin = S * wl / m.P;
+        m.end = S * (wl + 1) / m.P;
+    }
+    // uniform values: scalar registers and scalar branches in the piece loop
+    m.begin = uniform64(m.begin);
+    m.end = uniform64(m.end);
+    m.P = __builtin_amdgcn_readfirstlane(m.P);
+    m.k = __builtin_amdgcn_readfirstlane(m.k);
+    m.w1 = __builtin_amdgcn_readfirstlane(m.w1);
+    wl = __builtin_amdgcn_readfirstlane(wl);
+    return m;
 }
 
 template <int D, int RT, bool F32IN, bool PG>
@@ -308,12 +436,12 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
 
     const int64_t S = schedule_scan<R, KST>(a, s_cum, s_misc);
     const int grid = gridDim.x;
-    const int wl = (grid % 8 == 0) ? (blockIdx.x % 8) * (grid / 8) + blockIdx.x / 8 : blockIdx.x;
-    // logical workgroups: never more than stages, so every logical range is non-empty
-    const int P = static_cast<int>(S < grid ? S : grid);
+    int wl;
+    const PieceMap pm = map_pieces(a, s_cum, S, grid, wl);
+    const int P = pm.P;
     if (tid == 0) a.table[wl] = int4{0, 0, 0, 0};  // no split unit starts here (until one does)
     if (wl >= P) return;
-    const int64_t begin = S * wl / P, end = S * (wl + 1) / P;
+    const int64_t begin = pm.begin, end = pm.end;
 
     for (int64_t pos = begin; pos < end;) {
         // ---- locate the unit that holds stage `pos`
@@ -782,7 +910,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
 
         // ---- split unit: publish this piece's partial (m, l, unnormalised O); the merge launch
         // combines the unit's pieces
-        const int w1 = wg_of(ustart, S, P);
+        const int w1 = pm.k ? pm.w1 : wg_of(ustart, S, P);
         {
             float *slot = slot_of_piece(a.part, w1, wl - w1, Lay::kSlotFloats);
 #pragma unroll
@@ -798,7 +926,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
                 }
             }
         }
-        if (wl == w1 && tid == 0) a.table[wl] = int4{wg_of(uend - 1, S, P) - w1 + 1, ns0, n, ui};
+        if (wl == w1 && tid == 0) a.table[wl] = int4{pm.k ? pm.k : wg_of(uend - 1, S, P) - w1 + 1, ns0, n, ui};
     }
 }
 
@@ -949,11 +1077,12 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
 
     const int64_t S = schedule_scan<R, KST>(a, s_cum, s_misc);
     const int grid = gridDim.x;
-    const int wl = (grid % 8 == 0) ? (blockIdx.x % 8) * (grid / 8) + blockIdx.x / 8 : blockIdx.x;
-    const int P = static_cast<int>(S < grid ? S : grid);
+    int wl;
+    const PieceMap pm = map_pieces(a, s_cum, S, grid, wl);
+    const int P = pm.P;
     if (tid == 0) a.table[wl] = int4{0, 0, 0, 0};  // no split unit starts here (until one does)
     if (wl >= P) return;
-    const int64_t begin = S * wl / P, end = S * (wl + 1) / P;
+    const int64_t begin = pm.begin, end = pm.end;
 
     // Chunks are XOR-swizzled per row (same rule as the other bf16 path): K row r keeps global
     // chunk c at slot c ^ fk(r), V row r at slot c ^ fv(r); rows are local to a 16-row block.
@@ -1361,7 +1490,7 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
             continue;
         }
         // split unit: publish this piece's partial; the merge launch combines the unit's pieces
-        const int w1 = wg_of(ustart, S, P);
+        const int w1 = pm.k ? pm.w1 : wg_of(ustart, S, P);
         {
             float *slot = slot_of_piece(a.part, w1, wl - w1, R * D + 2 * R);
 #pragma unroll
@@ -1375,7 +1504,7 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
                 }
             }
         }
-        if (wl == w1 && tid == 0) a.table[wl] = int4{wg_of(uend - 1, S, P) - w1 + 1, ns0, n, ui};
+        if (wl == w1 && tid == 0) a.table[wl] = int4{pm.k ? pm.k : wg_of(uend - 1, S, P) - w1 + 1, ns0, n, ui};
     }
 }
 
