@@ -76,6 +76,13 @@ def _bind(lib):
                                             _I32, _I64, _I32, _I32, _P, _P]
     lib.oracle_node_argmax.restype = None
     lib.oracle_node_argmax.argtypes = [_P, _I32, _I64, _I32, _I32, _P, _P]
+    lib.oracle_philox4x64_10.restype = None
+    lib.oracle_philox4x64_10.argtypes = [_P, _P, _P]
+    lib.oracle_sample_uniform.restype = ctypes.c_float
+    lib.oracle_sample_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64, _I64, _I64]
+    lib.oracle_node_sample.restype = None
+    lib.oracle_node_sample.argtypes = [_P, _I32, _I64, _I32, _I32, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64,
+                                       _P, _P]
     lib.oracle_greedy_accept.restype = None
     lib.oracle_greedy_accept.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]
     lib.oracle_compact_kv.restype = None
@@ -193,6 +200,38 @@ def node_argmax(logits, vocab: int = None, row_stride: int = None, lib=None):
     mx = np.zeros(max(R, 1))
     lib.oracle_node_argmax(_ptr(logits), dt, int(row_stride), R, int(vocab), _ptr(tgt), _ptr(mx))
     return tgt[:R], mx[:R]
+
+
+def philox4x64_10(ctr, key, lib=None) -> np.ndarray:
+    """Philox4x64-10 of a 256-bit counter (4 words) under a 128-bit key (2 words)."""
+    lib = lib or load()
+    c = np.ascontiguousarray(ctr, dtype=np.uint64)
+    k = np.ascontiguousarray(key, dtype=np.uint64)
+    out = np.zeros(4, dtype=np.uint64)
+    lib.oracle_philox4x64_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sample_uniform(seed: int, offset: int, row: int, v: int, lib=None) -> float:
+    """The uniform in (0, 1) that the sampled draw uses for element v of row `row`."""
+    return float((lib or load()).oracle_sample_uniform(seed, offset, row, v))
+
+
+def node_sample(logits, temperature: float, seed: int, offset: int, vocab: int = None, row_stride: int = None,
+                lib=None):
+    """Sampled target token per row (Gumbel-max draw from softmax(logits / T) with Philox noise).
+    Returns (token [R] int32, score [R] float32: the winning base-2 score)."""
+    lib = lib or load()
+    logits = np.ascontiguousarray(logits)
+    dt = _dtype_of(logits)
+    R = logits.shape[0]
+    vocab = logits.shape[1] if vocab is None else vocab
+    row_stride = logits.shape[1] if row_stride is None else row_stride
+    tok = np.zeros(max(R, 1), dtype=np.int32)
+    sc = np.zeros(max(R, 1), dtype=np.float32)
+    lib.oracle_node_sample(_ptr(logits), dt, int(row_stride), R, int(vocab), float(temperature), int(seed),
+                           int(offset), _ptr(tok), _ptr(sc))
+    return tok[:R], sc[:R]
 
 
 def greedy_accept(node_start, parent, draft, target, max_nodes: int, vocab: int, lib=None):

@@ -19,7 +19,14 @@
  *   - q head h reads KV head h / (Hq / Hkv);
  *   - argmax ties go to the lowest index, +0 == -0, NaN ranks above everything
  *     (first NaN wins);
- *   - the accepted node is the deepest accepted node, lowest index on equal depth.
+ *   - the accepted node is the deepest accepted node, lowest index on equal depth;
+ *   - sliding windows keep the last W prefix tokens; paged caches map token t through a
+ *     block table (page t / P, row t % P);
+ *   - sampled verification (T > 0, reported at temperature 1 in aiposthub.com analysis, "它和
+ *     DFlash 2、DSpark 比，贏在哪個條件？", and arex-research.com, "论文口径与推文口径"): drafted
+ *     children are point proposals, so speculative sampling along the tree is a per-node draw
+ *     from softmax(z / T) followed by the greedy acceptance rule on the draws (see the sampled
+ *     section below for the draw and its generator).
  *
  * Parity pins: every function here is checked in tests against an independent formulation
  * (brute force / library routines / closed forms / hand-built cases); none is unpinned.
@@ -269,6 +276,77 @@ void oracle_node_argmax(const void *logits, int32_t dtype, int64_t row_stride, i
         }
         target[r] = best;
         if (max_value) max_value[r] = bv;
+    }
+}
+
+/* ---- Sampled verification (temperature T > 0) ----
+   Reading: a drafted child is a point proposal for its parent's next token (the dynamic tree
+   expands the drafter's best tokens).  Speculative sampling with point proposals tries a node's
+   children in turn, accepting child token x with the residual target probability of x and
+   removing x from the residual when it is rejected; the bonus token is then drawn from what is
+   left.  The result has the law of one draw y from the target distribution at the node, with the
+   walk descending into the child whose token is y and stopping with bonus y when no child holds
+   it (the target's output distribution is kept).  So the sampled step is a per-node draw
+   followed by the greedy acceptance rule applied to the draws.
+
+   The draw is the Gumbel-max rule in base 2: with u_v uniform in (0, 1),
+       y = argmax_v  z_v * log2(e) / T  -  log2(-log2(u_v)),
+   which equals argmax_v (z_v / T + g_v) / ln 2 + const with g_v = -ln(-ln u_v) standard Gumbel
+   noise, hence y ~ softmax(z / T).  The uniforms come from Philox4x64-10 (Salmon, Moraes, Dror
+   and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11): key (seed, offset), counter
+   (v / 8, row, 0, 0); of the four 64-bit outputs, output k gives elements 8j + 2k (low 32 bits)
+   and 8j + 2k + 1 (high 32 bits); a 32-bit word w maps to u = ((w >> 9) + 1/2) * 2^-23 (exact in
+   fp32, strictly inside (0, 1)).
+   The decision is taken in fp32 as the library computes it: c = (float)(log2(e) / T) rounded
+   from double, s_v = fmaf(z_v, c, -log2f(-log2f(u_v))); largest s wins, lowest index on ties, a
+   NaN score (NaN logit) above every number. */
+static void philox_round(uint64_t x[4], const uint64_t k[2]) {
+    const unsigned __int128 p0 = (unsigned __int128)0xD2E7470EE14C6C93ull * x[0];
+    const unsigned __int128 p1 = (unsigned __int128)0xCA5A826395121157ull * x[2];
+    const uint64_t y0 = (uint64_t)(p1 >> 64) ^ x[1] ^ k[0];
+    const uint64_t y1 = (uint64_t)p1;
+    const uint64_t y2 = (uint64_t)(p0 >> 64) ^ x[3] ^ k[1];
+    const uint64_t y3 = (uint64_t)p0;
+    x[0] = y0; x[1] = y1; x[2] = y2; x[3] = y3;
+}
+
+void oracle_philox4x64_10(const uint64_t *ctr, const uint64_t *key, uint64_t *out) {
+    uint64_t x[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+    uint64_t k[2] = {key[0], key[1]};
+    for (int r = 0; r < 10; ++r) {
+        if (r) { k[0] += 0x9E3779B97F4A7C15ull; k[1] += 0xBB67AE8584CAA73Bull; }
+        philox_round(x, k);
+    }
+    for (int i = 0; i < 4; ++i) out[i] = x[i];
+}
+
+float oracle_sample_uniform(uint64_t seed, uint64_t offset, int64_t row, int64_t v) {
+    const uint64_t ctr[4] = {(uint64_t)v / 8, (uint64_t)row, 0, 0};
+    const uint64_t key[2] = {seed, offset};
+    uint64_t out[4];
+    oracle_philox4x64_10(ctr, key, out);
+    const int w = (int)(v % 8);
+    const uint32_t word = (w & 1) ? (uint32_t)(out[w / 2] >> 32) : (uint32_t)out[w / 2];
+    return ((float)(word >> 9) + 0.5f) * 0x1p-23f;
+}
+
+void oracle_node_sample(const void *logits, int32_t dtype, int64_t row_stride, int32_t num_rows, int32_t vocab,
+                        float temperature, uint64_t seed, uint64_t offset, int32_t *token, float *score) {
+    const float c = (float)(1.4426950408889634 / (double)temperature);
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int32_t r = 0; r < num_rows; ++r) {
+        const size_t base = (size_t)r * row_stride;
+        int32_t best = -1;
+        float bs = 0.f;
+        for (int32_t v = 0; v < vocab; ++v) {
+            const float z = (float)elem(logits, dtype, base + v);
+            const float u = oracle_sample_uniform(seed, offset, r, v);
+            const float s = fmaf(z, c, -log2f(-log2f(u)));
+            if (isnan(s)) { best = v; bs = s; break; }
+            if (best < 0 || s > bs) { best = v; bs = s; }
+        }
+        token[r] = best;
+        if (score) score[r] = bs;
     }
 }
 

@@ -381,3 +381,114 @@ def pin_paged_compact(lib):
 
 
 ALL_PINS = ALL_PINS + (pin_window, pin_paged, pin_paged_compact)
+
+
+# ------------------------------------------------------------------ sampled verification (T > 0)
+_M64 = (1 << 64) - 1
+
+
+def _numpy_philox(ctr, key):
+    """numpy's Philox4x64-10 (an independent implementation) for one counter: numpy advances its
+    256-bit counter before each block, so it starts one below."""
+    bg = np.random.Philox(key=np.array(key, dtype=np.uint64))
+    st = bg.state
+    cm1 = (sum(int(v) << (64 * i) for i, v in enumerate(ctr)) - 1) % (1 << 256)
+    st["state"]["counter"] = np.array([(cm1 >> (64 * i)) & _M64 for i in range(4)], dtype=np.uint64)
+    st["buffer_pos"] = 4
+    bg.state = st
+    return [int(x) for x in bg.random_raw(4)]
+
+
+def _chi2_ok(counts, probs, what, alpha=1e-4):
+    from scipy import stats
+    n = counts.sum()
+    exp = n * np.asarray(probs, np.float64)
+    keep = exp > 0
+    assert (counts[~keep] == 0).all(), f"{what}: draws of impossible tokens"
+    chi = (((counts[keep] - exp[keep]) ** 2) / exp[keep]).sum()
+    pv = stats.chi2.sf(chi, keep.sum() - 1)
+    assert pv > alpha, f"{what}: chi2 {chi:.1f} p={pv:.2e} counts {counts.tolist()} expected {exp.round(1).tolist()}"
+
+
+def _softmax(z):
+    z = np.asarray(z, np.float64)
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+def pin_sample(lib):
+    """Sampled draws.  The generator against numpy's Philox4x64-10; the per-element uniforms
+    against numpy's words under the documented layout; the law of the draw against softmax(z/T)
+    (chi-square, fp32 and bf16 rows, three temperatures); equal logits give uniform draws; a tiny
+    temperature gives the argmax; a NaN logit wins its row."""
+    for ctr, key in (((0, 0, 0, 0), (0, 0)), ((5, 7, 11, 13), (0x1234, 0xABCDEF)),
+                     ((_M64, _M64, _M64, _M64), (_M64, _M64)), ((_M64, 3, 0, 0), (9, 10))):
+        assert [int(x) for x in oracle.philox4x64_10(ctr, key, lib=lib)] == _numpy_philox(ctr, key), (ctr, key)
+    seed, offset = 0x0123456789ABCDEF, 42
+    for row, v in ((0, 0), (0, 1), (0, 7), (3, 8), (17, 151935), (5, 12345), (1 << 20, 6)):
+        words = _numpy_philox((v // 8, row, 0, 0), (seed, offset))
+        k = v % 8
+        w32 = (words[k // 2] >> 32) if k & 1 else (words[k // 2] & 0xFFFFFFFF)
+        assert oracle.sample_uniform(seed, offset, row, v, lib=lib) == ((w32 >> 9) + 0.5) * 2.0 ** -23, (row, v)
+    z = np.array([0.3, -1.2, 2.0, 0.0, 1.1, -0.4], np.float32)
+    R = 30000
+    for T, dtype in ((0.5, F32), (1.0, BF16), (2.5, F32)):
+        zz = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(z)) if dtype == BF16 else z
+        rows = np.tile(zz, (R, 1)).astype(np.float32)
+        if dtype == BF16:
+            rows = synth.f32_to_bf16_bits(rows)
+        tok, _ = oracle.node_sample(rows, T, seed=7, offset=int(T * 100), lib=lib)
+        _chi2_ok(np.bincount(tok, minlength=6), _softmax(zz.astype(np.float64) / T), f"law T={T}")
+    tok, _ = oracle.node_sample(np.zeros((R, 9), np.float32), 1.0, seed=3, offset=0, lib=lib)
+    _chi2_ok(np.bincount(tok, minlength=9), np.full(9, 1 / 9), "equal logits")
+    rng = np.random.default_rng(5)
+    sep = np.stack([rng.permutation(40).astype(np.float32) * 0.5 for _ in range(200)])
+    tok, _ = oracle.node_sample(sep, 0.01, seed=11, offset=1, lib=lib)
+    assert (tok == sep.argmax(axis=1)).all(), "a tiny temperature must give the argmax"
+    nanrow = np.array([[0.0, 5.0, np.nan, 9.0, np.nan]], np.float32)
+    assert oracle.node_sample(nanrow, 1.0, seed=1, offset=1, lib=lib)[0][0] == 2
+
+
+def pin_sampled_verification_lossless(lib):
+    """Sampled draws followed by the greedy acceptance rule along a draft tree emit tokens with the
+    target's own law (the release note's claim that verification keeps the target's output
+    distribution): on a toy target whose next-token logits depend on the context, the first
+    emitted token follows p(. | prefix), the second follows p(. | prefix, first) whenever the first
+    was a drafted child, the third likewise below that child, and a round ends after one token
+    when the first draw matches no child."""
+    V, T = 5, 1.0
+    rng = np.random.default_rng(17)
+    table = {}
+
+    def logits_of(ctx):
+        if ctx not in table:
+            table[ctx] = rng.normal(0, 1.3, V).astype(np.float32)
+        return table[ctx]
+
+    # root; children tokens 2 (node 1) and 0 (node 2); under node 1: tokens 4 (node 3), 1 (node 4);
+    # under node 2: token 3 (node 5); under node 3: token 4 (node 6)
+    parent = np.array([-1, 0, 0, 1, 1, 2, 3], np.int32)
+    draft = np.array([-1, 2, 0, 4, 1, 3, 4], np.int32)
+    ctx = [()]
+    for i in range(1, len(parent)):
+        ctx.append(ctx[parent[i]] + (int(draft[i]),))
+    rows = np.stack([logits_of(c) for c in ctx])
+    M = 40000
+    n = len(parent)
+    logits = np.tile(rows, (M, 1))
+    tok, _ = oracle.node_sample(logits, T, seed=99, offset=5, lib=lib)
+    node_start = np.arange(M + 1, dtype=np.int32) * n
+    acc = oracle.greedy_accept(node_start, np.tile(parent, M), np.tile(np.maximum(draft, 0), M), tok, n, V, lib=lib)
+    out, ln = acc["out_tokens"], acc["accept_len"]
+    first = out[:, 0]
+    _chi2_ok(np.bincount(first, minlength=V), _softmax(rows[0] / T), "first token")
+    assert (ln[~np.isin(first, (2, 0))] == 1).all()
+    for f, node in ((2, 1), (0, 2)):
+        sel = first == f
+        assert (ln[sel] >= 2).all()
+        _chi2_ok(np.bincount(out[sel, 1], minlength=V), _softmax(rows[node] / T), f"second token after {f}")
+    sel = (first == 2) & (out[:, 1] == 4)
+    _chi2_ok(np.bincount(out[sel, 2], minlength=V), _softmax(rows[3] / T), "third token after (2, 4)")
+
+
+ALL_PINS = ALL_PINS + (pin_sample, pin_sampled_verification_lossless)

@@ -33,6 +33,13 @@ MUTANTS = {
         "                const size_t src = lo + (size_t)token_slot(NULL, block_table, bt_stride, page_size, b, L + path[t]) * row;\n"
         "                memcpy((char *)k_out + dst, (const char *)k_out + src, row);\n"
         "                memcpy((char *)v_out + dst, (const char *)v_out + src, row);"),
+    "philox_weyl_constant": ("k[0] += 0x9E3779B97F4A7C15ull;", "k[0] += 0x9E3779B97F4A7C17ull;"),
+    "philox_nine_rounds": ("for (int r = 0; r < 10; ++r) {\n        if (r) {", "for (int r = 0; r < 9; ++r) {\n        if (r) {"),
+    "sample_word_halves_swapped": ("(w & 1) ? (uint32_t)(out[w / 2] >> 32) : (uint32_t)out[w / 2];",
+                                   "(w & 1) ? (uint32_t)out[w / 2] : (uint32_t)(out[w / 2] >> 32);"),
+    "sample_noise_sign": ("fmaf(z, c, -log2f(-log2f(u)))", "fmaf(z, c, log2f(-log2f(u)))"),
+    "sample_temperature_ignored": ("(float)(1.4426950408889634 / (double)temperature)", "1.4426950408889634f"),
+    "sample_exponential_noise": ("fmaf(z, c, -log2f(-log2f(u)))", "fmaf(z, c, -log2f(u))"),
     "softmax_sign": ("scratch[t] = exp(scratch[t] - m);", "scratch[t] = exp(m - scratch[t]);"),
     "scale_dropped": ("scratch[t] = sm_scale * dot;", "scratch[t] = dot;"),
     "k_v_swapped": ("dot += elem(q, dtype, qrow + c) * elem(k, dtype, krow + c);",
