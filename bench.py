@@ -7,6 +7,7 @@ steps rotate over them, so the 256 MB Infinity Cache cannot serve one step's rea
 previous step's.  Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload c8|c128k|c512|c1x4k|tiny] [--no-cpu]
+                  [--kv contiguous|paged|window] [--page-size P] [--window W] [--sample T]
   python bench.py --copy-calibration     (a plain device copy of known size, for counter scaling)
 
 The default workload is the 8-sequence batch (prefix lengths uniform in [1024, 8192], 16-node
@@ -42,6 +43,13 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--kv", default="contiguous", choices=("contiguous", "paged", "window"),
+                   help="K/V layout of the step: contiguous slots (default), a paged pool through a block "
+                        "table (--page-size), or a sliding window over the prefix (--window)")
+    p.add_argument("--page-size", type=int, default=16)
+    p.add_argument("--window", type=int, default=4096)
+    p.add_argument("--sample", type=float, default=0.0,
+                   help="temperature > 0: sampled verification (per-node draw instead of the argmax)")
     return p.parse_args()
 
 
@@ -84,7 +92,7 @@ def counters_for(kernel_src: str, workload: str):
     return float(vals["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(w, target_seconds: float):
+def cpu_baseline(w, target_seconds: float, temperature: float = 0.0):
     """The oracle (plain C, OpenMP over rows) on the host cores, on a bounded sample of the workload:
     whole steps over the first sequences, repeated until about target_seconds of CPU time."""
     import numpy as np
@@ -111,7 +119,10 @@ def cpu_baseline(w, target_seconds: float):
         oracle.tree_attention(q, k, v, ns, par, ks, pl, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                               head_dim=w.head_dim, sm_scale=w.sm_scale, total_slots=slot_end,
                               max_nodes=w.max_nodes, lib=lib)
-        tgt, _ = oracle.node_argmax(logits, lib=lib)
+        if temperature > 0:
+            tgt, _ = oracle.node_sample(logits, temperature, 0x5EED, reps, lib=lib)
+        else:
+            tgt, _ = oracle.node_argmax(logits, lib=lib)
         acc_r = oracle.greedy_accept(ns, par, draft, tgt, w.max_nodes, w.vocab, lib=lib)
         oracle.compact_kv(k[None], v[None], ks, pl, acc_r["accept_len"], acc_r["accept_path"], num_layers=1,
                           total_slots=slot_end, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, lib=lib)
@@ -155,7 +166,17 @@ def main():
 
     meta = {n: dev(getattr(w, n).astype(np.int32)) for n in ("node_start", "parent", "kv_start", "prefix_len",
                                                              "draft")}
-    host = {n: dev(getattr(w, n)) for n in ("q", "k", "v", "logits")}
+    host = {n: dev(getattr(w, n)) for n in ("q", "logits")}
+    if args.kv == "paged":
+        if w.dtype != synth.BF16:
+            raise SystemExit("paged K/V pools hold bf16")
+        pk, pv, bt = synth.paged_layout(w, args.page_size, 77)
+        host["k"], host["v"] = dev(pk), dev(pv)
+        meta["block_table"] = dev(bt)
+        num_pages = pk.shape[0] // args.page_size
+        del pk, pv
+    else:
+        host["k"], host["v"] = dev(w.k), dev(w.v)
     sets = [host] + [{n: t.clone() for n, t in host.items()} for _ in range(nsets - 1)]
     print(f"[bench] {nsets} input sets of {set_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
 
@@ -178,16 +199,35 @@ def main():
     m = {n: p(t) for n, t in meta.items()}
     calls = []
     for i, s in enumerate(sets):
+        if args.kv == "paged":
+            bts = meta["block_table"].shape[1]
+            attn = (p(s["q"]), p(s["k"]), p(s["v"]), p(out[i]), p(lse), m["node_start"], m["parent"],
+                    m["block_table"], bts, args.page_size, m["prefix_len"], B, T, maxn, num_pages, Hq, Hkv, D, dt,
+                    w.sm_scale, 0, aws.ptr, aws.nbytes, p(err), stream)
+            cmp = (p(s["k"]), p(s["v"]), esz, 1, num_pages * args.page_size * Hkv * D * esz, m["block_table"], bts,
+                   args.page_size, m["prefix_len"], p(acc_len), p(acc_path), B, maxn, num_pages, Hkv, D,
+                   p(new_len), p(err), stream)
+        else:
+            attn = (p(s["q"]), p(s["k"]), p(s["v"]), p(out[i]), p(lse), m["node_start"], m["parent"],
+                    m["kv_start"], m["prefix_len"], B, T, maxn, w.total_slots, Hq, Hkv, D, dt, w.sm_scale) + \
+                   ((args.window,) if args.kv == "window" else ()) + (aws.ptr, aws.nbytes, p(err), stream)
+            cmp = (p(s["k"]), p(s["v"]), esz, 1, w.total_slots * Hkv * D * esz, m["kv_start"], m["prefix_len"],
+                   p(acc_len), p(acc_path), B, maxn, w.total_slots, Hkv, D, p(new_len), p(err), stream)
+        if args.sample > 0:  # noise offset = the input set's index
+            sel = (p(s["logits"]), dt, w.vocab, T, w.vocab, args.sample, 0x5EED, i, p(target), gws.ptr, gws.nbytes,
+                   stream)
+        else:
+            sel = (p(s["logits"]), dt, w.vocab, T, w.vocab, p(target), p(maxv), gws.ptr, gws.nbytes, stream)
         calls.append((
-            (p(s["q"]), p(s["k"]), p(s["v"]), p(out[i]), p(lse), m["node_start"], m["parent"], m["kv_start"],
-             m["prefix_len"], B, T, maxn, w.total_slots, Hq, Hkv, D, dt, w.sm_scale, aws.ptr, aws.nbytes,
-             p(err), stream),
-            (p(s["logits"]), dt, w.vocab, T, w.vocab, p(target), p(maxv), gws.ptr, gws.nbytes, stream),
+            attn,
+            sel,
             (m["node_start"], m["parent"], m["draft"], p(target), B, T, maxn, w.vocab, p(acc_len), p(acc_path),
              p(bonus), p(out_tok), p(err), stream),
-            (p(s["k"]), p(s["v"]), esz, 1, w.total_slots * Hkv * D * esz, m["kv_start"], m["prefix_len"],
-             p(acc_len), p(acc_path), B, maxn, w.total_slots, Hkv, D, p(new_len), p(err), stream)))
-    f_attn, f_arg, f_acc, f_cmp = lib.ev_tree_attention, lib.ev_node_argmax, lib.ev_greedy_accept, lib.ev_compact_kv
+            cmp))
+    f_attn = {"contiguous": lib.ev_tree_attention, "paged": lib.ev_tree_attention_paged,
+              "window": lib.ev_tree_attention_window}[args.kv]
+    f_arg, f_acc = (lib.ev_node_sample if args.sample > 0 else lib.ev_node_argmax), lib.ev_greedy_accept
+    f_cmp = lib.ev_compact_kv_paged if args.kv == "paged" else lib.ev_compact_kv
 
     def step(c, ev0=None, ev1=None):
         if ev0 is not None:
@@ -235,9 +275,13 @@ def main():
         evs[i][4].record()
     torch.cuda.synchronize()
     kernel_ms = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K
-                 for j, n in enumerate(("tree_attention", "node_argmax", "greedy_accept", "compact_kv"))}
+                 for j, n in enumerate(("tree_attention", "node_sample" if args.sample > 0 else "node_argmax",
+                                        "greedy_accept", "compact_kv"))}
 
     acc_sum = int(acc_len.sum().item())
+    if args.kv == "window":  # only the last `window` prefix tokens (and the tree) are read
+        vis = sum(min(int(w.prefix_len[b]), args.window) + int(w.nodes_per_seq[b]) for b in range(B))
+        kv_bytes = 2 * vis * Hkv * D * esz
     tree_tps = T / (ms_step / 1e3)
     # algorithmic bytes of one attention launch: every K/V row of every (sequence, KV head) once,
     # Q read once, the output and the log-sum-exp written once
@@ -245,7 +289,7 @@ def main():
     achieved = alg_bytes / (attn_ms * 1e-3) / 1e9
     kv_gbps = kv_bytes / (attn_ms * 1e-3) / 1e9
     traffic = counters_for(os.path.join(ROOT, "draft_tree_verification_amd", "csrc", "ev_attention.hip"),
-                           args.workload)
+                           args.workload) if args.kv == "contiguous" else None
     rec = {
         "metric": METRIC,
         "value": round(tree_tps, 1),
@@ -259,13 +303,17 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == synth.BF16 else "f32",
         "data": "synthetic (seeded; shapes of the workload, no dataset or weights)",
-        "config": dict(synth.describe(w), input_sets=nsets, kv_bytes=kv_bytes),
+        "config": dict(synth.describe(w), input_sets=nsets, kv_bytes=kv_bytes,
+                       kv_layout={"contiguous": "contiguous", "paged": f"paged{args.page_size}",
+                                  "window": f"window{args.window}"}[args.kv],
+                       verification=f"sampled T={args.sample}" if args.sample > 0 else "greedy T=0"),
         "accepted_tokens_per_s": round(acc_sum / (ms_step / 1e3), 1),
         "accept_len_mean": acc_sum / B,
         "kv_read_gbps": round(kv_gbps, 1),
         "kv_read_pct_of_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
-        "argmax_gbps": round(w.logits.nbytes / (kernel_ms["node_argmax"] * 1e-3) / 1e9, 1),
+        "argmax_gbps": (None if args.sample > 0 else
+                        round(w.logits.nbytes / (kernel_ms["node_argmax"] * 1e-3) / 1e9, 1)),
         "wall_s_timed": round(t_wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
@@ -276,7 +324,7 @@ def main():
     if not args.no_cpu:
         del sets, out
         torch.cuda.empty_cache()
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.sample)
     print(json.dumps(rec), flush=True)
 
 

@@ -12,6 +12,8 @@
 // after the first few loads), so ties keep the earliest index for free.  Rows with few rows in the
 // batch are split across workgroups; the pieces meet through a 64-bit atomicMax on
 // (key << 32 | ~index) and the last-arriving workgroup writes the token.
+#include <cmath>
+
 #include "ev_internal.h"
 
 namespace {
@@ -33,6 +35,8 @@ struct ArgmaxArgs {
     float *max_value;
     unsigned long long *keys;  // [rows] (only when splits > 1)
     int32_t *counters;         // [rows]
+    float c;                   // sampling: log2(e) / temperature
+    uint64_t seed, offset;     // sampling: Philox key
 };
 
 // Order-preserving key of a bf16 value (16 bits, in a uint32): +-0 -> 0x8000, NaN -> 0xFFFF.
@@ -68,6 +72,37 @@ __device__ __forceinline__ us2 keys2(uint32_t w) {
 
 __device__ __forceinline__ unsigned long long pack(uint32_t key, int32_t idx) {
     return (static_cast<unsigned long long>(key) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(idx));
+}
+
+// The workgroup's best (key, lowest index) for `row`, then across the row's split workgroups;
+// the row's token (and the maximum, if asked for) is written once.  Workgroup-uniform call.
+__device__ __forceinline__ void finish_row(const ArgmaxArgs &a, int row, uint32_t best, int32_t bidx, bool f32) {
+    const int tid = threadIdx.x;
+    // workgroup reduction of (key, -index)
+    unsigned long long p = best ? pack(best, bidx) : 0ull;
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long q = __shfl_xor(p, o, 64);
+        p = q > p ? q : p;
+    }
+    __shared__ unsigned long long s_red[kThreads / 64];
+    if ((tid & 63) == 0) s_red[tid >> 6] = p;
+    __syncthreads();
+    if (tid != 0) return;
+    for (int w = 1; w < kThreads / 64; ++w) p = s_red[w] > p ? s_red[w] : p;
+
+    if (a.splits > 1) {
+        // all three are device-coherent atomics on the same path: the max lands before this
+        // workgroup's arrival is counted, and the last arriver's exchange sees every max
+        __hip_atomic_fetch_max(a.keys + row, p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ev::vm_wait();
+        const int old = ev::atomic_add_agent(a.counters + row, 1);
+        if (old != a.splits - 1) return;
+        p = __hip_atomic_exchange(a.keys + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.counters + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const uint32_t key = static_cast<uint32_t>(p >> 32);
+    a.target[row] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(p & 0xFFFFFFFFu));
+    if (a.max_value) a.max_value[row] = value_of_key(key, f32);
 }
 
 template <bool F32IN>
@@ -144,31 +179,121 @@ __global__ __launch_bounds__(kThreads) void node_argmax_kernel(const ArgmaxArgs 
         }
     }
 
-    // workgroup reduction of (key, -index)
-    unsigned long long p = best ? pack(best, bidx) : 0ull;
-    for (int o = 32; o > 0; o >>= 1) {
-        const unsigned long long q = __shfl_xor(p, o, 64);
-        p = q > p ? q : p;
-    }
-    __shared__ unsigned long long s_red[kThreads / 64];
-    if ((tid & 63) == 0) s_red[tid >> 6] = p;
-    __syncthreads();
-    if (tid != 0) return;
-    for (int w = 1; w < kThreads / 64; ++w) p = s_red[w] > p ? s_red[w] : p;
+    finish_row(a, row, best, bidx, F32IN);
+}
 
-    if (a.splits > 1) {
-        // all three are device-coherent atomics on the same path: the max lands before this
-        // workgroup's arrival is counted, and the last arriver's exchange sees every max
-        __hip_atomic_fetch_max(a.keys + row, p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ev::vm_wait();
-        const int old = ev::atomic_add_agent(a.counters + row, 1);
-        if (old != a.splits - 1) return;
-        p = __hip_atomic_exchange(a.keys + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a.counters + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// ---------------------------------------------------------------------------------------------
+// Sampled draw per row (temperature T > 0): y = argmax_v  z_v * c - log2(-log2(u_v)),
+// c = log2(e) / T, the Gumbel-max rule in base 2, so y ~ softmax(z / T).  Each draw feeds the same
+// greedy acceptance rule as the argmax: with drafted children taken as point proposals, a walk
+// that descends into the child holding the node's draw is speculative sampling along the tree
+// (the target's sampling distribution is kept; arex-research.com release note, opening section).
+// Uniforms: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) keyed by (seed, offset) on the
+// counter (v / 8, row, 0, 0); output k feeds elements 8j + 2k (low word) and 8j + 2k + 1 (high
+// word); word w -> u = ((w >> 9) + 1/2) * 2^-23.  One Philox block per thread per 16-byte load of
+// eight bf16 logits.  The scores are fp32: the logit times c fused with the noise subtraction.
+// Bound by the ALU (about 30 integer ops of Philox and two hardware log2 per element), not HBM.
+constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull, kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull, kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+
+__device__ __forceinline__ void philox4x64_10(uint64_t (&x)[4], uint64_t k0, uint64_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += kPhiloxW0;
+            k1 += kPhiloxW1;
+        }
+        const uint64_t lo0 = kPhiloxM0 * x[0], hi0 = __umul64hi(kPhiloxM0, x[0]);
+        const uint64_t lo1 = kPhiloxM1 * x[2], hi1 = __umul64hi(kPhiloxM1, x[2]);
+        const uint64_t y0 = hi1 ^ x[1] ^ k0, y2 = hi0 ^ x[3] ^ k1;
+        x[0] = y0;
+        x[1] = lo1;
+        x[2] = y2;
+        x[3] = lo0;
     }
-    const uint32_t key = static_cast<uint32_t>(p >> 32);
-    a.target[row] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(p & 0xFFFFFFFFu));
-    if (a.max_value) a.max_value[row] = value_of_key(key, F32IN);
+}
+
+// Score of one element from its logit and its 32-bit random word.
+__device__ __forceinline__ float sample_score(float z, uint32_t word, float c) {
+    const float u = (static_cast<float>(word >> 9) + 0.5f) * 0x1p-23f;  // exact: 24 significant bits
+    const float e = -__builtin_amdgcn_logf(u);                          // -log2(u) > 0
+    return __builtin_fmaf(z, c, -__builtin_amdgcn_logf(e));
+}
+
+template <bool F32IN>
+__global__ __launch_bounds__(kThreads) void node_sample_kernel(const ArgmaxArgs a) {
+    const int row = blockIdx.x / a.splits, split = blockIdx.x % a.splits;
+    const int v0 = split * a.seg;
+    const int v1 = min(a.vocab, v0 + a.seg);
+    const int tid = threadIdx.x;
+    uint32_t best = 0;
+    int32_t bidx = 0x7FFFFFFF;
+    const float c = a.c;
+    auto take = [&](float z, uint32_t word, int idx) {
+        const uint32_t k = key_f32(__builtin_bit_cast(uint32_t, sample_score(z, word, c)));
+        if (k > best) { best = k; bidx = idx; }
+    };
+    auto block = [&](int j, uint32_t (&w)[8]) {
+        uint64_t x[4] = {static_cast<uint64_t>(j), static_cast<uint64_t>(row), 0ull, 0ull};
+        philox4x64_10(x, a.seed, a.offset);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            w[2 * k] = static_cast<uint32_t>(x[k]);
+            w[2 * k + 1] = static_cast<uint32_t>(x[k] >> 32);
+        }
+    };
+    const unsigned char *rp = static_cast<const unsigned char *>(a.logits) +
+                              static_cast<int64_t>(row) * a.row_stride * (F32IN ? 4 : 2);
+    int base = v0 + tid * kChunk;
+    // two 16-byte loads (bf16) or four (fp32) ahead of the ALU work of each group of eight
+    for (; base + kSegQuantum + kChunk <= v1; base += 2 * kSegQuantum) {
+        float z[2][8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int at = base + h * kSegQuantum;
+            if constexpr (F32IN) {
+                const f32x4_t p = ev::ld16f_stream(reinterpret_cast<const float *>(rp) + at);
+                const f32x4_t q = ev::ld16f_stream(reinterpret_cast<const float *>(rp) + at + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { z[h][e] = p[e]; z[h][e + 4] = q[e]; }
+            } else {
+                const u32x4_t p = ev::ld16_stream(reinterpret_cast<const uint16_t *>(rp) + at);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    z[h][2 * e] = __builtin_bit_cast(float, p[e] << 16);
+                    z[h][2 * e + 1] = __builtin_bit_cast(float, p[e] & 0xFFFF0000u);
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int at = base + h * kSegQuantum;
+            uint32_t w[8];
+            block(at >> 3, w);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) take(z[h][e], w[e], at + e);
+        }
+    }
+    for (; base + kChunk <= v1; base += kSegQuantum) {
+        uint32_t w[8];
+        block(base >> 3, w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float z = F32IN ? reinterpret_cast<const float *>(rp)[base + e]
+                                  : __builtin_bit_cast(float, static_cast<uint32_t>(reinterpret_cast<const uint16_t *>(rp)[base + e]) << 16);
+            take(z, w[e], base + e);
+        }
+    }
+    if (base < v1) {  // ragged end of the row (fewer than eight elements): one block for all of them
+        uint32_t w[8];
+        block(base >> 3, w);
+        for (int e = base; e < v1; ++e) {
+            const float z = F32IN ? reinterpret_cast<const float *>(rp)[e]
+                                  : __builtin_bit_cast(float, static_cast<uint32_t>(reinterpret_cast<const uint16_t *>(rp)[e]) << 16);
+            take(z, w[e - base], e);
+        }
+    }
+    finish_row(a, row, best, bidx, F32IN);
 }
 
 struct ArgmaxPlan {
@@ -228,5 +353,45 @@ extern "C" ev_status ev_node_argmax(const void *logits, ev_dtype dtype, int64_t 
         hipLaunchKernelGGL(node_argmax_kernel<false>, grid, dim3(kThreads), 0, stream, args);
     else
         hipLaunchKernelGGL(node_argmax_kernel<true>, grid, dim3(kThreads), 0, stream, args);
+    return ev::launch_status();
+}
+
+extern "C" ev_status ev_node_sample(const void *logits, ev_dtype dtype, int64_t row_stride, int32_t num_rows,
+                                    int32_t vocab, float temperature, uint64_t seed, uint64_t offset,
+                                    int32_t *target_token, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    if (!logits || !target_token) return EV_ERR_NULL;
+    if (num_rows < 0 || vocab < 1 || row_stride < vocab) return EV_ERR_SHAPE;
+    if (!std::isfinite(temperature) || !(temperature > 0.f)) return EV_ERR_SHAPE;
+    const float c = static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
+    if (!std::isfinite(c)) return EV_ERR_SHAPE;
+    if (dtype != EV_BF16 && dtype != EV_F32) return EV_ERR_DTYPE;
+    const int esz = dtype == EV_BF16 ? 2 : 4;
+    if (!ev::aligned16(logits) || (row_stride * esz) % 16) return EV_ERR_ALIGN;
+    const ArgmaxPlan plan = make_plan(num_rows, vocab);
+    if (plan.bytes && (!workspace || workspace_bytes < plan.bytes)) return EV_ERR_WORKSPACE;
+    const ev_status dev = ev::check_device();
+    if (dev != EV_OK) return dev;
+    if (num_rows == 0) return EV_OK;
+    ArgmaxArgs args;
+    args.logits = logits;
+    args.row_stride = row_stride;
+    args.rows = num_rows;
+    args.vocab = vocab;
+    args.splits = plan.splits;
+    args.seg = plan.seg;
+    args.target = target_token;
+    args.max_value = nullptr;
+    args.keys = static_cast<unsigned long long *>(workspace);
+    args.counters = reinterpret_cast<int32_t *>(static_cast<unsigned char *>(workspace) +
+                                                static_cast<size_t>(num_rows) * 8);
+    args.c = c;
+    args.seed = seed;
+    args.offset = offset;
+    const dim3 grid(static_cast<unsigned>(num_rows) * plan.splits);
+    if (dtype == EV_BF16)
+        hipLaunchKernelGGL(node_sample_kernel<false>, grid, dim3(kThreads), 0, stream, args);
+    else
+        hipLaunchKernelGGL(node_sample_kernel<true>, grid, dim3(kThreads), 0, stream, args);
     return ev::launch_status();
 }

@@ -26,7 +26,7 @@ MAX_BATCH = 2048
 
 EXPORTS = ("ev_status_string", "ev_tree_attention_workspace_size", "ev_tree_attention",
            "ev_tree_attention_window", "ev_tree_attention_paged", "ev_node_argmax_workspace_size",
-           "ev_node_argmax", "ev_greedy_accept", "ev_compact_kv", "ev_compact_kv_paged")
+           "ev_node_argmax", "ev_node_sample", "ev_greedy_accept", "ev_compact_kv", "ev_compact_kv_paged")
 
 _lib = None
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -64,6 +64,9 @@ def load(path: str = LIB_PATH):
     lib.ev_node_argmax_workspace_size.argtypes = [_I32, _I32]
     lib.ev_node_argmax.restype = ctypes.c_int
     lib.ev_node_argmax.argtypes = [_P, ctypes.c_int, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]
+    lib.ev_node_sample.restype = ctypes.c_int
+    lib.ev_node_sample.argtypes = [_P, ctypes.c_int, _I64, _I32, _I32, _F, ctypes.c_uint64, ctypes.c_uint64, _P, _P,
+                                   _SZ, _P]
     lib.ev_greedy_accept.restype = ctypes.c_int
     lib.ev_greedy_accept.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]
     lib.ev_compact_kv.restype = ctypes.c_int
@@ -128,6 +131,12 @@ def ev_node_argmax(logits, dtype, row_stride, num_rows, vocab, target_token, max
                    stream) -> int:
     return load().ev_node_argmax(logits, dtype, row_stride, num_rows, vocab, target_token, max_value, workspace,
                                  workspace_bytes, stream)
+
+
+def ev_node_sample(logits, dtype, row_stride, num_rows, vocab, temperature, seed, offset, target_token, workspace,
+                   workspace_bytes, stream) -> int:
+    return load().ev_node_sample(logits, dtype, row_stride, num_rows, vocab, temperature, seed, offset, target_token,
+                                 workspace, workspace_bytes, stream)
 
 
 def ev_greedy_accept(node_start, parent, draft_token, target_token, batch, total_nodes, max_nodes, vocab, accept_len,
@@ -288,6 +297,27 @@ def node_argmax(logits, *, vocab: int = None, target=None, max_value=None, works
                         workspace.nbytes if workspace is not None else 0, _stream(stream))
     _check(st, "ev_node_argmax")
     return target, max_value, workspace
+
+
+def node_sample(logits, *, temperature: float, seed: int, offset: int, vocab: int = None, target=None,
+                workspace: Workspace = None, stream=None):
+    """Sampled token per row at temperature > 0 (ev_node_sample).  logits [R, stride] bf16/fp32.
+    Returns (target, workspace)."""
+    torch = _torch()
+    _need(logits, "logits", ndim=2)
+    R, stride = logits.shape
+    vocab = stride if vocab is None else vocab
+    if target is None:
+        target = torch.empty(R, dtype=torch.int32, device=logits.device)
+    need = ev_node_argmax_workspace_size(R, vocab)
+    if need and (workspace is None or workspace.nbytes < need):
+        workspace = Workspace(need, logits.device)
+    st = ev_node_sample(_addr(logits), _dtype_code(logits), stride, R, vocab, float(temperature),
+                        int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFFFFFFFFFF, _addr(target),
+                        workspace.ptr if workspace is not None else None,
+                        workspace.nbytes if workspace is not None else 0, _stream(stream))
+    _check(st, "ev_node_sample")
+    return target, workspace
 
 
 def greedy_accept(node_start, parent, draft_token, target_token, *, max_nodes: int, vocab: int, out=None,

@@ -20,7 +20,8 @@
  *
  * plus variants of the same operations: ev_tree_attention_window (a sliding window over the
  * prefix, as in the drafter's layers), ev_tree_attention_paged and ev_compact_kv_paged (KV
- * held in a paged pool through a per-sequence block table).
+ * held in a paged pool through a per-sequence block table), and ev_node_sample (the per-node
+ * draw of sampled verification at temperature > 0, in place of the argmax).
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer owned by the caller; the library allocates
@@ -192,6 +193,34 @@ size_t ev_node_argmax_workspace_size(int32_t num_rows, int32_t vocab);
 ev_status ev_node_argmax(const void *logits, ev_dtype dtype, int64_t row_stride, int32_t num_rows, int32_t vocab,
                          int32_t *target_token, float *max_value, void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ev_node_sample
+ *
+ * Sampled verification (temperature T > 0; the pages report T = 1 results: aiposthub.com
+ * analysis, section "它和 DFlash 2、DSpark 比，贏在哪個條件？"; arex-research.com release note,
+ * section "论文口径与推文口径").  target_token[r] = one draw from softmax(logits[r] / T):
+ *     y = argmax_v  fma(z_v, c, -log2(-log2(u_v))),   c = log2(e) / T
+ * (Gumbel-max in base 2), fp32 scores, largest score wins, lowest index on ties, a NaN logit
+ * above every number.  u_v = ((w >> 9) + 1/2) * 2^-23 with w the 32-bit word of element v from
+ * Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) under key (seed, offset) and counter
+ * (v / 8, r, 0, 0): 64-bit output k gives elements 8j + 2k (low half) and 8j + 2k + 1 (high
+ * half).  Use a fresh (seed, offset) per call (e.g. offset = decoding round) for fresh noise.
+ * Fed to ev_greedy_accept as target_token, the draws make the accept step speculative sampling
+ * along the tree with the drafted children as point proposals: a sequence descends into the
+ * child holding its node's draw and otherwise stops with the draw as bonus, which keeps the
+ * target's sampling distribution (release note, opening section).  The log2 is the hardware's
+ * (about 1 ulp), so a draw can differ from an exact evaluation only where two scores of the row
+ * agree to a few ulps.
+ *
+ *   logits, dtype, row_stride, num_rows, vocab   as in ev_node_argmax
+ *   temperature    finite, > 0, with log2(e) / temperature finite in fp32 (EV_ERR_SHAPE otherwise)
+ *   workspace      >= ev_node_argmax_workspace_size(num_rows, vocab) bytes, zeroed once before
+ *                  first use and left reusable (the same buffer may serve both calls)
+ * -------------------------------------------------------------------------------------------*/
+ev_status ev_node_sample(const void *logits, ev_dtype dtype, int64_t row_stride, int32_t num_rows, int32_t vocab,
+                         float temperature, uint64_t seed, uint64_t offset, int32_t *target_token, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * ev_greedy_accept

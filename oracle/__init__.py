@@ -80,6 +80,8 @@ def _bind(lib):
     lib.oracle_philox4x64_10.argtypes = [_P, _P, _P]
     lib.oracle_sample_uniform.restype = ctypes.c_float
     lib.oracle_sample_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64, _I64, _I64]
+    lib.oracle_sample_score.restype = ctypes.c_float
+    lib.oracle_sample_score.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, _I64, _I64]
     lib.oracle_node_sample.restype = None
     lib.oracle_node_sample.argtypes = [_P, _I32, _I64, _I32, _I32, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64,
                                        _P, _P]
@@ -215,6 +217,11 @@ def philox4x64_10(ctr, key, lib=None) -> np.ndarray:
 def sample_uniform(seed: int, offset: int, row: int, v: int, lib=None) -> float:
     """The uniform in (0, 1) that the sampled draw uses for element v of row `row`."""
     return float((lib or load()).oracle_sample_uniform(seed, offset, row, v))
+
+
+def sample_score(z: float, temperature: float, seed: int, offset: int, row: int, v: int, lib=None) -> float:
+    """The fp32 score the draw maximises for element v of row `row` with logit z."""
+    return float((lib or load()).oracle_sample_score(z, temperature, seed, offset, row, v))
 
 
 def node_sample(logits, temperature: float, seed: int, offset: int, vocab: int = None, row_stride: int = None,

@@ -330,9 +330,18 @@ float oracle_sample_uniform(uint64_t seed, uint64_t offset, int64_t row, int64_t
     return ((float)(word >> 9) + 0.5f) * 0x1p-23f;
 }
 
+static float sample_c(float temperature) { return (float)(1.4426950408889634 / (double)temperature); }
+
+static float score_of(float z, float c, float u) { return fmaf(z, c, -log2f(-log2f(u))); }
+
+/* Score of element v of row `row` with logit z (the quantity the draw maximises). */
+float oracle_sample_score(float z, float temperature, uint64_t seed, uint64_t offset, int64_t row, int64_t v) {
+    return score_of(z, sample_c(temperature), oracle_sample_uniform(seed, offset, row, v));
+}
+
 void oracle_node_sample(const void *logits, int32_t dtype, int64_t row_stride, int32_t num_rows, int32_t vocab,
                         float temperature, uint64_t seed, uint64_t offset, int32_t *token, float *score) {
-    const float c = (float)(1.4426950408889634 / (double)temperature);
+    const float c = sample_c(temperature);
 #pragma omp parallel for schedule(dynamic, 4)
     for (int32_t r = 0; r < num_rows; ++r) {
         const size_t base = (size_t)r * row_stride;
@@ -340,8 +349,7 @@ void oracle_node_sample(const void *logits, int32_t dtype, int64_t row_stride, i
         float bs = 0.f;
         for (int32_t v = 0; v < vocab; ++v) {
             const float z = (float)elem(logits, dtype, base + v);
-            const float u = oracle_sample_uniform(seed, offset, r, v);
-            const float s = fmaf(z, c, -log2f(-log2f(u)));
+            const float s = score_of(z, c, oracle_sample_uniform(seed, offset, r, v));
             if (isnan(s)) { best = v; bs = s; break; }
             if (best < 0 || s > bs) { best = v; bs = s; }
         }

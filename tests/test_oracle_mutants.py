@@ -38,7 +38,8 @@ MUTANTS = {
     "sample_word_halves_swapped": ("(w & 1) ? (uint32_t)(out[w / 2] >> 32) : (uint32_t)out[w / 2];",
                                    "(w & 1) ? (uint32_t)out[w / 2] : (uint32_t)(out[w / 2] >> 32);"),
     "sample_noise_sign": ("fmaf(z, c, -log2f(-log2f(u)))", "fmaf(z, c, log2f(-log2f(u)))"),
-    "sample_temperature_ignored": ("(float)(1.4426950408889634 / (double)temperature)", "1.4426950408889634f"),
+    "sample_temperature_ignored": ("return (float)(1.4426950408889634 / (double)temperature);",
+                                   "return 1.4426950408889634f;"),
     "sample_exponential_noise": ("fmaf(z, c, -log2f(-log2f(u)))", "fmaf(z, c, -log2f(u))"),
     "softmax_sign": ("scratch[t] = exp(scratch[t] - m);", "scratch[t] = exp(m - scratch[t]);"),
     "scale_dropped": ("scratch[t] = sm_scale * dot;", "scratch[t] = dot;"),
