@@ -48,6 +48,8 @@ def parse():
                         "table (--page-size), or a sliding window over the prefix (--window)")
     p.add_argument("--page-size", type=int, default=16)
     p.add_argument("--window", type=int, default=4096)
+    p.add_argument("--separate", action="store_true",
+                   help="run the per-node token, acceptance and compaction as three calls instead of the fused one")
     p.add_argument("--sample", type=float, default=0.0,
                    help="temperature > 0: sampled verification (per-node draw instead of the argmax)")
     return p.parse_args()
@@ -193,6 +195,7 @@ def main():
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     aws = ev.Workspace(ev.ev_tree_attention_workspace_size(B, maxn, Hq, Hkv, D), "cuda")
     gws = ev.Workspace(max(ev.ev_node_argmax_workspace_size(T, w.vocab), 256), "cuda")
+    sws = ev.Workspace(max(ev.ev_select_workspace_size(T, w.vocab), 256), "cuda")
     stream = torch.cuda.current_stream().cuda_stream
     lib = ev.load()
     p = lambda t: t.data_ptr()
@@ -213,6 +216,18 @@ def main():
                    ((args.window,) if args.kv == "window" else ()) + (aws.ptr, aws.nbytes, p(err), stream)
             cmp = (p(s["k"]), p(s["v"]), esz, 1, w.total_slots * Hkv * D * esz, m["kv_start"], m["prefix_len"],
                    p(acc_len), p(acc_path), B, maxn, w.total_slots, Hkv, D, p(new_len), p(err), stream)
+        if not args.separate:  # token, acceptance and compaction in one call (noise offset = the set's index)
+            head = (p(s["logits"]), dt, w.vocab, w.vocab, args.sample, 0x5EED, i, m["node_start"], m["parent"],
+                    m["draft"], B, T, maxn, p(s["k"]), p(s["v"]), esz, 1)
+            out_args = (p(target), p(acc_len), p(acc_path), p(bonus), p(out_tok), p(new_len), sws.ptr, sws.nbytes,
+                        p(err), stream)
+            if args.kv == "paged":
+                fused = head + (num_pages * args.page_size * Hkv * D * esz, m["block_table"],
+                                meta["block_table"].shape[1], args.page_size, m["prefix_len"], num_pages, Hkv, D)
+            else:
+                fused = head + (w.total_slots * Hkv * D * esz, m["kv_start"], m["prefix_len"], w.total_slots, Hkv, D)
+            calls.append((attn, fused + out_args))
+            continue
         if args.sample > 0:  # noise offset = the input set's index
             sel = (p(s["logits"]), dt, w.vocab, T, w.vocab, args.sample, 0x5EED, i, p(target), gws.ptr, gws.nbytes,
                    stream)
@@ -226,16 +241,23 @@ def main():
             cmp))
     f_attn = {"contiguous": lib.ev_tree_attention, "paged": lib.ev_tree_attention_paged,
               "window": lib.ev_tree_attention_window}[args.kv]
-    f_arg, f_acc = (lib.ev_node_sample if args.sample > 0 else lib.ev_node_argmax), lib.ev_greedy_accept
-    f_cmp = lib.ev_compact_kv_paged if args.kv == "paged" else lib.ev_compact_kv
+    if args.separate:
+        f_arg, f_acc = (lib.ev_node_sample if args.sample > 0 else lib.ev_node_argmax), lib.ev_greedy_accept
+        f_cmp = lib.ev_compact_kv_paged if args.kv == "paged" else lib.ev_compact_kv
+        fns = (f_attn, f_arg, f_acc, f_cmp)
+        names = ("tree_attention", "node_sample" if args.sample > 0 else "node_argmax", "greedy_accept", "compact_kv")
+    else:
+        fns = (f_attn, lib.ev_select_accept_compact_paged if args.kv == "paged" else lib.ev_select_accept_compact)
+        names = ("tree_attention", "select_accept_compact")
 
     def step(c, ev0=None, ev1=None):
         if ev0 is not None:
             ev0.record()
-        r = f_attn(*c[0])
+        r = fns[0](*c[0])
         if ev1 is not None:
             ev1.record()
-        r |= f_arg(*c[1]) | f_acc(*c[2]) | f_cmp(*c[3])
+        for f, a in zip(fns[1:], c[1:]):
+            r |= f(*a)
         return r
 
     for i in range(args.warmup):
@@ -265,18 +287,16 @@ def main():
     attn_ms = sum(a0[i].elapsed_time(a1[i]) for i in range(K)) / K
 
     # per-kernel breakdown (separate pass, not part of the timed region)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
-    fns = (f_attn, f_arg, f_acc, f_cmp)
+    nf = len(fns)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nf + 1)] for _ in range(K)]
     for i in range(K):
         c = calls[i % nsets]
-        for j in range(4):
+        for j in range(nf):
             evs[i][j].record()
             fns[j](*c[j])
-        evs[i][4].record()
+        evs[i][nf].record()
     torch.cuda.synchronize()
-    kernel_ms = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K
-                 for j, n in enumerate(("tree_attention", "node_sample" if args.sample > 0 else "node_argmax",
-                                        "greedy_accept", "compact_kv"))}
+    kernel_ms = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K for j, n in enumerate(names)}
 
     acc_sum = int(acc_len.sum().item())
     if args.kv == "window":  # only the last `window` prefix tokens (and the tree) are read
@@ -312,8 +332,7 @@ def main():
         "kv_read_gbps": round(kv_gbps, 1),
         "kv_read_pct_of_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
-        "argmax_gbps": (None if args.sample > 0 else
-                        round(w.logits.nbytes / (kernel_ms["node_argmax"] * 1e-3) / 1e9, 1)),
+        "selection": "separate calls" if args.separate else "fused (ev_select_accept_compact)",
         "wall_s_timed": round(t_wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,

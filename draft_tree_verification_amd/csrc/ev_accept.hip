@@ -10,6 +10,8 @@
 // right after its own prefix.
 //
 // One wavefront per sequence, lane i = tree node i (trees have at most 64 nodes).
+#include <cmath>
+
 #include "ev_internal.h"
 
 namespace {
@@ -20,35 +22,25 @@ struct AcceptArgs {
     int32_t *accept_len, *accept_path, *bonus, *out_tokens, *err_flag;
 };
 
-__global__ __launch_bounds__(64) void greedy_accept_kernel(const AcceptArgs a) {
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x;
-    int32_t *path = a.accept_path + static_cast<size_t>(b) * a.max_nodes;
-    int32_t *outt = a.out_tokens + static_cast<size_t>(b) * a.max_nodes;
-    const int ns0 = a.node_start[b], ns1 = a.node_start[b + 1];
-    const int n = ns1 - ns0;
-    int err = 0;
-    if (ns0 < 0 || ns1 > a.total_nodes || n < 1 || n > a.max_nodes) err = EV_DATA_BAD_NODES;
-    int par = -1, tgt = 0, dft = 0;
+// Acceptance of one sequence by one wave, lane i = node i of n, from each lane's parent, draft
+// token and target token.
+struct LaneAccept {
+    int err;    // EV_DATA_* bits found (the same in every lane); nothing is accepted then
+    int len;    // nodes on the accepted path, root included
+    int bonus;  // target token of the deepest accepted node
+    int depth;  // this lane's depth when its node is on the accepted path, else -1
+};
+
+__device__ LaneAccept accept_lanes(int lane, int n, int err, int par, int tgt, int dft, int vocab) {
     if (!err && lane < n) {
-        par = a.parent[ns0 + lane];
-        tgt = a.target[ns0 + lane];
-        dft = a.draft[ns0 + lane];
         if (lane == 0 ? par != -1 : (par < 0 || par >= lane)) err |= EV_DATA_BAD_PARENT;
-        if (tgt < 0 || tgt >= a.vocab) err |= EV_DATA_BAD_TOKEN;
-        if (lane > 0 && (dft < 0 || dft >= a.vocab)) err |= EV_DATA_BAD_TOKEN;
+        if (tgt < 0 || tgt >= vocab) err |= EV_DATA_BAD_TOKEN;
+        if (lane > 0 && (dft < 0 || dft >= vocab)) err |= EV_DATA_BAD_TOKEN;
     }
     // OR of the error bits over the wave
     for (int o = 32; o > 0; o >>= 1) err |= __shfl_xor(err, o, 64);
-    if (err) {
-        if (lane == 0) {
-            ev::flag_error(a.err_flag, err);
-            a.accept_len[b] = 0;
-            a.bonus[b] = -1;
-        }
-        for (int i = lane; i < a.max_nodes; i += 64) path[i] = outt[i] = -1;
-        return;
-    }
+    LaneAccept r{err, 0, -1, -1};
+    if (err) return r;
     // an edge agrees when the child's draft token is the parent's greedy token
     const int tpar = __shfl(tgt, par >= 0 ? par : 0, 64);
     const bool agree = lane < n && (lane == 0 || dft == tpar);
@@ -72,23 +64,70 @@ __global__ __launch_bounds__(64) void greedy_accept_kernel(const AcceptArgs a) {
     int key = (lane < n && acc) ? (depth << 8) | (255 - lane) : -1;
     for (int o = 32; o > 0; o >>= 1) key = max(key, __shfl_xor(key, o, 64));
     const int best = 255 - (key & 255);
-    const int len = (key >> 8) + 1;
+    r.len = (key >> 8) + 1;
     const uint32_t mlo = __shfl(static_cast<uint32_t>(anc), best, 64);
     const uint32_t mhi = __shfl(static_cast<uint32_t>(anc >> 32), best, 64);
     const uint64_t on_path = (static_cast<uint64_t>(mhi) << 32) | mlo;
-    const int bonus = __shfl(tgt, best, 64);
-    // each position is written by exactly one lane: the on-path node of that depth, or lane d
-    if (lane < n && ((on_path >> lane) & 1ull)) {
-        path[depth] = lane;
-        if (lane > 0) outt[depth - 1] = dft;
+    r.bonus = __shfl(tgt, best, 64);
+    r.depth = (lane < n && ((on_path >> lane) & 1ull)) ? depth : -1;
+    return r;
+}
+
+// The acceptance outputs of sequence b; each position is written by exactly one lane: the
+// on-path node of that depth, or lane d past the path.
+__device__ void write_accept(const AcceptArgs &a, int b, int lane, const LaneAccept &r, int dft) {
+    int32_t *path = a.accept_path + static_cast<size_t>(b) * a.max_nodes;
+    int32_t *outt = a.out_tokens + static_cast<size_t>(b) * a.max_nodes;
+    if (r.err) {
+        if (lane == 0) {
+            ev::flag_error(a.err_flag, r.err);
+            a.accept_len[b] = 0;
+            a.bonus[b] = -1;
+        }
+        for (int i = lane; i < a.max_nodes; i += 64) path[i] = outt[i] = -1;
+        return;
     }
-    if (lane >= len && lane < a.max_nodes) path[lane] = outt[lane] = -1;
+    if (r.depth >= 0) {
+        path[r.depth] = lane;
+        if (lane > 0) outt[r.depth - 1] = dft;
+    }
+    if (lane >= r.len && lane < a.max_nodes) path[lane] = outt[lane] = -1;
     if (lane == 0) {
-        outt[len - 1] = bonus;
-        a.accept_len[b] = len;
-        a.bonus[b] = bonus;
+        outt[r.len - 1] = r.bonus;
+        a.accept_len[b] = r.len;
+        a.bonus[b] = r.bonus;
     }
 }
+
+// The sequence's node range (bad ranges flag EV_DATA_BAD_NODES).
+__device__ __forceinline__ int node_range(const AcceptArgs &a, int b, int &ns0, int &n) {
+    ns0 = a.node_start[b];
+    const int ns1 = a.node_start[b + 1];
+    n = ns1 - ns0;
+    return (ns0 < 0 || ns1 > a.total_nodes || n < 1 || n > a.max_nodes) ? EV_DATA_BAD_NODES : 0;
+}
+
+__global__ __launch_bounds__(64) void greedy_accept_kernel(const AcceptArgs a) {
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    int ns0, n;
+    const int err = node_range(a, b, ns0, n);
+    int par = -1, tgt = 0, dft = 0;
+    if (!err && lane < n) {
+        par = a.parent[ns0 + lane];
+        tgt = a.target[ns0 + lane];
+        dft = a.draft[ns0 + lane];
+    }
+    write_accept(a, b, lane, accept_lanes(lane, n, err, par, tgt, dft, a.vocab), dft);
+}
+
+// Fused step: the per-piece winners of the selection pass and where the row tokens go.
+struct SelectArgs {
+    AcceptArgs acc;                      // target: unused (the tokens come from the pieces)
+    const unsigned long long *pieces;    // [rows][splits]: (order key << 32) | ~index
+    int32_t splits;
+    int32_t *target_out;                 // [rows] the finished tokens
+};
 
 struct CompactArgs {
     unsigned char *k, *v;
@@ -109,25 +148,61 @@ constexpr int kBatchRows = 8;
 // read before anything overwrites it even though each thread streams its own columns
 // independently.  With a block table the same holds row by row as long as the sequence's pages
 // are distinct (tokens then map to distinct rows).
-__global__ __launch_bounds__(kCompactThreads) void compact_kv_kernel(const CompactArgs a) {
+//
+// Fused step (FUSED): wave 0 first finishes the sequence's target tokens from the selection
+// pass's pieces (maximum of the packed words), runs the acceptance rule, and hands the accepted
+// path to the other waves through LDS; the layer-0 workgroup writes the tokens and the
+// acceptance outputs.  Every layer's workgroup repeats the (small) acceptance work instead of
+// waiting for another workgroup.
+template <bool FUSED>
+__global__ __launch_bounds__(kCompactThreads) void compact_kv_kernel(const CompactArgs a, const SelectArgs sel) {
     const int b = blockIdx.x;
     const int layer = blockIdx.y;
     const int tid = threadIdx.x;
     __shared__ int64_t s_src[EV_MAX_NODES], s_dst[EV_MAX_NODES];
-    const int len = a.accept_len[b];
+    __shared__ int s_path[FUSED ? EV_MAX_NODES : 1];
+    __shared__ int s_len;
     const int L = a.prefix_len[b];
-    int err = 0, p = 0;
-    if (len > 0) {
-        if (len > a.max_nodes) err = EV_DATA_BAD_PATH;
-        if (!err && tid < len) {
-            p = a.accept_path[static_cast<size_t>(b) * a.max_nodes + tid];
-            const int prev = tid ? a.accept_path[static_cast<size_t>(b) * a.max_nodes + tid - 1] : -1;
-            if (tid == 0 ? p != 0 : p <= prev) err = EV_DATA_BAD_PATH;
+    int len, err = 0, p = 0, last = 0;
+    if constexpr (FUSED) {
+        if (tid < 64) {
+            const AcceptArgs &x = sel.acc;
+            int ns0, n;
+            const int err0 = node_range(x, b, ns0, n);
+            int par = -1, tgt = 0, dft = 0;
+            if (!err0 && tid < n) {
+                const int row = ns0 + tid;
+                par = x.parent[row];
+                dft = x.draft[row];
+                const unsigned long long *pc = sel.pieces + static_cast<size_t>(row) * sel.splits;
+                unsigned long long w = 0;
+                for (int k = 0; k < sel.splits; ++k) w = pc[k] > w ? pc[k] : w;
+                tgt = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(w & 0xFFFFFFFFu));
+                if (layer == 0) sel.target_out[row] = tgt;
+            }
+            const LaneAccept r = accept_lanes(tid, n, err0, par, tgt, dft, x.vocab);
+            if (layer == 0) write_accept(x, b, tid, r, dft);
+            if (r.depth >= 0) s_path[r.depth] = tid;
+            if (tid == 0) s_len = r.err ? 0 : r.len;
         }
+        __syncthreads();
+        len = s_len;
+        if (tid < len) p = s_path[tid];
+        if (len > 0) last = s_path[len - 1];
+    } else {
+        len = a.accept_len[b];
+        if (len > 0) {
+            if (len > a.max_nodes) err = EV_DATA_BAD_PATH;
+            if (!err && tid < len) {
+                p = a.accept_path[static_cast<size_t>(b) * a.max_nodes + tid];
+                const int prev = tid ? a.accept_path[static_cast<size_t>(b) * a.max_nodes + tid - 1] : -1;
+                if (tid == 0 ? p != 0 : p <= prev) err = EV_DATA_BAD_PATH;
+            }
+        }
+        err = __syncthreads_or(err) ? EV_DATA_BAD_PATH : 0;
+        if (len > 0 && !err) last = a.accept_path[static_cast<size_t>(b) * a.max_nodes + len - 1];
     }
-    err = __syncthreads_or(err) ? EV_DATA_BAD_PATH : 0;
     if (len > 0 && !err) {
-        const int last = a.accept_path[static_cast<size_t>(b) * a.max_nodes + len - 1];
         if (!a.block_table) {
             const int s0 = a.kv_start[b];
             if (s0 < 0 || L < 0 || static_cast<int64_t>(s0) + L + last >= a.total_slots) err = EV_DATA_BAD_SLOTS;
@@ -198,13 +273,14 @@ extern "C" ev_status ev_greedy_accept(const int32_t *node_start, const int32_t *
 }
 
 namespace {
-ev_status launch_compact(void *k_cache, void *v_cache, int32_t elem_bytes, int32_t num_layers,
-                         int64_t layer_stride_bytes, const int32_t *kv_start, const int32_t *block_table,
-                         int32_t bt_stride, int32_t page_size, const int32_t *prefix_len, const int32_t *accept_len,
-                         const int32_t *accept_path, int32_t batch, int32_t max_nodes, int64_t total_slots,
-                         int32_t num_kv_heads, int32_t head_dim, int32_t *new_len, int32_t *err_flag,
-                         hipStream_t stream) {
-    if (!k_cache || !v_cache || !prefix_len || !accept_len || !accept_path || !new_len ||
+// Checks of the compaction's arguments; fills the kernel arguments.
+ev_status compact_args(void *k_cache, void *v_cache, int32_t elem_bytes, int32_t num_layers,
+                       int64_t layer_stride_bytes, const int32_t *kv_start, const int32_t *block_table,
+                       int32_t bt_stride, int32_t page_size, const int32_t *prefix_len, const int32_t *accept_len,
+                       const int32_t *accept_path, int32_t batch, int32_t max_nodes, int64_t total_slots,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t *new_len, int32_t *err_flag, bool fused,
+                       CompactArgs &args) {
+    if (!k_cache || !v_cache || !prefix_len || (!fused && (!accept_len || !accept_path)) || !new_len ||
         (block_table ? false : !kv_start))
         return EV_ERR_NULL;
     if (batch < 0 || num_layers < 1 || max_nodes < 1 || max_nodes > EV_MAX_NODES || total_slots < 0 ||
@@ -216,10 +292,6 @@ ev_status launch_compact(void *k_cache, void *v_cache, int32_t elem_bytes, int32
     if (!ev::aligned16(k_cache) || !ev::aligned16(v_cache) || row_bytes % 16 || layer_stride_bytes % 16)
         return EV_ERR_ALIGN;
     if (new_len == prefix_len) return EV_ERR_SHAPE;
-    const ev_status dev = ev::check_device();
-    if (dev != EV_OK) return dev;
-    if (batch == 0) return EV_OK;
-    CompactArgs args;
     args.k = static_cast<unsigned char *>(k_cache);
     args.v = static_cast<unsigned char *>(v_cache);
     args.layer_stride = layer_stride_bytes;
@@ -237,7 +309,82 @@ ev_status launch_compact(void *k_cache, void *v_cache, int32_t elem_bytes, int32
     args.row_bytes = row_bytes;
     args.new_len = new_len;
     args.err_flag = err_flag;
-    hipLaunchKernelGGL(compact_kv_kernel, dim3(batch, num_layers), dim3(kCompactThreads), 0, stream, args);
+    return EV_OK;
+}
+
+ev_status launch_compact(void *k_cache, void *v_cache, int32_t elem_bytes, int32_t num_layers,
+                         int64_t layer_stride_bytes, const int32_t *kv_start, const int32_t *block_table,
+                         int32_t bt_stride, int32_t page_size, const int32_t *prefix_len, const int32_t *accept_len,
+                         const int32_t *accept_path, int32_t batch, int32_t max_nodes, int64_t total_slots,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t *new_len, int32_t *err_flag,
+                         hipStream_t stream) {
+    CompactArgs args;
+    const ev_status st = compact_args(k_cache, v_cache, elem_bytes, num_layers, layer_stride_bytes, kv_start,
+                                      block_table, bt_stride, page_size, prefix_len, accept_len, accept_path, batch,
+                                      max_nodes, total_slots, num_kv_heads, head_dim, new_len, err_flag, false, args);
+    if (st != EV_OK) return st;
+    const ev_status dev = ev::check_device();
+    if (dev != EV_OK) return dev;
+    if (batch == 0) return EV_OK;
+    hipLaunchKernelGGL(compact_kv_kernel<false>, dim3(batch, num_layers), dim3(kCompactThreads), 0, stream, args,
+                       SelectArgs{});
+    return ev::launch_status();
+}
+
+size_t select_bytes(int32_t rows, int32_t vocab) {
+    if (rows <= 0 || vocab < 1) return 0;
+    const size_t b = static_cast<size_t>(rows) * ev::select_splits(rows, vocab) * 8;
+    return (b + 255) / 256 * 256;
+}
+
+// The fused step: every argument is checked before the first launch; then the selection pass
+// (pieces into the workspace) and the fused compaction launch, which finishes the row tokens,
+// accepts and compacts.
+ev_status select_accept_compact(const void *logits, ev_dtype dtype, int64_t row_stride, int32_t vocab,
+                                float temperature, uint64_t seed, uint64_t offset, const int32_t *node_start,
+                                const int32_t *parent, const int32_t *draft_token, int32_t batch,
+                                int32_t total_nodes, int32_t max_nodes, void *k_cache, void *v_cache,
+                                int32_t elem_bytes, int32_t num_layers, int64_t layer_stride_bytes,
+                                const int32_t *kv_start, const int32_t *block_table, int32_t bt_stride,
+                                int32_t page_size, const int32_t *prefix_len, int64_t total_slots,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t *target_token, int32_t *accept_len,
+                                int32_t *accept_path, int32_t *bonus_token, int32_t *out_tokens, int32_t *new_len,
+                                void *workspace, size_t workspace_bytes, int32_t *err_flag, hipStream_t stream) {
+    if (!logits || !node_start || !parent || !draft_token || !target_token || !accept_len || !accept_path ||
+        !bonus_token || !out_tokens)
+        return EV_ERR_NULL;
+    if (batch < 0 || total_nodes < 0 || max_nodes < 1 || max_nodes > EV_MAX_NODES || vocab < 1 || row_stride < vocab)
+        return EV_ERR_SHAPE;
+    if (!std::isfinite(temperature) || temperature < 0.f) return EV_ERR_SHAPE;
+    // (the draw's scale log2(e)/T must be a finite float)
+    if (temperature > 0.f && !std::isfinite(static_cast<float>(1.4426950408889634 / static_cast<double>(temperature))))
+        return EV_ERR_SHAPE;
+    if (dtype != EV_BF16 && dtype != EV_F32) return EV_ERR_DTYPE;
+    const int esz = dtype == EV_BF16 ? 2 : 4;
+    if (!ev::aligned16(logits) || (row_stride * esz) % 16) return EV_ERR_ALIGN;
+    const size_t need = select_bytes(total_nodes, vocab);
+    if (need && (!workspace || workspace_bytes < need)) return EV_ERR_WORKSPACE;
+    if (need && (reinterpret_cast<uintptr_t>(workspace) & 7u)) return EV_ERR_ALIGN;
+    CompactArgs cargs;
+    ev_status st = compact_args(k_cache, v_cache, elem_bytes, num_layers, layer_stride_bytes, kv_start, block_table,
+                                bt_stride, page_size, prefix_len, nullptr, nullptr, batch, max_nodes, total_slots,
+                                num_kv_heads, head_dim, new_len, err_flag, true, cargs);
+    if (st != EV_OK) return st;
+    const ev_status dev = ev::check_device();
+    if (dev != EV_OK) return dev;
+    if (batch == 0) return EV_OK;
+    SelectArgs sel{};
+    sel.acc = AcceptArgs{node_start, parent, draft_token, nullptr, batch, total_nodes, max_nodes, vocab,
+                         accept_len, accept_path, bonus_token, out_tokens, err_flag};
+    sel.pieces = static_cast<const unsigned long long *>(workspace);
+    sel.splits = total_nodes > 0 ? ev::select_splits(total_nodes, vocab) : 1;
+    sel.target_out = target_token;
+    if (total_nodes > 0) {
+        st = ev::launch_select_pieces(logits, dtype, row_stride, total_nodes, vocab, temperature, seed, offset,
+                                      static_cast<unsigned long long *>(workspace), stream);
+        if (st != EV_OK) return st;
+    }
+    hipLaunchKernelGGL(compact_kv_kernel<true>, dim3(batch, num_layers), dim3(kCompactThreads), 0, stream, cargs, sel);
     return ev::launch_status();
 }
 }  // namespace
@@ -264,4 +411,39 @@ extern "C" ev_status ev_compact_kv_paged(void *k_pages, void *v_pages, int32_t e
                           bt_stride, page_size, prefix_len, accept_len, accept_path, batch, max_nodes,
                           static_cast<int64_t>(num_pages) * page_size, num_kv_heads, head_dim, new_len, err_flag,
                           stream);
+}
+
+extern "C" size_t ev_select_workspace_size(int32_t num_rows, int32_t vocab) { return select_bytes(num_rows, vocab); }
+
+extern "C" ev_status ev_select_accept_compact(
+    const void *logits, ev_dtype dtype, int64_t row_stride, int32_t vocab, float temperature, uint64_t seed,
+    uint64_t offset, const int32_t *node_start, const int32_t *parent, const int32_t *draft_token, int32_t batch,
+    int32_t total_nodes, int32_t max_nodes, void *k_cache, void *v_cache, int32_t elem_bytes, int32_t num_layers,
+    int64_t layer_stride_bytes, const int32_t *kv_start, const int32_t *prefix_len, int64_t total_slots,
+    int32_t num_kv_heads, int32_t head_dim, int32_t *target_token, int32_t *accept_len, int32_t *accept_path,
+    int32_t *bonus_token, int32_t *out_tokens, int32_t *new_len, void *workspace, size_t workspace_bytes,
+    int32_t *err_flag, hipStream_t stream) {
+    return select_accept_compact(logits, dtype, row_stride, vocab, temperature, seed, offset, node_start, parent,
+                                 draft_token, batch, total_nodes, max_nodes, k_cache, v_cache, elem_bytes, num_layers,
+                                 layer_stride_bytes, kv_start, nullptr, 0, 0, prefix_len, total_slots, num_kv_heads,
+                                 head_dim, target_token, accept_len, accept_path, bonus_token, out_tokens, new_len,
+                                 workspace, workspace_bytes, err_flag, stream);
+}
+
+extern "C" ev_status ev_select_accept_compact_paged(
+    const void *logits, ev_dtype dtype, int64_t row_stride, int32_t vocab, float temperature, uint64_t seed,
+    uint64_t offset, const int32_t *node_start, const int32_t *parent, const int32_t *draft_token, int32_t batch,
+    int32_t total_nodes, int32_t max_nodes, void *k_pages, void *v_pages, int32_t elem_bytes, int32_t num_layers,
+    int64_t layer_stride_bytes, const int32_t *block_table, int32_t bt_stride, int32_t page_size,
+    const int32_t *prefix_len, int32_t num_pages, int32_t num_kv_heads, int32_t head_dim, int32_t *target_token,
+    int32_t *accept_len, int32_t *accept_path, int32_t *bonus_token, int32_t *out_tokens, int32_t *new_len,
+    void *workspace, size_t workspace_bytes, int32_t *err_flag, hipStream_t stream) {
+    if (!block_table) return EV_ERR_NULL;
+    if (page_size < 1 || bt_stride < 1 || num_pages < 0) return EV_ERR_SHAPE;
+    return select_accept_compact(logits, dtype, row_stride, vocab, temperature, seed, offset, node_start, parent,
+                                 draft_token, batch, total_nodes, max_nodes, k_pages, v_pages, elem_bytes, num_layers,
+                                 layer_stride_bytes, nullptr, block_table, bt_stride, page_size, prefix_len,
+                                 static_cast<int64_t>(num_pages) * page_size, num_kv_heads, head_dim, target_token,
+                                 accept_len, accept_path, bonus_token, out_tokens, new_len, workspace,
+                                 workspace_bytes, err_flag, stream);
 }

@@ -11,7 +11,10 @@
 // ops, and the index of a new maximum is searched only when a load beats the running best (rare
 // after the first few loads), so ties keep the earliest index for free.  Rows with few rows in the
 // batch are split across workgroups; the pieces meet through a 64-bit atomicMax on
-// (key << 32 | ~index) and the last-arriving workgroup writes the token.
+// (key << 32 | ~index) and the last-arriving workgroup writes the token.  In the fused step
+// (ev_select_accept_compact) each piece instead stores its (key << 32 | ~index) word, and the
+// acceptance launch that follows takes the maximum over a row's pieces: no atomics, no arrival
+// counting, nothing to reset.
 #include <cmath>
 
 #include "ev_internal.h"
@@ -35,6 +38,7 @@ struct ArgmaxArgs {
     float *max_value;
     unsigned long long *keys;  // [rows] (only when splits > 1)
     int32_t *counters;         // [rows]
+    unsigned long long *pieces;  // [rows][splits] each piece's winner (fused step), else NULL
     float c;                   // sampling: log2(e) / temperature
     uint64_t seed, offset;     // sampling: Philox key
 };
@@ -90,6 +94,10 @@ __device__ __forceinline__ void finish_row(const ArgmaxArgs &a, int row, uint32_
     if (tid != 0) return;
     for (int w = 1; w < kThreads / 64; ++w) p = s_red[w] > p ? s_red[w] : p;
 
+    if (a.pieces) {  // the acceptance launch combines the row's pieces
+        a.pieces[static_cast<size_t>(row) * a.splits + blockIdx.x % a.splits] = p;
+        return;
+    }
     if (a.splits > 1) {
         // all three are device-coherent atomics on the same path: the max lands before this
         // workgroup's arrival is counted, and the last arriver's exchange sees every max
@@ -318,6 +326,41 @@ ArgmaxPlan make_plan(int32_t rows, int32_t vocab) {
 
 }  // namespace
 
+namespace ev {
+
+int select_splits(int32_t rows, int32_t vocab) { return make_plan(rows, vocab).splits; }
+
+ev_status launch_select_pieces(const void *logits, ev_dtype dtype, int64_t row_stride, int32_t rows, int32_t vocab,
+                               float temperature, uint64_t seed, uint64_t offset, unsigned long long *pieces,
+                               hipStream_t stream) {
+    const ArgmaxPlan plan = make_plan(rows, vocab);
+    ArgmaxArgs args{};
+    args.logits = logits;
+    args.row_stride = row_stride;
+    args.rows = rows;
+    args.vocab = vocab;
+    args.splits = plan.splits;
+    args.seg = plan.seg;
+    args.pieces = pieces;
+    const dim3 grid(static_cast<unsigned>(rows) * plan.splits);
+    if (temperature > 0.f) {
+        args.c = static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
+        args.seed = seed;
+        args.offset = offset;
+        if (dtype == EV_BF16)
+            hipLaunchKernelGGL(node_sample_kernel<false>, grid, dim3(kThreads), 0, stream, args);
+        else
+            hipLaunchKernelGGL(node_sample_kernel<true>, grid, dim3(kThreads), 0, stream, args);
+    } else if (dtype == EV_BF16) {
+        hipLaunchKernelGGL(node_argmax_kernel<false>, grid, dim3(kThreads), 0, stream, args);
+    } else {
+        hipLaunchKernelGGL(node_argmax_kernel<true>, grid, dim3(kThreads), 0, stream, args);
+    }
+    return launch_status();
+}
+
+}  // namespace ev
+
 extern "C" size_t ev_node_argmax_workspace_size(int32_t num_rows, int32_t vocab) {
     if (num_rows < 0 || vocab < 1) return 0;
     return make_plan(num_rows, vocab).bytes;
@@ -336,7 +379,7 @@ extern "C" ev_status ev_node_argmax(const void *logits, ev_dtype dtype, int64_t 
     const ev_status dev = ev::check_device();
     if (dev != EV_OK) return dev;
     if (num_rows == 0) return EV_OK;
-    ArgmaxArgs args;
+    ArgmaxArgs args{};
     args.logits = logits;
     args.row_stride = row_stride;
     args.rows = num_rows;
@@ -373,7 +416,7 @@ extern "C" ev_status ev_node_sample(const void *logits, ev_dtype dtype, int64_t 
     const ev_status dev = ev::check_device();
     if (dev != EV_OK) return dev;
     if (num_rows == 0) return EV_OK;
-    ArgmaxArgs args;
+    ArgmaxArgs args{};
     args.logits = logits;
     args.row_stride = row_stride;
     args.rows = num_rows;

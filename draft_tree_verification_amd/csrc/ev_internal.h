@@ -21,6 +21,14 @@ int current_device();
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline ev_status launch_status() { return hipGetLastError() == hipSuccess ? EV_OK : EV_ERR_HIP; }
 
+// The per-node selection pass of the fused step (ev_argmax.hip): argmax (temperature 0) or the
+// sampled draw of every row, each row cut into select_splits() pieces whose winners, packed as
+// (order key << 32 | ~index), go to pieces[row * splits + piece].  Arguments already validated.
+int select_splits(int32_t rows, int32_t vocab);
+ev_status launch_select_pieces(const void *logits, ev_dtype dtype, int64_t row_stride, int32_t rows, int32_t vocab,
+                               float temperature, uint64_t seed, uint64_t offset, unsigned long long *pieces,
+                               hipStream_t stream);
+
 // ---------------------------------------------------------------- device side
 __device__ __forceinline__ u32x4_t ld16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
 

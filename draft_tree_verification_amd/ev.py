@@ -26,7 +26,8 @@ MAX_BATCH = 2048
 
 EXPORTS = ("ev_status_string", "ev_tree_attention_workspace_size", "ev_tree_attention",
            "ev_tree_attention_window", "ev_tree_attention_paged", "ev_node_argmax_workspace_size",
-           "ev_node_argmax", "ev_node_sample", "ev_greedy_accept", "ev_compact_kv", "ev_compact_kv_paged")
+           "ev_node_argmax", "ev_node_sample", "ev_greedy_accept", "ev_compact_kv", "ev_compact_kv_paged",
+           "ev_select_workspace_size", "ev_select_accept_compact", "ev_select_accept_compact_paged")
 
 _lib = None
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -75,6 +76,17 @@ def load(path: str = LIB_PATH):
     lib.ev_compact_kv_paged.restype = ctypes.c_int
     lib.ev_compact_kv_paged.argtypes = [_P, _P, _I32, _I32, _I64, _P, _I32, _I32, _P, _P, _P, _I32, _I32, _I32, _I32,
                                         _I32, _P, _P, _P]
+    _U64 = ctypes.c_uint64
+    lib.ev_select_workspace_size.restype = _SZ
+    lib.ev_select_workspace_size.argtypes = [_I32, _I32]
+    lib.ev_select_accept_compact.restype = ctypes.c_int
+    lib.ev_select_accept_compact.argtypes = [_P, ctypes.c_int, _I64, _I32, _F, _U64, _U64, _P, _P, _P, _I32, _I32,
+                                             _I32, _P, _P, _I32, _I32, _I64, _P, _P, _I64, _I32, _I32, _P, _P, _P,
+                                             _P, _P, _P, _P, _SZ, _P, _P]
+    lib.ev_select_accept_compact_paged.restype = ctypes.c_int
+    lib.ev_select_accept_compact_paged.argtypes = [_P, ctypes.c_int, _I64, _I32, _F, _U64, _U64, _P, _P, _P, _I32,
+                                                   _I32, _I32, _P, _P, _I32, _I32, _I64, _P, _I32, _I32, _P, _I32,
+                                                   _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -151,6 +163,38 @@ def ev_compact_kv(k_cache, v_cache, elem_bytes, num_layers, layer_stride_bytes, 
     return load().ev_compact_kv(k_cache, v_cache, elem_bytes, num_layers, layer_stride_bytes, kv_start, prefix_len,
                                 accept_len, accept_path, batch, max_nodes, total_slots, num_kv_heads, head_dim,
                                 new_len, err_flag, stream)
+
+
+def ev_select_workspace_size(num_rows, vocab) -> int:
+    return int(load().ev_select_workspace_size(num_rows, vocab))
+
+
+def ev_select_accept_compact(logits, dtype, row_stride, vocab, temperature, seed, offset, node_start, parent,
+                             draft_token, batch, total_nodes, max_nodes, k_cache, v_cache, elem_bytes, num_layers,
+                             layer_stride_bytes, kv_start, prefix_len, total_slots, num_kv_heads, head_dim,
+                             target_token, accept_len, accept_path, bonus_token, out_tokens, new_len, workspace,
+                             workspace_bytes, err_flag, stream) -> int:
+    return load().ev_select_accept_compact(logits, dtype, row_stride, vocab, temperature, seed, offset, node_start,
+                                           parent, draft_token, batch, total_nodes, max_nodes, k_cache, v_cache,
+                                           elem_bytes, num_layers, layer_stride_bytes, kv_start, prefix_len,
+                                           total_slots, num_kv_heads, head_dim, target_token, accept_len,
+                                           accept_path, bonus_token, out_tokens, new_len, workspace,
+                                           workspace_bytes, err_flag, stream)
+
+
+def ev_select_accept_compact_paged(logits, dtype, row_stride, vocab, temperature, seed, offset, node_start, parent,
+                                   draft_token, batch, total_nodes, max_nodes, k_pages, v_pages, elem_bytes,
+                                   num_layers, layer_stride_bytes, block_table, bt_stride, page_size, prefix_len,
+                                   num_pages, num_kv_heads, head_dim, target_token, accept_len, accept_path,
+                                   bonus_token, out_tokens, new_len, workspace, workspace_bytes, err_flag,
+                                   stream) -> int:
+    return load().ev_select_accept_compact_paged(logits, dtype, row_stride, vocab, temperature, seed, offset,
+                                                 node_start, parent, draft_token, batch, total_nodes, max_nodes,
+                                                 k_pages, v_pages, elem_bytes, num_layers, layer_stride_bytes,
+                                                 block_table, bt_stride, page_size, prefix_len, num_pages,
+                                                 num_kv_heads, head_dim, target_token, accept_len, accept_path,
+                                                 bonus_token, out_tokens, new_len, workspace, workspace_bytes,
+                                                 err_flag, stream)
 
 
 # ------------------------------------------------------------------------------ torch helpers
@@ -398,9 +442,79 @@ def compact_kv_paged(k_pages, v_pages, block_table, prefix_len, accept_len, acce
     return new_len
 
 
+def _accept_outputs(B, max_nodes, dev, out):
+    torch = _torch()
+    if out is None:
+        out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+               "accept_path": torch.empty((B, max_nodes), dtype=torch.int32, device=dev),
+               "bonus": torch.empty(B, dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((B, max_nodes), dtype=torch.int32, device=dev)}
+    return out
+
+
+def select_accept_compact(logits, node_start, parent, draft_token, k_cache, v_cache, kv_start, prefix_len, *,
+                          max_nodes: int, temperature: float = 0.0, seed: int = 0, offset: int = 0, vocab: int = None,
+                          target=None, out=None, new_len=None, workspace: Workspace = None, err_flag=None,
+                          stream=None, block_table=None):
+    """Per-node token (argmax at temperature 0, else the sampled draw), acceptance and in-place KV
+    compaction in one call (ev_select_accept_compact; with block_table, the paged form and caches
+    are pools [pages, page_size, Hkv, D] or [layers, pages, page_size, Hkv, D]).
+    Returns (target [R], accept dict as greedy_accept's, new_len [B], workspace)."""
+    torch = _torch()
+    _need(logits, "logits", ndim=2)
+    for name, t in (("node_start", node_start), ("parent", parent), ("draft_token", draft_token)):
+        _need(t, name, torch.int32, 1)
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache", k_cache.dtype)
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache / v_cache shapes disagree")
+    R, stride = logits.shape
+    vocab = stride if vocab is None else vocab
+    B = node_start.shape[0] - 1
+    T = parent.shape[0]
+    dev = parent.device
+    paged = block_table is not None
+    base = 4 if paged else 3
+    if k_cache.dim() == base:
+        layers, dims = 1, tuple(k_cache.shape)
+    elif k_cache.dim() == base + 1:
+        layers, dims = k_cache.shape[0], tuple(k_cache.shape[1:])
+    else:
+        raise ValueError("caches must be [slots, Hkv, D] / [pages, page_size, Hkv, D], optionally with a layer axis")
+    Hkv, D = dims[-2], dims[-1]
+    rows_per_layer = 1
+    for x in dims[:-2]:
+        rows_per_layer *= int(x)
+    if target is None:
+        target = torch.empty(R, dtype=torch.int32, device=dev)
+    out = _accept_outputs(B, max_nodes, dev, out)
+    if new_len is None:
+        new_len = torch.empty(B, dtype=torch.int32, device=dev)
+    need = ev_select_workspace_size(T, vocab)
+    if need and (workspace is None or workspace.nbytes < need):
+        workspace = Workspace(need, dev)
+    esz = k_cache.element_size()
+    common = (_addr(logits), _dtype_code(logits), stride, vocab, float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
+              int(offset) & 0xFFFFFFFFFFFFFFFF, _addr(node_start), _addr(parent), _addr(draft_token), B, T, max_nodes,
+              _addr(k_cache), _addr(v_cache), esz, layers, rows_per_layer * Hkv * D * esz)
+    tail = (Hkv, D, _addr(target), _addr(out["accept_len"]), _addr(out["accept_path"]), _addr(out["bonus"]),
+            _addr(out["out_tokens"]), _addr(new_len), workspace.ptr if workspace is not None else None,
+            workspace.nbytes if workspace is not None else 0, _addr(err_flag), _stream(stream))
+    if paged:
+        _need(block_table, "block_table", torch.int32, 2)
+        st = ev_select_accept_compact_paged(*common, _addr(block_table), block_table.shape[1], dims[1],
+                                            _addr(prefix_len), dims[0], *tail)
+        _check(st, "ev_select_accept_compact_paged")
+    else:
+        st = ev_select_accept_compact(*common, _addr(kv_start), _addr(prefix_len), dims[0], *tail)
+        _check(st, "ev_select_accept_compact")
+    return target, out, new_len, workspace
+
+
 def verify_step(q, k_cache, v_cache, logits, node_start, parent, kv_start, prefix_len, draft_token, *,
                 max_nodes: int, sm_scale: float, state: dict = None, stream=None):
-    """One whole verification step: attention, argmax, acceptance, compaction (four launches, one stream).
+    """One whole verification step: attention, then argmax, acceptance and compaction fused
+    (ev_tree_attention + ev_select_accept_compact: four launches on one stream).
     ``state`` carries reusable outputs and workspaces between calls."""
     torch = _torch()
     state = {} if state is None else state
@@ -410,12 +524,9 @@ def verify_step(q, k_cache, v_cache, logits, node_start, parent, kv_start, prefi
                                   sm_scale=sm_scale, out=state.get("out"), lse=state.get("lse"),
                                   workspace=state.get("attn_ws"), err_flag=state["err"], stream=stream)
     state.update(out=out, lse=lse, attn_ws=ws)
-    tgt, mx, aws = node_argmax(logits, target=state.get("target"), max_value=state.get("max_value"),
-                               workspace=state.get("argmax_ws"), stream=stream)
-    state.update(target=tgt, max_value=mx, argmax_ws=aws)
-    acc = greedy_accept(node_start, parent, draft_token, tgt, max_nodes=max_nodes, vocab=logits.shape[1],
-                        out=state.get("accept"), err_flag=state["err"], stream=stream)
-    state["accept"] = acc
-    state["new_len"] = compact_kv(k_cache, v_cache, kv_start, prefix_len, acc["accept_len"], acc["accept_path"],
-                                  new_len=state.get("new_len"), err_flag=state["err"], stream=stream)
+    tgt, acc, nl, sws = select_accept_compact(logits, node_start, parent, draft_token, k_cache, v_cache, kv_start,
+                                              prefix_len, max_nodes=max_nodes, target=state.get("target"),
+                                              out=state.get("accept"), new_len=state.get("new_len"),
+                                              workspace=state.get("select_ws"), err_flag=state["err"], stream=stream)
+    state.update(target=tgt, accept=acc, new_len=nl, select_ws=sws)
     return state

@@ -22,6 +22,9 @@
  * prefix, as in the drafter's layers), ev_tree_attention_paged and ev_compact_kv_paged (KV
  * held in a paged pool through a per-sequence block table), and ev_node_sample (the per-node
  * draw of sampled verification at temperature > 0, in place of the argmax).
+ * ev_select_accept_compact (and its _paged form) runs the last three steps -- the per-node
+ * token, acceptance and compaction -- as one call of two launches, with results identical to
+ * the separate calls.
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer owned by the caller; the library allocates
@@ -291,6 +294,65 @@ ev_status ev_compact_kv_paged(void *k_pages, void *v_pages, int32_t elem_bytes, 
                               const int32_t *accept_path, int32_t batch, int32_t max_nodes, int32_t num_pages,
                               int32_t num_kv_heads, int32_t head_dim, int32_t *new_len, int32_t *err_flag,
                               hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ev_select_accept_compact
+ *
+ * ev_node_argmax (temperature == 0) or ev_node_sample (temperature > 0), then ev_greedy_accept
+ * on those tokens, then ev_compact_kv of the accepted paths: the per-node target token, the
+ * accept rule and the KV move of one verification round (kongchang.com English article,
+ * "Technical Background"), in two launches instead of three and without the arrival counting
+ * that the standalone argmax needs.  The first launch streams the logits and leaves every row
+ * piece's winner in the workspace; the second, one workgroup per (sequence, layer), finishes
+ * its rows' tokens, applies the accept rule and moves the layer's accepted K/V rows.  Every
+ * output is bit-identical to the three separate calls on the same inputs:
+ *
+ *   target_token   [total_nodes]  as ev_node_argmax / ev_node_sample (no max_value output)
+ *   accept_len, accept_path, bonus_token, out_tokens   as ev_greedy_accept
+ *   K/V caches, new_len                                as ev_compact_kv
+ *
+ *   logits, dtype, row_stride, vocab   as ev_node_argmax, num_rows = total_nodes
+ *   temperature    0 for the argmax; otherwise finite and > 0 with log2(e)/temperature finite
+ *                  in fp32 (EV_ERR_SHAPE otherwise); seed, offset as ev_node_sample (unused at 0)
+ *   node_start, parent, draft_token, batch, total_nodes, max_nodes   as ev_greedy_accept
+ *   k_cache ... head_dim, new_len                                    as ev_compact_kv
+ *   workspace      >= ev_select_workspace_size(total_nodes, vocab) bytes, 8-byte aligned (NULL
+ *                  when that size is 0); fully rewritten by each call, needs no zeroing
+ * Every argument is checked before the first launch.  Data errors are reported as by the
+ * separate calls (a sequence whose tree or tokens are bad gets accept_len 0 and its KV is left
+ * alone with new_len = L).
+ * -------------------------------------------------------------------------------------------*/
+size_t ev_select_workspace_size(int32_t num_rows, int32_t vocab);
+
+ev_status ev_select_accept_compact(const void *logits, ev_dtype dtype, int64_t row_stride, int32_t vocab,
+                                   float temperature, uint64_t seed, uint64_t offset, const int32_t *node_start,
+                                   const int32_t *parent, const int32_t *draft_token, int32_t batch,
+                                   int32_t total_nodes, int32_t max_nodes, void *k_cache, void *v_cache,
+                                   int32_t elem_bytes, int32_t num_layers, int64_t layer_stride_bytes,
+                                   const int32_t *kv_start, const int32_t *prefix_len, int64_t total_slots,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t *target_token,
+                                   int32_t *accept_len, int32_t *accept_path, int32_t *bonus_token,
+                                   int32_t *out_tokens, int32_t *new_len, void *workspace, size_t workspace_bytes,
+                                   int32_t *err_flag, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ev_select_accept_compact_paged
+ *
+ * ev_select_accept_compact with the K/V in a paged pool: the compaction is ev_compact_kv_paged
+ * (k_pages, v_pages, block_table, bt_stride, page_size, num_pages as there).
+ * -------------------------------------------------------------------------------------------*/
+ev_status ev_select_accept_compact_paged(const void *logits, ev_dtype dtype, int64_t row_stride, int32_t vocab,
+                                         float temperature, uint64_t seed, uint64_t offset,
+                                         const int32_t *node_start, const int32_t *parent,
+                                         const int32_t *draft_token, int32_t batch, int32_t total_nodes,
+                                         int32_t max_nodes, void *k_pages, void *v_pages, int32_t elem_bytes,
+                                         int32_t num_layers, int64_t layer_stride_bytes, const int32_t *block_table,
+                                         int32_t bt_stride, int32_t page_size, const int32_t *prefix_len,
+                                         int32_t num_pages, int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t *target_token, int32_t *accept_len, int32_t *accept_path,
+                                         int32_t *bonus_token, int32_t *out_tokens, int32_t *new_len,
+                                         void *workspace, size_t workspace_bytes, int32_t *err_flag,
+                                         hipStream_t stream);
 
 #ifdef __cplusplus
 }
