@@ -7,29 +7,30 @@
 // verification).  The KV cache is bf16 and never quantised (arex-research.com release note,
 // plugin section: tree verification needs an unquantised KV cache).
 //
-// How (one launch, no second merge kernel):
+// How (two launches on one stream: the attention kernel, then the merge of split units):
 //   * Work unit = (sequence, row group, KV head).  A unit's rows are all (node, q-head-in-group)
 //     pairs of that KV head -- up to 80 rows -- so every K/V byte is read from HBM exactly once
 //     and shared by all N*G rows (the arithmetic intensity is N*G flop per byte).
-//   * Stream-K split: each unit's keys are cut into stages (64 keys for 80-row units, 32 keys
-//     otherwise); all stages of all units are laid end to end and the grid's workgroups take
-//     equal contiguous ranges (ragged prefix lengths cost nothing in balance).  Ranges are
-//     mapped XCD-major so the pieces of one unit mostly land on one XCD.
-//   * bf16 inputs stream HBM -> LDS with direct 16-byte loads (global_load_lds_dwordx4), three
+//   * Each unit's keys are cut into stages (64 keys for 80-row units, 32 keys otherwise) and a
+//     workgroup takes a range of stages.  When the units fit the grid the split is unit-aligned
+//     (each workgroup one near-equal piece of one unit); otherwise all stages are laid end to end
+//     and the workgroups take equal contiguous ranges (stream-K), mapped XCD-major so the pieces
+//     of one unit mostly land on one XCD.
+//   * bf16 inputs stream HBM -> LDS with direct 16-byte loads (global_load_lds_dwordx4), several
 //     stages in flight, no register staging.  K and V rows keep their natural layout with the
 //     16-byte chunks XOR-swizzled per row: K operand reads are ds_read_b128 and the V^T operand
 //     comes from ds_read_b64_tr_b16 transpose reads, both bank-conflict free.  fp32 inputs go
 //     through registers (converted to bf16) into a padded K tile and a transposed V tile.
-//   * Four waves per workgroup.  Wave w owns 16-row tile w; an 80-row unit's fifth tile is split
-//     by keys, each wave taking a 16-key quarter of every stage with the K and V^T operands it
-//     has already read (16x16x16 MFMA for that quarter's PV), and the four quarter states are
-//     merged through LDS at the end of each piece.  S^T = K Q^T and O^T = V^T P^T run on
-//     v_mfma_f32_16x16x32_bf16; the online softmax is fp32 base-2 with the scale folded into the
-//     exponent's FMA; the ancestor mask is applied only on stages that reach the tree slots.  The
-//     score layout already matches P^T's operand layout, so P needs no shuffle.
-//   * A unit covered by one workgroup is written directly; otherwise each piece publishes (m, l,
-//     O) partials with device-coherent stores and pieces merge hierarchically (groups of 8,
-//     last arriver merges in fixed order: deterministic, no L2 flushes).
+//   * Four waves per workgroup.  In the row-tile kernels wave w owns 16-row tile w; 80-row bf16
+//     units run the key-split kernel below, where every wave covers all 80 rows for its own
+//     16-key quarter of each stage.  S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 and O^T =
+//     V^T P^T on the 16x16x32 or 16x16x16 form; the online softmax is fp32 base-2 with the scale
+//     folded into the exponent's FMA; the ancestor mask is applied only on stages that reach the
+//     tree slots.  The score layout already matches P^T's operand layout, so P needs no shuffle.
+//   * A unit covered by one workgroup is written directly; otherwise each piece publishes its
+//     (m, l, O) partial and the unit's first piece records the unit in a table, and the merge
+//     launch (whose launch boundary makes the partials visible) combines each unit's pieces in
+//     piece order: deterministic, no atomics, no L2 flushes.
 #include <cmath>
 #include <mutex>
 #include <type_traits>
