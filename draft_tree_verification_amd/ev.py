@@ -512,8 +512,10 @@ def select_accept_compact(logits, node_start, parent, draft_token, k_cache, v_ca
 
 
 def verify_step(q, k_cache, v_cache, logits, node_start, parent, kv_start, prefix_len, draft_token, *,
-                max_nodes: int, sm_scale: float, state: dict = None, stream=None):
-    """One whole verification step: attention, then argmax, acceptance and compaction fused
+                max_nodes: int, sm_scale: float, temperature: float = 0.0, seed: int = 0, offset: int = 0,
+                state: dict = None, stream=None):
+    """One whole verification step: attention, then the per-node token (argmax at temperature 0,
+    else the sampled draw keyed by (seed, offset)), acceptance and compaction fused
     (ev_tree_attention + ev_select_accept_compact: four launches on one stream).
     ``state`` carries reusable outputs and workspaces between calls."""
     torch = _torch()
@@ -525,7 +527,8 @@ def verify_step(q, k_cache, v_cache, logits, node_start, parent, kv_start, prefi
                                   workspace=state.get("attn_ws"), err_flag=state["err"], stream=stream)
     state.update(out=out, lse=lse, attn_ws=ws)
     tgt, acc, nl, sws = select_accept_compact(logits, node_start, parent, draft_token, k_cache, v_cache, kv_start,
-                                              prefix_len, max_nodes=max_nodes, target=state.get("target"),
+                                              prefix_len, max_nodes=max_nodes, temperature=temperature, seed=seed,
+                                              offset=offset, target=state.get("target"),
                                               out=state.get("accept"), new_len=state.get("new_len"),
                                               workspace=state.get("select_ws"), err_flag=state["err"], stream=stream)
     state.update(target=tgt, accept=acc, new_len=nl, select_ws=sws)

@@ -1,5 +1,5 @@
 """The whole verification step (four launches on one stream) against the oracle on every workload,
-in the launch configuration the benchmark times."""
+in the launch configuration the benchmark times; and the sampled step (temperature > 0)."""
 import numpy as np
 import pytest
 
@@ -71,3 +71,38 @@ def test_verify_step(name):
                                             head_dim=w.head_dim)
         got = _tree_rows(w, gu.to_host(cur))
         assert (err == 0).all() and np.array_equal(got, exp[0]), "compacted tree rows differ"
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("T", [1.0, 0.6])
+def test_verify_step_sampled(T):
+    """Sampled step on the 8-sequence workload: the draws match the oracle's (up to near ties of
+    the hardware log2), and acceptance and compaction are bit-exact against the oracle on the
+    GPU's own draws."""
+    import torch
+    from draft_tree_verification_amd import ev
+    gu.log(f"[case] verify step c8 sampled T={T}")
+    w = gu.cached_config("c8")
+    d = gu.dev_workload(w)
+    st = ev.verify_step(d["q"], d["k"], d["v"], d["logits"], d["node_start"], d["parent"], d["kv_start"],
+                        d["prefix_len"], d["draft"], max_nodes=w.max_nodes, sm_scale=w.sm_scale, temperature=T,
+                        seed=31, offset=4)
+    torch.cuda.synchronize()
+    assert int(st["err"].item()) == 0
+    draws = st["target"].cpu().numpy()
+    ref, ref_score = oracle.node_sample(w.logits, T, 31, 4)
+    bad = np.nonzero(draws != ref)[0]
+    z = gu.widen(w.logits)
+    for r in bad:
+        s_g = oracle.sample_score(float(z[r, draws[r]]), T, 31, 4, int(r), int(draws[r]))
+        assert s_g >= float(ref_score[r]) - 1e-5 - 8 * np.spacing(np.float32(max(1.0, abs(float(ref_score[r]))))), r
+    assert len(bad) <= 1
+    r = oracle.greedy_accept(w.node_start, w.parent, w.draft, draws, w.max_nodes, w.vocab)
+    for key in ("accept_len", "accept_path", "bonus", "out_tokens"):
+        assert np.array_equal(st["accept"][key].cpu().numpy(), r[key]), key
+    kx, vx, nl, err = oracle.compact_kv(w.k[None], w.v[None], w.kv_start, w.prefix_len, r["accept_len"],
+                                        r["accept_path"], num_layers=1, total_slots=w.total_slots,
+                                        num_kv_heads=w.num_kv_heads, head_dim=w.head_dim)
+    assert (err == 0).all() and np.array_equal(st["new_len"].cpu().numpy(), nl)
+    assert np.array_equal(gu.to_host(d["k"]), kx[0]) and np.array_equal(gu.to_host(d["v"]), vx[0])
+    gu.log(f"[step] sampled T={T}: mean accept_len {r['accept_len'].mean():.3f}")
