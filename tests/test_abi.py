@@ -84,6 +84,40 @@ def test_host_argument_checks_need_no_gpu(lib):
     assert ev.ev_compact_kv(P, P, 2, 1, 1 << 20, P, P, P, P, 1, 4, 16, 8, 128, P, None, None) == 2  # alias
 
 
+def test_fused_call_host_checks_need_no_gpu(lib):
+    """ev_select_accept_compact refuses bad arguments before any HIP call."""
+    P = 0x1000
+    assert ev.ev_select_workspace_size(128, 151936) == 128 * 10 * 8      # 10 pieces of 16,384 per row
+    assert ev.ev_select_workspace_size(4096, 151936) == 4096 * 8         # one piece per row
+    assert ev.ev_select_workspace_size(0, 151936) == 0
+
+    def call(logits=P, dtype=0, stride=1024, vocab=1000, T=0.0, max_nodes=8, elem=2, layer_stride=1 << 20,
+             new_len=P + 64, ws=P, ws_bytes=1 << 20):
+        return ev.ev_select_accept_compact(logits, dtype, stride, vocab, T, 0, 0, P, P, P, 2, 8, max_nodes, P, P,
+                                           elem, 1, layer_stride, P, P, 64, 2, 64, P, P, P, P, P, new_len, ws,
+                                           ws_bytes, None, None)
+    assert call(logits=None) == 1
+    assert call(stride=999) == 2                  # stride < vocab
+    assert call(max_nodes=65) == 2
+    for T in (-1.0, float("nan"), float("inf"), 1e-45):
+        assert call(T=T) == 2, T
+    assert call(dtype=2) == 3
+    assert call(logits=P + 2) == 4
+    assert call(stride=1028) == 4                 # 2056-byte rows
+    assert call(ws_bytes=8) == 5
+    assert call(ws=None, ws_bytes=0) == 5
+    assert call(ws=P + 4) == 4
+    assert call(elem=3) == 3                      # compaction element size
+    assert call(layer_stride=100) == 2            # layer stride below one layer
+    assert call(new_len=P) == 2                   # new_len aliases prefix_len
+    assert ev.ev_select_accept_compact_paged(P, 0, 1024, 1000, 0.0, 0, 0, P, P, P, 2, 8, 8, P, P, 2, 1, 1 << 20,
+                                             None, 4, 16, P, 8, 2, 64, P, P, P, P, P, P + 64, P, 1 << 20, None,
+                                             None) == 1      # no block table
+    assert ev.ev_select_accept_compact_paged(P, 0, 1024, 1000, 0.0, 0, 0, P, P, P, 2, 8, 8, P, P, 2, 1, 1 << 20,
+                                             P, 4, 0, P, 8, 2, 64, P, P, P, P, P, P + 64, P, 1 << 20, None,
+                                             None) == 2      # page size 0
+
+
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         ev.load(str(tmp_path / "libev.so"))

@@ -102,6 +102,19 @@ def test_many_sequences():
     _run_full(w, what="many")
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(2, 1, 64), (10, 2, 128)])
+def test_max_batch(hq, hkv, d):
+    """The largest batch (EV_MAX_BATCH = 2048 sequences; the schedule scan runs in eight chunks of
+    256 with a carry): ragged short prefixes, empty ones included, 1-5 node trees."""
+    from draft_tree_verification_amd import ev
+    gu.log(f"[case] attention max batch hq={hq} hkv={hkv} d={d}")
+    rng = np.random.default_rng(2048 + hq)
+    B = ev.MAX_BATCH
+    w = synth.make_workload("maxb", 99 + hq, prefix_lens=rng.integers(0, 40, B), nodes=rng.integers(1, 6, B),
+                            num_q_heads=hq, num_kv_heads=hkv, head_dim=d, vocab=64, sm_scale=0.4)
+    _run_full(w, what=f"max batch {hq}/{hkv}/{d}")
+
+
 def test_chain_equals_causal_decode():
     """A chain tree is causal attention; node 0 alone is decode attention (against the oracle)."""
     gu.log("[case] attention chain")
