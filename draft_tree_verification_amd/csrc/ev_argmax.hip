@@ -5,7 +5,7 @@
 // each child's draft token with it.  The result must be bit-exact, so the total order is fixed:
 // larger value first, lower index on ties, +0 == -0, any NaN above every number.
 //
-// HBM-bound streaming: each thread reads 16 bytes per load, four loads in flight.  Values are
+// HBM-bound streaming: each thread reads 16 bytes per load, eight loads in flight.  Values are
 // mapped to order-preserving unsigned keys (sign-magnitude -> offset binary, both zeros to the
 // same key); for bf16 the key transform and the per-load maximum run on packed 16-bit integer
 // ops, and the index of a new maximum is searched only when a load beats the running best (rare
@@ -78,16 +78,27 @@ __device__ __forceinline__ unsigned long long pack(uint32_t key, int32_t idx) {
     return (static_cast<unsigned long long>(key) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(idx));
 }
 
+// Wave-wide unsigned maximum: DPP row shifts (an inclusive scan within each 16-lane row; lanes
+// shifted in from outside the row read 0, the identity) and the four rows' last lanes.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+    x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x111, 0xf, 0xf, false)));
+    x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x112, 0xf, 0xf, false)));
+    x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x114, 0xf, 0xf, false)));
+    x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x118, 0xf, 0xf, false)));
+    const uint32_t r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+    const uint32_t r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
+    return max(max(r0, r1), max(r2, r3));
+}
+
 // The workgroup's best (key, lowest index) for `row`, then across the row's split workgroups;
 // the row's token (and the maximum, if asked for) is written once.  Workgroup-uniform call.
 __device__ __forceinline__ void finish_row(const ArgmaxArgs &a, int row, uint32_t best, int32_t bidx, bool f32) {
     const int tid = threadIdx.x;
-    // workgroup reduction of (key, -index)
-    unsigned long long p = best ? pack(best, bidx) : 0ull;
-    for (int o = 32; o > 0; o >>= 1) {
-        const unsigned long long q = __shfl_xor(p, o, 64);
-        p = q > p ? q : p;
-    }
+    // wave reduction of (key, lowest index): the largest key, then the lowest index among the
+    // lanes that hold it (register-only DPP steps, no LDS permutes)
+    const uint32_t kmax = wave_umax(best);
+    const uint32_t imin = ~wave_umax(~(best == kmax ? static_cast<uint32_t>(bidx) : 0xFFFFFFFFu));
+    unsigned long long p = kmax ? pack(kmax, static_cast<int32_t>(imin)) : 0ull;
     __shared__ unsigned long long s_red[kThreads / 64];
     if ((tid & 63) == 0) s_red[tid >> 6] = p;
     __syncthreads();
