@@ -1,13 +1,15 @@
 """Benchmark of the draft-tree verification step on one MI355X.
 
-One step = the whole hot path over one batch: tree-masked GQA attention, per-node argmax, greedy
-acceptance and in-place KV compaction (four launches on one stream).  Inputs are seeded synthetic
+One step = the whole hot path over one batch: tree-masked GQA attention (ev_tree_attention: the
+attention kernel and the split merge), then the per-node argmax, greedy acceptance and in-place KV
+compaction (ev_select_accept_compact: the selection pass and one acceptance-and-compaction
+launch); four launches on one stream.  --separate calls the four separate entry points instead.  Inputs are seeded synthetic
 data already resident in HBM; several identical input sets sit at different addresses and the
 steps rotate over them, so the 256 MB Infinity Cache cannot serve one step's reads from the
 previous step's.  Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload c8|c128k|c512|c1x4k|tiny] [--no-cpu]
-                  [--kv contiguous|paged|window] [--page-size P] [--window W] [--sample T]
+                  [--kv contiguous|paged|window] [--page-size P] [--window W] [--sample T] [--separate]
   python bench.py --copy-calibration     (a plain device copy of known size, for counter scaling)
 
 The default workload is the 8-sequence batch (prefix lengths uniform in [1024, 8192], 16-node

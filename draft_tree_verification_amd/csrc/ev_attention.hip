@@ -79,7 +79,7 @@ struct Layout {
     static constexpr int KST = X5 ? 64 : 32;        // keys per stage
     static constexpr int R = RT * 16;
     static constexpr int kScan = EV_MAX_BATCH * 4;  // int32 inclusive scan of per-sequence stages
-    static constexpr int kMisc = 32;                // wave sums and the last-arriver flag
+    static constexpr int kMisc = 32;                // wave sums of the schedule scan
     // fp32 inputs: two register-staged buffers (K row-major padded, V transposed)
     static constexpr int KP = 2 * D + 16;
     static constexpr int VTP = 2 * KST + 8;
