@@ -163,6 +163,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kv_kernel(const Compa
     __shared__ int s_path[FUSED ? EV_MAX_NODES : 1];
     __shared__ int s_len;
     const int L = a.prefix_len[b];
+    const int s0 = a.block_table ? 0 : a.kv_start[b];  // loaded up front, used after the path is known
     int len, err = 0, p = 0, last = 0;
     if constexpr (FUSED) {
         if (tid < 64) {
@@ -174,9 +175,17 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kv_kernel(const Compa
                 const int row = ns0 + tid;
                 par = x.parent[row];
                 dft = x.draft[row];
+                // the row's pieces in groups of eight independent loads (indices clamped to the
+                // last piece: a repeat does not change a maximum)
                 const unsigned long long *pc = sel.pieces + static_cast<size_t>(row) * sel.splits;
                 unsigned long long w = 0;
-                for (int k = 0; k < sel.splits; ++k) w = pc[k] > w ? pc[k] : w;
+                for (int k0 = 0; k0 < sel.splits; k0 += 8) {
+                    unsigned long long x[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) x[k] = pc[min(k0 + k, sel.splits - 1)];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) w = x[k] > w ? x[k] : w;
+                }
                 tgt = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(w & 0xFFFFFFFFu));
                 if (layer == 0) sel.target_out[row] = tgt;
             }
@@ -204,7 +213,6 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kv_kernel(const Compa
     }
     if (len > 0 && !err) {
         if (!a.block_table) {
-            const int s0 = a.kv_start[b];
             if (s0 < 0 || L < 0 || static_cast<int64_t>(s0) + L + last >= a.total_slots) err = EV_DATA_BAD_SLOTS;
             else if (tid < len) {
                 s_src[tid] = static_cast<int64_t>(s0) + L + p;
