@@ -1518,7 +1518,8 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel_ks(const At
 
 // ---------------------------------------------------------------------------------------------
 // Merge of split units (second launch; the launch boundary makes the published partials visible).
-// A resident grid: every block compacts the table's split units in LDS, then the blocks stride
+// A resident grid: every block compacts the table's split units (their entries, in LDS, so no
+// item re-reads the table), then the blocks stride
 // over the work items (unit, row tile, half of the d columns).  An item combines the unit's
 // pieces: M = max_i m_i, O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i, in piece order
 // (deterministic), 16 rows x D/8 threads with one float4 of O each.
@@ -1585,20 +1586,25 @@ template <int D, bool F32OUT>
 __global__ __launch_bounds__(2 * D, 2) void tree_attention_merge_kernel(const AttnArgs a, int R, int RT, int entries) {
     constexpr int NT = 2 * D;
     __shared__ int s_idx[kMaxGrid];
+    __shared__ int4 s_ent[kMaxGrid];
     __shared__ int s_cnt[NT / 64 + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // compact the table's split units (same order in every block)
     int base = 0;
     for (int e0 = 0; e0 < entries; e0 += NT) {
         const int e = e0 + tid;
-        const bool act = e < entries && a.table[e].x > 0;
+        const int4 v = e < entries ? a.table[e] : int4{0, 0, 0, 0};
+        const bool act = v.x > 0;
         const uint64_t bal = __ballot(act);
         const int before = __popcll(bal & ((1ull << lane) - 1));
         if (lane == 0) s_cnt[wave] = __popcll(bal);
         __syncthreads();
         int off = base;
         for (int w = 0; w < wave; ++w) off += s_cnt[w];
-        if (act) s_idx[off + before] = e;
+        if (act) {
+            s_idx[off + before] = e;
+            s_ent[off + before] = v;
+        }
         int tot = 0;
         for (int w = 0; w < NT / 64; ++w) tot += s_cnt[w];
         base += tot;
@@ -1608,7 +1614,7 @@ __global__ __launch_bounds__(2 * D, 2) void tree_attention_merge_kernel(const At
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
         const int u = it / (RT * 2), t = (it / 2) % RT, half = it % 2;
         const int w1 = s_idx[u];
-        const int4 e = a.table[w1];
+        const int4 e = s_ent[u];
         if (e.x <= 2) merge_item<D, 2, F32OUT>(a, R, w1, e, t, half);
         else if (e.x <= 4) merge_item<D, 4, F32OUT>(a, R, w1, e, t, half);
         else if (e.x <= 8) merge_item<D, 8, F32OUT>(a, R, w1, e, t, half);
