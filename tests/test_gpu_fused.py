@@ -279,3 +279,39 @@ def test_argument_errors():
                                      i32(3).data_ptr(), i32(12).data_ptr(), i32(3).data_ptr(), i32(12).data_ptr(),
                                      i32(3).data_ptr(), None, 0, None, torch.cuda.current_stream().cuda_stream)
     assert st == 0
+
+
+def test_randomized_against_separate_calls():
+    """Forty random configurations (batch 1-70, trees of 1-64 nodes, vocabularies 1-70,000 with
+    padded strides, bf16/fp32 logits, temperature 0 or 0.2-3, 1-2 layers, bf16/fp32 caches):
+    the fused call equals the three separate calls bit for bit every time."""
+    import torch
+    gu.log("[case] fused randomized")
+    rng = np.random.default_rng(2024)
+    for it in range(40):
+        B = int(rng.integers(1, 71))
+        max_n = int(rng.choice([1, 4, 16, 64]))
+        vocab = int(rng.choice([1, 7, 300, 4096, 70000]))
+        stride = vocab + int(rng.integers(0, 3)) * 8
+        ldt = BF16 if rng.random() < 0.7 else F32
+        if ldt == BF16 and stride % 8:
+            stride += 8 - stride % 8
+        if ldt == F32 and stride % 4:
+            stride += 4 - stride % 4
+        T = 0.0 if rng.random() < 0.5 else float(rng.uniform(0.2, 3.0))
+        layers = int(rng.integers(1, 3))
+        cdt = np.uint16 if rng.random() < 0.7 else np.float32
+        c = _case(int(rng.integers(1 << 30)), B, max_n, vocab, stride, ldt, layers, 2, 64, cdt, max_prefix=30)
+        if T > 0:
+            tref, _ = oracle.node_sample(c["logits"], T, 5, it, vocab=vocab, row_stride=stride)
+        else:
+            tref, _ = oracle.node_argmax(c["logits"], vocab=vocab, row_stride=stride)
+        draft = _planted(c["rng"], c["trees"], tref, vocab, float(rng.uniform(0.3, 1.0)))
+        d = _dev(c, draft)
+        k1, v1 = gu.to_dev(c["k"]), gu.to_dev(c["v"])
+        k2, v2 = k1.clone(), v1.clone()
+        what = f"random #{it}: B={B} max_n={max_n} vocab={vocab}/{stride} T={T:.2f} layers={layers}"
+        _compare(_separate(d, k1, v1, c, T, 5, it), _fused(d, k2, v2, c, T, 5, it), what)
+        assert gu.to_host(k1).tobytes() == gu.to_host(k2).tobytes(), what
+        assert gu.to_host(v1).tobytes() == gu.to_host(v2).tobytes(), what
+    gu.log("[fused] 40 random configurations bit-exact")
