@@ -310,6 +310,22 @@ def main():
     torch.cuda.synchronize()
     kernel_ms = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K for j, n in enumerate(names)}
 
+    # streaming-read ceiling of this GPU: ev_stream_read over 2 GiB (8x the Infinity Cache)
+    rbuf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        rc |= lib.ev_stream_read(p(rbuf), rbuf.numel(), p(sink), stream)
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for _ in range(10):
+        rc |= lib.ev_stream_read(p(rbuf), rbuf.numel(), p(sink), stream)
+    r1.record()
+    torch.cuda.synchronize()
+    if rc:
+        raise RuntimeError("the streaming-read measurement failed")
+    read_ceiling = 10 * rbuf.numel() / (r0.elapsed_time(r1) * 1e-3) / 1e9
+    del rbuf
+
     acc_sum = int(acc_len.sum().item())
     if args.kv == "window":  # only the last `window` prefix tokens (and the tree) are read
         vis = sum(min(int(w.prefix_len[b]), args.window) + int(w.nodes_per_seq[b]) for b in range(B))
@@ -343,6 +359,8 @@ def main():
         "accept_len_mean": acc_sum / B,
         "kv_read_gbps": round(kv_gbps, 1),
         "kv_read_pct_of_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
+        "read_ceiling_gbps": round(read_ceiling, 1),
+        "kv_read_pct_of_ceiling": round(100 * kv_gbps / read_ceiling, 2),
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
         "selection": "separate calls" if args.separate else "fused (ev_select_accept_compact)",
         "wall_s_timed": round(t_wall, 4),

@@ -27,7 +27,8 @@ MAX_BATCH = 2048
 EXPORTS = ("ev_status_string", "ev_tree_attention_workspace_size", "ev_tree_attention",
            "ev_tree_attention_window", "ev_tree_attention_paged", "ev_node_argmax_workspace_size",
            "ev_node_argmax", "ev_node_sample", "ev_greedy_accept", "ev_compact_kv", "ev_compact_kv_paged",
-           "ev_select_workspace_size", "ev_select_accept_compact", "ev_select_accept_compact_paged")
+           "ev_select_workspace_size", "ev_select_accept_compact", "ev_select_accept_compact_paged",
+           "ev_stream_read")
 
 _lib = None
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -87,6 +88,8 @@ def load(path: str = LIB_PATH):
     lib.ev_select_accept_compact_paged.argtypes = [_P, ctypes.c_int, _I64, _I32, _F, _U64, _U64, _P, _P, _P, _I32,
                                                    _I32, _I32, _P, _P, _I32, _I32, _I64, _P, _I32, _I32, _P, _I32,
                                                    _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
+    lib.ev_stream_read.restype = ctypes.c_int
+    lib.ev_stream_read.argtypes = [_P, _SZ, _P, _P]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -195,6 +198,10 @@ def ev_select_accept_compact_paged(logits, dtype, row_stride, vocab, temperature
                                                  num_kv_heads, head_dim, target_token, accept_len, accept_path,
                                                  bonus_token, out_tokens, new_len, workspace, workspace_bytes,
                                                  err_flag, stream)
+
+
+def ev_stream_read(src, nbytes, sink, stream) -> int:
+    return load().ev_stream_read(src, nbytes, sink, stream)
 
 
 # ------------------------------------------------------------------------------ torch helpers

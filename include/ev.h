@@ -354,6 +354,21 @@ ev_status ev_select_accept_compact_paged(const void *logits, ev_dtype dtype, int
                                          void *workspace, size_t workspace_bytes, int32_t *err_flag,
                                          hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * ev_stream_read
+ *
+ * Measurement helper, not part of the verification step: reads every byte of a device buffer
+ * once, with non-temporal 16-byte loads over the whole GPU, and discards the data.  Its rate on a
+ * buffer far larger than the 256 MB Infinity Cache is the streaming-read ceiling that the
+ * attention's K/V read rate is reported against, besides the 8 TB/s HBM peak.
+ *
+ *   src     device buffer, 16-byte aligned (EV_ERR_ALIGN), read only
+ *   bytes   > 0 and a multiple of 16 (EV_ERR_SHAPE)
+ *   sink    device uint32; written only in the (practically impossible) case that the XOR of all
+ *           data equals 0x9E3779B9, which keeps the loads from being removed
+ * -------------------------------------------------------------------------------------------*/
+ev_status ev_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

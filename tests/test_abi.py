@@ -118,6 +118,14 @@ def test_fused_call_host_checks_need_no_gpu(lib):
                                              None) == 2      # page size 0
 
 
+def test_stream_read_host_checks_need_no_gpu(lib):
+    P = 0x1000
+    assert ev.ev_stream_read(None, 16, P, None) == 1
+    assert ev.ev_stream_read(P, 0, P, None) == 2
+    assert ev.ev_stream_read(P, 24, P, None) == 2
+    assert ev.ev_stream_read(P + 8, 16, P, None) == 4
+
+
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         ev.load(str(tmp_path / "libev.so"))

@@ -188,3 +188,16 @@ def test_compact_data_errors():
     bad = np.array([[1, 2, -1], [0, 2, 1], [0, 1, 2], [0, 1, 2]], np.int32)
     k2, _, nl, err = _gpu_compact(k, k.copy(), [0, 0, 6, 0], [2, 2, 2, 1], [2, 3, 3, 0], bad)
     assert err == 16 | 8 and list(nl) == [2, 2, 2, 1] and np.array_equal(k2, k)
+
+
+def test_stream_read_runs():
+    """The streaming-read helper reads a buffer and leaves the sink alone (its XOR is not the
+    trigger constant for this data)."""
+    import torch
+    from draft_tree_verification_amd import ev
+    gu.log("[case] stream read")
+    x = torch.arange(1 << 22, dtype=torch.int32, device="cuda")   # XOR of 0..2^22-1 is 0
+    sink = torch.full((1,), -5, dtype=torch.int32, device="cuda")
+    st = ev.ev_stream_read(x.data_ptr(), x.numel() * 4, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0 and int(sink.item()) == -5
