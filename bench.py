@@ -325,6 +325,22 @@ def main():
         raise RuntimeError("the streaming-read measurement failed")
     read_ceiling = 10 * rbuf.numel() / (r0.elapsed_time(r1) * 1e-3) / 1e9
     del rbuf
+    # the same read over buffers the size of this workload's K/V (ramp-up and drain included),
+    # rotated past the Infinity Cache: the time no kernel reading these bytes once can beat
+    nsz = (kv_bytes + 15) // 16 * 16
+    nbuf = max(2, math.ceil(2 * MALL_BYTES / nsz))
+    sbufs = [torch.empty(nsz, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    for i in range(nbuf):
+        rc |= lib.ev_stream_read(p(sbufs[i]), nsz, p(sink), stream)
+    r0.record()
+    for i in range(20):
+        rc |= lib.ev_stream_read(p(sbufs[i % nbuf]), nsz, p(sink), stream)
+    r1.record()
+    torch.cuda.synchronize()
+    if rc:
+        raise RuntimeError("the same-size read measurement failed")
+    same_size_read_ms = r0.elapsed_time(r1) / 20
+    del sbufs
 
     acc_sum = int(acc_len.sum().item())
     if args.kv == "window":  # only the last `window` prefix tokens (and the tree) are read
@@ -361,6 +377,7 @@ def main():
         "kv_read_pct_of_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
         "read_ceiling_gbps": round(read_ceiling, 1),
         "kv_read_pct_of_ceiling": round(100 * kv_gbps / read_ceiling, 2),
+        "kv_sized_read_ms": round(same_size_read_ms, 5),
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
         "selection": "separate calls" if args.separate else "fused (ev_select_accept_compact)",
         "wall_s_timed": round(t_wall, 4),
