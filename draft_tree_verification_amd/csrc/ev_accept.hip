@@ -175,16 +175,17 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kv_kernel(const Compa
                 const int row = ns0 + tid;
                 par = x.parent[row];
                 dft = x.draft[row];
-                // the row's pieces in groups of eight independent loads (indices clamped to the
-                // last piece: a repeat does not change a maximum)
+                // the row's pieces in groups of sixteen independent loads, one round trip for
+                // vocabularies up to 16 pieces (indices clamped to the last piece: a repeat does
+                // not change a maximum)
                 const unsigned long long *pc = sel.pieces + static_cast<size_t>(row) * sel.splits;
                 unsigned long long w = 0;
-                for (int k0 = 0; k0 < sel.splits; k0 += 8) {
-                    unsigned long long x[8];
+                for (int k0 = 0; k0 < sel.splits; k0 += 16) {
+                    unsigned long long x[16];
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) x[k] = pc[min(k0 + k, sel.splits - 1)];
+                    for (int k = 0; k < 16; ++k) x[k] = pc[min(k0 + k, sel.splits - 1)];
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) w = x[k] > w ? x[k] : w;
+                    for (int k = 0; k < 16; ++k) w = x[k] > w ? x[k] : w;
                 }
                 tgt = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(w & 0xFFFFFFFFu));
                 if (layer == 0) sel.target_out[row] = tgt;
