@@ -144,7 +144,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the verification step "
-              "shards by sequence or KV head with no exchange; see the design notes)", file=sys.stderr)
+              "would shard by sequence or by KV head, with no exchange; only the one-GPU path is built)",
+              file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
