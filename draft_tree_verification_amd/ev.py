@@ -237,12 +237,42 @@ def _need(t, name, dtype=None, ndim=None):
     torch = _torch()
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a device tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}; the library launches on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _need_out(t, name, dtype, shape):
+    """A caller-supplied output: contiguous, on the current device, of exactly this dtype and shape
+    (the kernels write every element of that shape)."""
+    _need(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _need_flag(err_flag):
+    """The optional device error flag: int32 with at least one element (the first is used)."""
+    if err_flag is not None:
+        _need(err_flag, "err_flag", _torch().int32)
+        if err_flag.numel() < 1:
+            raise ValueError("err_flag must hold at least one int32")
+
+
+def _need_accept(out, B, max_nodes):
+    torch = _torch()
+    if not isinstance(out, dict):
+        raise TypeError("out must be a dict with accept_len, accept_path, bonus and out_tokens")
+    for key, shape in (("accept_len", (B,)), ("accept_path", (B, max_nodes)), ("bonus", (B,)),
+                       ("out_tokens", (B, max_nodes))):
+        if key not in out:
+            raise ValueError(f"out lacks {key}")
+        _need_out(out[key], key, torch.int32, shape)
 
 
 class Workspace:
@@ -280,8 +310,13 @@ def tree_attention(q, k_cache, v_cache, node_start, parent, kv_start, prefix_len
         raise ValueError("metadata lengths disagree with batch / total nodes")
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _need_out(out, "out", q.dtype, q.shape)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    else:
+        _need_out(lse, "lse", torch.float32, (T, Hq))
+    _need_flag(err_flag)
     need = ev_tree_attention_workspace_size(B, max_nodes, Hq, Hkv, D)
     if workspace is None or workspace.nbytes < need:
         workspace = Workspace(need, q.device)
@@ -316,8 +351,13 @@ def tree_attention_paged(q, k_pages, v_pages, node_start, parent, block_table, p
         raise ValueError("metadata lengths disagree with batch / total nodes")
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _need_out(out, "out", q.dtype, q.shape)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    else:
+        _need_out(lse, "lse", torch.float32, (T, Hq))
+    _need_flag(err_flag)
     need = ev_tree_attention_workspace_size(B, max_nodes, Hq, Hkv, D)
     if workspace is None or workspace.nbytes < need:
         workspace = Workspace(need, q.device)
@@ -338,8 +378,12 @@ def node_argmax(logits, *, vocab: int = None, target=None, max_value=None, works
     vocab = stride if vocab is None else vocab
     if target is None:
         target = torch.empty(R, dtype=torch.int32, device=logits.device)
+    else:
+        _need_out(target, "target", torch.int32, (R,))
     if max_value is None:
         max_value = torch.empty(R, dtype=torch.float32, device=logits.device)
+    else:
+        _need_out(max_value, "max_value", torch.float32, (R,))
     need = ev_node_argmax_workspace_size(R, vocab)
     if need and (workspace is None or workspace.nbytes < need):
         workspace = Workspace(need, logits.device)
@@ -360,6 +404,8 @@ def node_sample(logits, *, temperature: float, seed: int, offset: int, vocab: in
     vocab = stride if vocab is None else vocab
     if target is None:
         target = torch.empty(R, dtype=torch.int32, device=logits.device)
+    else:
+        _need_out(target, "target", torch.int32, (R,))
     need = ev_node_argmax_workspace_size(R, vocab)
     if need and (workspace is None or workspace.nbytes < need):
         workspace = Workspace(need, logits.device)
@@ -381,12 +427,10 @@ def greedy_accept(node_start, parent, draft_token, target_token, *, max_nodes: i
         _need(t, name, torch.int32, 1)
     B = node_start.shape[0] - 1
     T = parent.shape[0]
-    dev = parent.device
-    if out is None:
-        out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
-               "accept_path": torch.empty((B, max_nodes), dtype=torch.int32, device=dev),
-               "bonus": torch.empty(B, dtype=torch.int32, device=dev),
-               "out_tokens": torch.empty((B, max_nodes), dtype=torch.int32, device=dev)}
+    if draft_token.shape[0] != T or target_token.shape[0] != T:
+        raise ValueError("parent / draft_token / target_token lengths disagree")
+    out = _accept_outputs(B, max_nodes, parent.device, out)
+    _need_flag(err_flag)
     st = ev_greedy_accept(_addr(node_start), _addr(parent), _addr(draft_token), _addr(target_token), B, T, max_nodes,
                           vocab, _addr(out["accept_len"]), _addr(out["accept_path"]), _addr(out["bonus"]),
                           _addr(out["out_tokens"]), _addr(err_flag), _stream(stream))
@@ -408,10 +452,12 @@ def compact_kv(k_cache, v_cache, kv_start, prefix_len, accept_len, accept_path, 
         raise ValueError("caches must be [slots, Hkv, D] or [layers, slots, Hkv, D]")
     if tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("k_cache / v_cache shapes disagree")
-    B = prefix_len.shape[0]
-    max_nodes = accept_path.shape[1]
+    B, max_nodes = _compact_meta(prefix_len, accept_len, accept_path, kv_start=kv_start)
     if new_len is None:
         new_len = torch.empty(B, dtype=torch.int32, device=k_cache.device)
+    else:
+        _need_out(new_len, "new_len", torch.int32, (B,))
+    _need_flag(err_flag)
     esz = k_cache.element_size()
     st = ev_compact_kv(_addr(k_cache), _addr(v_cache), esz, layers, slots * Hkv * D * esz, _addr(kv_start),
                        _addr(prefix_len), _addr(accept_len), _addr(accept_path), B, max_nodes, slots, Hkv, D,
@@ -436,10 +482,14 @@ def compact_kv_paged(k_pages, v_pages, block_table, prefix_len, accept_len, acce
         raise ValueError("pools must be [pages, page_size, Hkv, D] or [layers, pages, page_size, Hkv, D]")
     if tuple(v_pages.shape) != tuple(k_pages.shape):
         raise ValueError("k_pages / v_pages shapes disagree")
-    B = prefix_len.shape[0]
-    max_nodes = accept_path.shape[1]
+    B, max_nodes = _compact_meta(prefix_len, accept_len, accept_path)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table rows disagree with the batch")
     if new_len is None:
         new_len = torch.empty(B, dtype=torch.int32, device=k_pages.device)
+    else:
+        _need_out(new_len, "new_len", torch.int32, (B,))
+    _need_flag(err_flag)
     esz = k_pages.element_size()
     st = ev_compact_kv_paged(_addr(k_pages), _addr(v_pages), esz, layers, pages * page_size * Hkv * D * esz,
                              _addr(block_table), block_table.shape[1], page_size, _addr(prefix_len),
@@ -456,7 +506,25 @@ def _accept_outputs(B, max_nodes, dev, out):
                "accept_path": torch.empty((B, max_nodes), dtype=torch.int32, device=dev),
                "bonus": torch.empty(B, dtype=torch.int32, device=dev),
                "out_tokens": torch.empty((B, max_nodes), dtype=torch.int32, device=dev)}
+    else:
+        _need_accept(out, B, max_nodes)
     return out
+
+
+def _compact_meta(prefix_len, accept_len, accept_path, kv_start=None):
+    """Checks the compaction's per-sequence inputs; returns (batch, max_nodes)."""
+    torch = _torch()
+    _need(prefix_len, "prefix_len", torch.int32, 1)
+    _need(accept_len, "accept_len", torch.int32, 1)
+    _need(accept_path, "accept_path", torch.int32, 2)
+    B = prefix_len.shape[0]
+    if kv_start is not None:
+        _need(kv_start, "kv_start", torch.int32, 1)
+        if kv_start.shape[0] != B:
+            raise ValueError("kv_start / prefix_len lengths disagree")
+    if accept_len.shape[0] != B or accept_path.shape[0] != B:
+        raise ValueError("accept_len / accept_path rows disagree with the batch")
+    return B, accept_path.shape[1]
 
 
 def select_accept_compact(logits, node_start, parent, draft_token, k_cache, v_cache, kv_start, prefix_len, *,
@@ -479,8 +547,21 @@ def select_accept_compact(logits, node_start, parent, draft_token, k_cache, v_ca
     vocab = stride if vocab is None else vocab
     B = node_start.shape[0] - 1
     T = parent.shape[0]
+    if R != T or draft_token.shape[0] != T:
+        raise ValueError("logits rows / parent / draft_token lengths disagree")
+    _need(prefix_len, "prefix_len", torch.int32, 1)
+    if prefix_len.shape[0] != B:
+        raise ValueError("prefix_len length disagrees with the batch")
     dev = parent.device
     paged = block_table is not None
+    if paged:
+        _need(block_table, "block_table", torch.int32, 2)
+        if block_table.shape[0] != B:
+            raise ValueError("block_table rows disagree with the batch")
+    else:
+        _need(kv_start, "kv_start", torch.int32, 1)
+        if kv_start.shape[0] != B:
+            raise ValueError("kv_start length disagrees with the batch")
     base = 4 if paged else 3
     if k_cache.dim() == base:
         layers, dims = 1, tuple(k_cache.shape)
@@ -494,9 +575,14 @@ def select_accept_compact(logits, node_start, parent, draft_token, k_cache, v_ca
         rows_per_layer *= int(x)
     if target is None:
         target = torch.empty(R, dtype=torch.int32, device=dev)
+    else:
+        _need_out(target, "target", torch.int32, (R,))
     out = _accept_outputs(B, max_nodes, dev, out)
     if new_len is None:
         new_len = torch.empty(B, dtype=torch.int32, device=dev)
+    else:
+        _need_out(new_len, "new_len", torch.int32, (B,))
+    _need_flag(err_flag)
     need = ev_select_workspace_size(T, vocab)
     if need and (workspace is None or workspace.nbytes < need):
         workspace = Workspace(need, dev)
@@ -508,7 +594,6 @@ def select_accept_compact(logits, node_start, parent, draft_token, k_cache, v_ca
             _addr(out["out_tokens"]), _addr(new_len), workspace.ptr if workspace is not None else None,
             workspace.nbytes if workspace is not None else 0, _addr(err_flag), _stream(stream))
     if paged:
-        _need(block_table, "block_table", torch.int32, 2)
         st = ev_select_accept_compact_paged(*common, _addr(block_table), block_table.shape[1], dims[1],
                                             _addr(prefix_len), dims[0], *tail)
         _check(st, "ev_select_accept_compact_paged")
