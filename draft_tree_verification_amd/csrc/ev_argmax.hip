@@ -8,8 +8,8 @@
 // HBM-bound streaming: each thread reads 16 bytes per load, eight loads in flight.  Values are
 // mapped to order-preserving unsigned keys (sign-magnitude -> offset binary, both zeros to the
 // same key); for bf16 the key transform and the per-load maximum run on packed 16-bit integer
-// ops, and the index of a new maximum is searched only when a load beats the running best (rare
-// after the first few loads), so ties keep the earliest index for free.  Rows with few rows in the
+// ops, and a round of eight loads searches an index only when its maximum beats the running best,
+// and then only in the first load that holds it, so ties keep the earliest index for free.  Rows with few rows in the
 // batch are split across workgroups; the pieces meet through a 64-bit atomicMax on
 // (key << 32 | ~index) and the last-arriving workgroup writes the token.  In the fused step
 // (ev_select_accept_compact) each piece instead stores its (key << 32 | ~index) word, and the
@@ -72,6 +72,17 @@ __device__ __forceinline__ us2 keys2(uint32_t w) {
     const us2 mag = h & static_cast<unsigned short>(0x7FFF);
     const us2 smask = __builtin_bit_cast(us2, __builtin_bit_cast(ss2, h) >> static_cast<short>(15));
     return ((mag ^ smask) - smask) + static_cast<unsigned short>(0x8000);
+}
+
+// Largest key of the eight bf16 values in one 16-byte load, 0xFFFF when any of them is a NaN.
+__device__ __forceinline__ uint32_t load_max_key(u32x4_t w) {
+    const us2 k0 = keys2(w[0]), k1 = keys2(w[1]), k2 = keys2(w[2]), k3 = keys2(w[3]);
+    const us2 km = __builtin_elementwise_max(__builtin_elementwise_max(k0, k1), __builtin_elementwise_max(k2, k3));
+    const us2 mags = __builtin_elementwise_max(
+        __builtin_elementwise_max(__builtin_bit_cast(us2, w[0] & 0x7FFF7FFFu), __builtin_bit_cast(us2, w[1] & 0x7FFF7FFFu)),
+        __builtin_elementwise_max(__builtin_bit_cast(us2, w[2] & 0x7FFF7FFFu), __builtin_bit_cast(us2, w[3] & 0x7FFF7FFFu)));
+    const bool has_nan = mags[0] > 0x7F80u || mags[1] > 0x7F80u;
+    return has_nan ? 0xFFFFu : (km[0] > km[1] ? km[0] : km[1]);
 }
 
 __device__ __forceinline__ unsigned long long pack(uint32_t key, int32_t idx) {
@@ -156,13 +167,41 @@ __global__ __launch_bounds__(kThreads) void node_argmax_kernel(const ArgmaxArgs 
                 }
             }
         };
-        // main body: eight 16-byte loads in flight per thread (a split of 8 quanta is one round trip)
+        // main body: eight 16-byte loads in flight per thread (a split of 8 quanta is one round trip).
+        // Each load's maximum key comes from the packed keys (0xFFFF when the load holds a NaN);
+        // only when the round's maximum beats the running best is a single load -- the first
+        // one holding that maximum -- scanned value by value for its lowest index.  (A wave runs
+        // a per-lane scan whenever any of its lanes needs one, so scanning per load would run
+        // nearly every load's scan in the first rounds.)
         for (; base + 7 * kSegQuantum + kChunk <= v1; base += 8 * kSegQuantum) {
             u32x4_t w[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) w[k] = ev::ld16_stream(rp + base + k * kSegQuantum);
+            uint32_t km[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) consume(w[k], base + k * kSegQuantum);
+            for (int k = 0; k < 8; ++k) km[k] = load_max_key(w[k]);
+            uint32_t rk = km[0];
+#pragma unroll
+            for (int k = 1; k < 8; ++k) rk = km[k] > rk ? km[k] : rk;
+            if (rk > best) {
+                u32x4_t x = w[7];
+                int at = base + 7 * kSegQuantum;
+#pragma unroll
+                for (int k = 6; k >= 0; --k) {
+                    if (km[k] == rk) {
+                        x = w[k];
+                        at = base + k * kSegQuantum;
+                    }
+                }
+                int first = at + 7;
+#pragma unroll
+                for (int e = 6; e >= 0; --e) {
+                    const uint32_t h = (e & 1) ? (x[e >> 1] >> 16) : (x[e >> 1] & 0xFFFFu);
+                    if (key_bf16(h) == rk) first = at + e;
+                }
+                best = rk;
+                bidx = first;
+            }
         }
         for (; base + 3 * kSegQuantum + kChunk <= v1; base += 4 * kSegQuantum) {
             u32x4_t w[4];
