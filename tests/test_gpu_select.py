@@ -74,6 +74,39 @@ def test_argmax_special_values(dtype):
     _check_argmax(np.ascontiguousarray(np.repeat(raw, 200, axis=0)), what="special x200")
 
 
+@pytest.mark.parametrize("rows,vocab", [(64, 151936), (2048, 40000)])
+def test_argmax_full_rounds_placements(rows, vocab):
+    """bf16 rows long enough for whole rounds of eight loads per thread (split rows of one round
+    per piece, and unsplit rows of several rounds): repeated maxima, NaNs of either sign, signed
+    zeros and infinities at random positions, so the winner lies in any load, lane or round."""
+    gu.log(f"[case] argmax placements rows={rows} vocab={vocab}")
+    rng = np.random.default_rng(rows * 7 + vocab)
+    x = rng.standard_normal((rows, vocab)).astype(np.float32)
+    for r in range(rows):
+        kind = r % 6
+        pos = rng.choice(vocab, size=4, replace=False)
+        if kind == 0:                                   # the maximum three times
+            x[r, pos[:3]] = 8.0
+        elif kind == 1:                                 # twice in one 16-byte load, once later
+            p0 = int(rng.integers(0, vocab - 8)) // 8 * 8
+            x[r, [p0 + 5, p0 + 2]] = 8.0
+            x[r, pos[0]] = 8.0
+        elif kind == 2:                                 # NaNs of either sign: the first one wins
+            x[r, pos[0]] = np.float32("nan")
+            x[r, pos[1]] = -np.float32("nan")
+        elif kind == 3:                                 # all negative but for signed zeros
+            x[r] = -np.abs(x[r]) - 1.0
+            x[r, pos[0]] = -0.0
+            x[r, pos[1]] = 0.0
+            x[r, pos[2]] = -0.0
+        elif kind == 4:                                 # +inf twice
+            x[r, pos[:2]] = np.float32("inf")
+        else:                                           # every value equal: the first index
+            x[r] = 1.5
+    raw = synth.f32_to_bf16_bits(x)
+    _check_argmax(raw, what=f"placements {rows}x{vocab}")
+
+
 def _gpu_accept(node_start, parent, draft, target, max_nodes, vocab):
     import torch
     from draft_tree_verification_amd import ev
