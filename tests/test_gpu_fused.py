@@ -125,6 +125,45 @@ def _run(c, temperature=0.0, seed=0, offset=0, p_agree=0.8, what=""):
     return mean_len
 
 
+def test_special_logits_full_rounds():
+    """Rows long enough for whole rounds of loads, with repeated maxima, NaNs of either sign,
+    signed zeros and infinities at random positions: the fused call's tokens (the maximum over a
+    row's per-piece words) equal the oracle's argmax, and the step matches the separate calls."""
+    gu.log("[case] fused special logits, full rounds")
+    c = _case(77, B=6, max_n=16, vocab=151936, stride=151936, logit_dtype=BF16, layers=1, H=2, D=64,
+              cache_dtype=np.uint16)
+    rng = np.random.default_rng(78)
+    T, V = c["logits"].shape
+    x = rng.standard_normal((T, V)).astype(np.float32)
+    for r in range(T):
+        pos = rng.choice(V, size=3, replace=False)
+        kind = r % 5
+        if kind == 0:
+            x[r, pos] = 8.0
+        elif kind == 1:
+            x[r, pos[0]] = np.float32("nan")
+            x[r, pos[1]] = -np.float32("nan")
+        elif kind == 2:
+            x[r] = -np.abs(x[r]) - 1.0
+            x[r, pos[0]] = -0.0
+            x[r, pos[1]] = 0.0
+        elif kind == 3:
+            x[r, pos[:2]] = np.float32("inf")
+        else:
+            x[r] = -2.5
+    c["logits"] = synth.f32_to_bf16_bits(x)
+    tref, _ = oracle.node_argmax(c["logits"], vocab=V, row_stride=V)
+    draft = _planted(c["rng"], c["trees"], tref, V, 0.8)
+    d = _dev(c, draft)
+    k1, v1 = gu.to_dev(c["k"]), gu.to_dev(c["v"])
+    k2, v2 = k1.clone(), v1.clone()
+    sep = _separate(d, k1, v1, c, 0.0, 0, 0)
+    fus = _fused(d, k2, v2, c, 0.0, 0, 0)
+    _compare(sep, fus, "special logits")
+    assert np.array_equal(fus[0].cpu().numpy(), tref), "fused tokens differ from the oracle argmax"
+    assert gu.to_host(k1).tobytes() == gu.to_host(k2).tobytes()
+
+
 @pytest.mark.parametrize("cache_dtype", [np.uint16, np.float32])
 def test_greedy_layers(cache_dtype):
     gu.log(f"[case] fused greedy 3 layers {cache_dtype}")
