@@ -127,7 +127,8 @@ def cpu_baseline(w, target_seconds: float, temperature: float = 0.0):
             tgt, _ = oracle.node_sample(logits, temperature, 0x5EED, reps, lib=lib)
         else:
             tgt, _ = oracle.node_argmax(logits, lib=lib)
-        acc_r = oracle.greedy_accept(ns, par, draft, tgt, w.max_nodes, w.vocab, lib=lib)
+        accept = oracle.sampled_accept if temperature > 0 else oracle.greedy_accept
+        acc_r = accept(ns, par, draft, tgt, w.max_nodes, w.vocab, lib=lib)
         oracle.compact_kv(k[None], v[None], ks, pl, acc_r["accept_len"], acc_r["accept_path"], num_layers=1,
                           total_slots=slot_end, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, lib=lib)
         reps += 1
@@ -245,10 +246,12 @@ def main():
     f_attn = {"contiguous": lib.ev_tree_attention, "paged": lib.ev_tree_attention_paged,
               "window": lib.ev_tree_attention_window}[args.kv]
     if args.separate:
-        f_arg, f_acc = (lib.ev_node_sample if args.sample > 0 else lib.ev_node_argmax), lib.ev_greedy_accept
+        f_arg = lib.ev_node_sample if args.sample > 0 else lib.ev_node_argmax
+        f_acc = lib.ev_sampled_accept if args.sample > 0 else lib.ev_greedy_accept
         f_cmp = lib.ev_compact_kv_paged if args.kv == "paged" else lib.ev_compact_kv
         fns = (f_attn, f_arg, f_acc, f_cmp)
-        names = ("tree_attention", "node_sample" if args.sample > 0 else "node_argmax", "greedy_accept", "compact_kv")
+        names = ("tree_attention", "node_sample" if args.sample > 0 else "node_argmax",
+                 "sampled_accept" if args.sample > 0 else "greedy_accept", "compact_kv")
     else:
         fns = (f_attn, lib.ev_select_accept_compact_paged if args.kv == "paged" else lib.ev_select_accept_compact)
         names = ("tree_attention", "select_accept_compact")

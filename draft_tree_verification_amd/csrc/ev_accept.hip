@@ -9,6 +9,13 @@
 // batch (same article, "Current Limitation"), so compaction moves each sequence's accepted rows
 // right after its own prefix.
 //
+// Sampled verification (temperature > 0; the pages report T = 1 results and state that
+// verification keeps the target's output distribution) takes each node's draw as its target
+// token, and a child is accepted only if no lower-index sibling holds the same drafted token:
+// speculative sampling tries the children in order against the node's draw, so a repeated token
+// is never tried twice.  The accepted nodes are then one root path -- the walk that enters the
+// first child holding the draw -- and its last node ends the round.
+//
 // One wavefront per sequence, lane i = tree node i (trees have at most 64 nodes).
 #include <cmath>
 
@@ -31,7 +38,9 @@ struct LaneAccept {
     int depth;  // this lane's depth when its node is on the accepted path, else -1
 };
 
-__device__ LaneAccept accept_lanes(int lane, int n, int err, int par, int tgt, int dft, int vocab) {
+// sampled: the first-child rule of sampled verification (a child repeating a lower-index
+// sibling's drafted token is never accepted); otherwise the greedy rule.  n is wave-uniform.
+__device__ LaneAccept accept_lanes(int lane, int n, int err, int par, int tgt, int dft, int vocab, bool sampled) {
     if (!err && lane < n) {
         if (lane == 0 ? par != -1 : (par < 0 || par >= lane)) err |= EV_DATA_BAD_PARENT;
         if (tgt < 0 || tgt >= vocab) err |= EV_DATA_BAD_TOKEN;
@@ -43,7 +52,18 @@ __device__ LaneAccept accept_lanes(int lane, int n, int err, int par, int tgt, i
     if (err) return r;
     // an edge agrees when the child's draft token is the parent's greedy token
     const int tpar = __shfl(tgt, par >= 0 ? par : 0, 64);
-    const bool agree = lane < n && (lane == 0 || dft == tpar);
+    bool agree = lane < n && (lane == 0 || dft == tpar);
+    if (sampled) {
+        // a lower-index sibling with the same drafted token takes precedence (scalar reads of
+        // every node's parent and token, one node per step)
+        bool repeat = false;
+        for (int j = 1; j < n; ++j) {
+            const int pj = __builtin_amdgcn_readlane(par, j);
+            const int dj = __builtin_amdgcn_readlane(dft, j);
+            repeat |= j < lane && pj == par && dj == dft;
+        }
+        agree = agree && !repeat;
+    }
     // accepted(i) = every edge on the root path agrees; depth(i) = edges on it; anc = bitmask
     bool acc = agree;
     int depth = 0;
@@ -107,7 +127,8 @@ __device__ __forceinline__ int node_range(const AcceptArgs &a, int b, int &ns0, 
     return (ns0 < 0 || ns1 > a.total_nodes || n < 1 || n > a.max_nodes) ? EV_DATA_BAD_NODES : 0;
 }
 
-__global__ __launch_bounds__(64) void greedy_accept_kernel(const AcceptArgs a) {
+template <bool SAMPLED>
+__global__ __launch_bounds__(64) void accept_kernel(const AcceptArgs a) {
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
     int ns0, n;
@@ -118,7 +139,7 @@ __global__ __launch_bounds__(64) void greedy_accept_kernel(const AcceptArgs a) {
         tgt = a.target[ns0 + lane];
         dft = a.draft[ns0 + lane];
     }
-    write_accept(a, b, lane, accept_lanes(lane, n, err, par, tgt, dft, a.vocab), dft);
+    write_accept(a, b, lane, accept_lanes(lane, n, err, par, tgt, dft, a.vocab, SAMPLED), dft);
 }
 
 // Fused step: the per-piece winners of the selection pass and where the row tokens go.
@@ -126,6 +147,7 @@ struct SelectArgs {
     AcceptArgs acc;                      // target: unused (the tokens come from the pieces)
     const unsigned long long *pieces;    // [rows][splits]: (order key << 32) | ~index
     int32_t splits;
+    int32_t sampled;                     // the pieces are draws (temperature > 0): first-child rule
     int32_t *target_out;                 // [rows] the finished tokens
 };
 
@@ -190,7 +212,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kv_kernel(const Compa
                 tgt = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(w & 0xFFFFFFFFu));
                 if (layer == 0) sel.target_out[row] = tgt;
             }
-            const LaneAccept r = accept_lanes(tid, n, err0, par, tgt, dft, x.vocab);
+            const LaneAccept r = accept_lanes(tid, n, err0, par, tgt, dft, x.vocab, sel.sampled != 0);
             if (layer == 0) write_accept(x, b, tid, r, dft);
             if (r.depth >= 0) s_path[r.depth] = tid;
             if (tid == 0) s_len = r.err ? 0 : r.len;
@@ -263,11 +285,11 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kv_kernel(const Compa
 
 }  // namespace
 
-extern "C" ev_status ev_greedy_accept(const int32_t *node_start, const int32_t *parent, const int32_t *draft_token,
-                                      const int32_t *target_token, int32_t batch, int32_t total_nodes,
-                                      int32_t max_nodes, int32_t vocab, int32_t *accept_len, int32_t *accept_path,
-                                      int32_t *bonus_token, int32_t *out_tokens, int32_t *err_flag,
-                                      hipStream_t stream) {
+namespace {
+ev_status launch_accept(const int32_t *node_start, const int32_t *parent, const int32_t *draft_token,
+                        const int32_t *target_token, int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                        int32_t vocab, int32_t *accept_len, int32_t *accept_path, int32_t *bonus_token,
+                        int32_t *out_tokens, int32_t *err_flag, bool sampled, hipStream_t stream) {
     if (!node_start || !parent || !draft_token || !target_token || !accept_len || !accept_path || !bonus_token ||
         !out_tokens)
         return EV_ERR_NULL;
@@ -277,8 +299,28 @@ extern "C" ev_status ev_greedy_accept(const int32_t *node_start, const int32_t *
     if (batch == 0) return EV_OK;
     AcceptArgs args{node_start, parent, draft_token, target_token, batch, total_nodes, max_nodes, vocab,
                     accept_len, accept_path, bonus_token, out_tokens, err_flag};
-    hipLaunchKernelGGL(greedy_accept_kernel, dim3(batch), dim3(64), 0, stream, args);
+    if (sampled) hipLaunchKernelGGL(accept_kernel<true>, dim3(batch), dim3(64), 0, stream, args);
+    else hipLaunchKernelGGL(accept_kernel<false>, dim3(batch), dim3(64), 0, stream, args);
     return ev::launch_status();
+}
+}  // namespace
+
+extern "C" ev_status ev_greedy_accept(const int32_t *node_start, const int32_t *parent, const int32_t *draft_token,
+                                      const int32_t *target_token, int32_t batch, int32_t total_nodes,
+                                      int32_t max_nodes, int32_t vocab, int32_t *accept_len, int32_t *accept_path,
+                                      int32_t *bonus_token, int32_t *out_tokens, int32_t *err_flag,
+                                      hipStream_t stream) {
+    return launch_accept(node_start, parent, draft_token, target_token, batch, total_nodes, max_nodes, vocab,
+                         accept_len, accept_path, bonus_token, out_tokens, err_flag, false, stream);
+}
+
+extern "C" ev_status ev_sampled_accept(const int32_t *node_start, const int32_t *parent, const int32_t *draft_token,
+                                       const int32_t *target_token, int32_t batch, int32_t total_nodes,
+                                       int32_t max_nodes, int32_t vocab, int32_t *accept_len, int32_t *accept_path,
+                                       int32_t *bonus_token, int32_t *out_tokens, int32_t *err_flag,
+                                       hipStream_t stream) {
+    return launch_accept(node_start, parent, draft_token, target_token, batch, total_nodes, max_nodes, vocab,
+                         accept_len, accept_path, bonus_token, out_tokens, err_flag, true, stream);
 }
 
 namespace {
@@ -388,6 +430,7 @@ ev_status select_accept_compact(const void *logits, ev_dtype dtype, int64_t row_
     sel.pieces = static_cast<const unsigned long long *>(workspace);
     sel.splits = total_nodes > 0 ? ev::select_splits(total_nodes, vocab) : 1;
     sel.target_out = target_token;
+    sel.sampled = temperature > 0.f;
     if (total_nodes > 0) {
         st = ev::launch_select_pieces(logits, dtype, row_stride, total_nodes, vocab, temperature, seed, offset,
                                       static_cast<unsigned long long *>(workspace), stream);

@@ -26,7 +26,8 @@ MAX_BATCH = 2048
 
 EXPORTS = ("ev_status_string", "ev_tree_attention_workspace_size", "ev_tree_attention",
            "ev_tree_attention_window", "ev_tree_attention_paged", "ev_node_argmax_workspace_size",
-           "ev_node_argmax", "ev_node_sample", "ev_greedy_accept", "ev_compact_kv", "ev_compact_kv_paged",
+           "ev_node_argmax", "ev_node_sample", "ev_greedy_accept", "ev_sampled_accept", "ev_compact_kv",
+           "ev_compact_kv_paged",
            "ev_select_workspace_size", "ev_select_accept_compact", "ev_select_accept_compact_paged",
            "ev_stream_read")
 
@@ -71,6 +72,8 @@ def load(path: str = LIB_PATH):
                                    _SZ, _P]
     lib.ev_greedy_accept.restype = ctypes.c_int
     lib.ev_greedy_accept.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]
+    lib.ev_sampled_accept.restype = ctypes.c_int
+    lib.ev_sampled_accept.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]
     lib.ev_compact_kv.restype = ctypes.c_int
     lib.ev_compact_kv.argtypes = [_P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P,
                                   _P, _P]
@@ -157,6 +160,12 @@ def ev_node_sample(logits, dtype, row_stride, num_rows, vocab, temperature, seed
 def ev_greedy_accept(node_start, parent, draft_token, target_token, batch, total_nodes, max_nodes, vocab, accept_len,
                      accept_path, bonus_token, out_tokens, err_flag, stream) -> int:
     return load().ev_greedy_accept(node_start, parent, draft_token, target_token, batch, total_nodes, max_nodes,
+                                   vocab, accept_len, accept_path, bonus_token, out_tokens, err_flag, stream)
+
+
+def ev_sampled_accept(node_start, parent, draft_token, target_token, batch, total_nodes, max_nodes, vocab, accept_len,
+                     accept_path, bonus_token, out_tokens, err_flag, stream) -> int:
+    return load().ev_sampled_accept(node_start, parent, draft_token, target_token, batch, total_nodes, max_nodes,
                                    vocab, accept_len, accept_path, bonus_token, out_tokens, err_flag, stream)
 
 
@@ -421,6 +430,19 @@ def greedy_accept(node_start, parent, draft_token, target_token, *, max_nodes: i
                   err_flag=None, stream=None):
     """Longest accepted path per sequence (ev_greedy_accept).
     Returns dict(accept_len [B], accept_path [B, max_nodes], bonus [B], out_tokens [B, max_nodes])."""
+    return _accept(ev_greedy_accept, "ev_greedy_accept", node_start, parent, draft_token, target_token, max_nodes,
+                   vocab, out, err_flag, stream)
+
+
+def sampled_accept(node_start, parent, draft_token, target_token, *, max_nodes: int, vocab: int, out=None,
+                   err_flag=None, stream=None):
+    """Sampled-verification acceptance from per-node draws (ev_sampled_accept): the walk into the
+    lowest-index child holding each node's draw.  Returns what greedy_accept returns."""
+    return _accept(ev_sampled_accept, "ev_sampled_accept", node_start, parent, draft_token, target_token, max_nodes,
+                   vocab, out, err_flag, stream)
+
+
+def _accept(fn, name, node_start, parent, draft_token, target_token, max_nodes, vocab, out, err_flag, stream):
     torch = _torch()
     for name, t in (("node_start", node_start), ("parent", parent), ("draft_token", draft_token),
                     ("target_token", target_token)):
@@ -431,10 +453,10 @@ def greedy_accept(node_start, parent, draft_token, target_token, *, max_nodes: i
         raise ValueError("parent / draft_token / target_token lengths disagree")
     out = _accept_outputs(B, max_nodes, parent.device, out)
     _need_flag(err_flag)
-    st = ev_greedy_accept(_addr(node_start), _addr(parent), _addr(draft_token), _addr(target_token), B, T, max_nodes,
-                          vocab, _addr(out["accept_len"]), _addr(out["accept_path"]), _addr(out["bonus"]),
-                          _addr(out["out_tokens"]), _addr(err_flag), _stream(stream))
-    _check(st, "ev_greedy_accept")
+    st = fn(_addr(node_start), _addr(parent), _addr(draft_token), _addr(target_token), B, T, max_nodes, vocab,
+            _addr(out["accept_len"]), _addr(out["accept_path"]), _addr(out["bonus"]), _addr(out["out_tokens"]),
+            _addr(err_flag), _stream(stream))
+    _check(st, name)
     return out
 
 

@@ -12,7 +12,8 @@
  *                       prefix plus its own ancestors (and itself)
  *   ev_node_argmax      the target's greedy token for every tree node (row argmax of logits)
  *   ev_greedy_accept    the longest accepted root-to-node path per sequence, its bonus token
- *                       and the tokens the round emits
+ *                       and the tokens the round emits (ev_sampled_accept: the same at
+ *                       temperature > 0, from per-node draws)
  *   ev_compact_kv       in-place move of the accepted nodes' K/V rows right after the prefix,
  *                       so the next round sees prefix + accepted tokens contiguously (the pages
  *                       name per-sequence acceptance lengths under continuous batching as the
@@ -209,10 +210,12 @@ ev_status ev_node_argmax(const void *logits, ev_dtype dtype, int64_t row_stride,
  * Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) under key (seed, offset) and counter
  * (v / 8, r, 0, 0): 64-bit output k gives elements 8j + 2k (low half) and 8j + 2k + 1 (high
  * half).  Use a fresh (seed, offset) per call (e.g. offset = decoding round) for fresh noise.
- * Fed to ev_greedy_accept as target_token, the draws make the accept step speculative sampling
- * along the tree with the drafted children as point proposals: a sequence descends into the
- * child holding its node's draw and otherwise stops with the draw as bonus, which keeps the
- * target's sampling distribution (release note, opening section).  The log2 is the hardware's
+ * Fed to ev_sampled_accept as target_token, the draws make the accept step speculative
+ * sampling along the tree with the drafted children as point proposals: a sequence descends
+ * into the lowest-index child holding its node's draw and otherwise stops with the draw as
+ * bonus, which keeps the target's sampling distribution (release note, opening section).  (Not
+ * ev_greedy_accept: its deepest-path choice among siblings holding the same token would pick
+ * between independent draws by their outcomes.)  The log2 is the hardware's
  * (about 1 ulp), so a draw can differ from an exact evaluation only where two scores of the row
  * agree to a few ulps.
  *
@@ -245,6 +248,27 @@ ev_status ev_greedy_accept(const int32_t *node_start, const int32_t *parent, con
                            int32_t vocab,
                            int32_t *accept_len, int32_t *accept_path, int32_t *bonus_token, int32_t *out_tokens,
                            int32_t *err_flag, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ev_sampled_accept
+ *
+ * Acceptance of sampled verification (temperature > 0; the pages report T = 1 results --
+ * aiposthub.com analysis, section "它和 DFlash 2、DSpark 比，贏在哪個條件？" -- and say that
+ * verification keeps the target model's output distribution: kongchang.com English article,
+ * "Technical Background"; arex-research.com release note, opening section).  target_token[i] is
+ * node i's draw from the target (ev_node_sample).  Drafted children are point proposals, and
+ * speculative sampling tries a node's children in index order against its draw, so:
+ *   accepted(0) = true;  for i >= 1, accepted(i) = accepted(parent(i)) and
+ *   draft_token[i] == target_token[parent(i)] and no sibling j < i has draft_token[j] ==
+ *   draft_token[i]
+ * The accepted nodes form one root path (the walk into the lowest-index child holding each
+ * node's draw); i* is its last node.  Outputs, arguments, layouts and data errors are those of
+ * ev_greedy_accept; on trees whose siblings hold distinct tokens both calls give the same result.
+ * -------------------------------------------------------------------------------------------*/
+ev_status ev_sampled_accept(const int32_t *node_start, const int32_t *parent, const int32_t *draft_token,
+                            const int32_t *target_token, int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                            int32_t vocab, int32_t *accept_len, int32_t *accept_path, int32_t *bonus_token,
+                            int32_t *out_tokens, int32_t *err_flag, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * ev_compact_kv
@@ -298,8 +322,9 @@ ev_status ev_compact_kv_paged(void *k_pages, void *v_pages, int32_t elem_bytes, 
 /* ---------------------------------------------------------------------------------------------
  * ev_select_accept_compact
  *
- * ev_node_argmax (temperature == 0) or ev_node_sample (temperature > 0), then ev_greedy_accept
- * on those tokens, then ev_compact_kv of the accepted paths: the per-node target token, the
+ * ev_node_argmax then ev_greedy_accept (temperature == 0), or ev_node_sample then
+ * ev_sampled_accept (temperature > 0), then ev_compact_kv of the accepted paths: the per-node
+ * target token, the
  * accept rule and the KV move of one verification round (kongchang.com English article,
  * "Technical Background"), in two launches instead of three and without the arrival counting
  * that the standalone argmax needs.  The first launch streams the logits and leaves every row
@@ -308,7 +333,7 @@ ev_status ev_compact_kv_paged(void *k_pages, void *v_pages, int32_t elem_bytes, 
  * output is bit-identical to the three separate calls on the same inputs:
  *
  *   target_token   [total_nodes]  as ev_node_argmax / ev_node_sample (no max_value output)
- *   accept_len, accept_path, bonus_token, out_tokens   as ev_greedy_accept
+ *   accept_len, accept_path, bonus_token, out_tokens   as ev_greedy_accept / ev_sampled_accept
  *   K/V caches, new_len                                as ev_compact_kv
  *
  *   logits, dtype, row_stride, vocab   as ev_node_argmax, num_rows = total_nodes

@@ -87,6 +87,8 @@ def _bind(lib):
                                        _P, _P]
     lib.oracle_greedy_accept.restype = None
     lib.oracle_greedy_accept.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]
+    lib.oracle_sampled_accept.restype = None
+    lib.oracle_sampled_accept.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]
     lib.oracle_compact_kv.restype = None
     lib.oracle_compact_kv.argtypes = [_P, _P, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _I32, _I64,
                                       _I32, _I32, _P, _P]
@@ -242,8 +244,20 @@ def node_sample(logits, temperature: float, seed: int, offset: int, vocab: int =
 
 
 def greedy_accept(node_start, parent, draft, target, max_nodes: int, vocab: int, lib=None):
-    """Returns dict of accept_len [B], accept_path [B, max_nodes], bonus [B], out_tokens [B, max_nodes],
+    """Greedy (temperature 0) acceptance: the deepest accepted node, lowest index on equal depth.
+    Returns dict of accept_len [B], accept_path [B, max_nodes], bonus [B], out_tokens [B, max_nodes],
     seq_err [B]."""
+    return _accept("oracle_greedy_accept", node_start, parent, draft, target, max_nodes, vocab, lib)
+
+
+def sampled_accept(node_start, parent, draft, target, max_nodes: int, vocab: int, lib=None):
+    """Sampled (temperature > 0) acceptance, ``target`` holding each node's draw: the walk from the
+    root into the lowest-index child holding the current node's draw.  Same returns as
+    greedy_accept."""
+    return _accept("oracle_sampled_accept", node_start, parent, draft, target, max_nodes, vocab, lib)
+
+
+def _accept(fn, node_start, parent, draft, target, max_nodes, vocab, lib):
     lib = lib or load()
     node_start, parent, draft, target = map(_i32, (node_start, parent, draft, target))
     B = len(node_start) - 1
@@ -253,8 +267,8 @@ def greedy_accept(node_start, parent, draft, target, max_nodes: int, vocab: int,
     bonus = np.zeros(max(B, 1), np.int32)
     outt = np.zeros((max(B, 1), max_nodes), np.int32)
     err = np.zeros(max(B, 1), np.int32)
-    lib.oracle_greedy_accept(_ptr(node_start), _ptr(parent), _ptr(draft), _ptr(target), B, max_nodes,
-                             int(vocab), _ptr(acc), _ptr(path), _ptr(bonus), _ptr(outt), _ptr(err))
+    getattr(lib, fn)(_ptr(node_start), _ptr(parent), _ptr(draft), _ptr(target), B, max_nodes, int(vocab),
+                     _ptr(acc), _ptr(path), _ptr(bonus), _ptr(outt), _ptr(err))
     return {"accept_len": acc[:B], "accept_path": path[:B], "bonus": bonus[:B], "out_tokens": outt[:B],
             "seq_err": err[:B]}
 

@@ -25,8 +25,13 @@
  *   - sampled verification (T > 0, reported at temperature 1 in aiposthub.com analysis, "它和
  *     DFlash 2、DSpark 比，贏在哪個條件？", and arex-research.com, "论文口径与推文口径"): drafted
  *     children are point proposals, so speculative sampling along the tree is a per-node draw
- *     from softmax(z / T) followed by the greedy acceptance rule on the draws (see the sampled
- *     section below for the draw and its generator).
+ *     from softmax(z / T) and a walk from the root that enters the LOWEST-INDEX child holding
+ *     the current node's draw and stops with the draw as bonus when no child holds it (see the
+ *     sampled section below for the draw, its generator and why a repeated sibling token is
+ *     never entered).
+ *
+ * Fixed-size work arrays hold at most ORACLE_MAX_NODES tree nodes; larger trees are reported as
+ * a node-count error (bit 2) instead of being processed.
  *
  * Parity pins: every function here is checked in tests against an independent formulation
  * (brute force / library routines / closed forms / hand-built cases); none is unpinned.
@@ -44,6 +49,7 @@
 #endif
 
 enum { OR_BF16 = 0, OR_F32 = 1 };
+enum { ORACLE_MAX_NODES = 1024 }; /* capacity of the per-tree work arrays below */
 
 /* Element `idx` of a bf16 (raw bits) or fp32 array, widened exactly to double. */
 static double elem(const void *base, int dtype, size_t idx) {
@@ -64,10 +70,11 @@ int oracle_num_threads(void) {
 #endif
 }
 
-/* Tree rule: parent[0] == -1 and 0 <= parent[i] < i; 1 <= n <= max_nodes. */
+/* Tree rule: parent[0] == -1 and 0 <= parent[i] < i; 1 <= n <= max_nodes (and n within the
+   work arrays' capacity). */
 int32_t oracle_tree_errors(const int32_t *parent, int32_t n, int32_t max_nodes) {
     int32_t err = 0;
-    if (n < 1 || n > max_nodes) return 2;
+    if (n < 1 || n > max_nodes || n > ORACLE_MAX_NODES) return 2;
     if (parent[0] != -1) err |= 1;
     for (int32_t i = 1; i < n; ++i)
         if (parent[i] < 0 || parent[i] >= i) err |= 1;
@@ -75,11 +82,17 @@ int32_t oracle_tree_errors(const int32_t *parent, int32_t n, int32_t max_nodes) 
 }
 
 /* Ancestors of node i including i itself, written root first (increasing depth).
-   Returns how many there are, i.e. depth(i) + 1. */
+   Returns how many there are, i.e. depth(i) + 1; -1 when i is outside [0, ORACLE_MAX_NODES) or
+   the chain breaks the topological rule (a parent index not below its child's), which would
+   otherwise loop or overrun the work array. */
 int32_t oracle_ancestor_path(const int32_t *parent, int32_t i, int32_t *path) {
-    int32_t rev[1024];
+    int32_t rev[ORACLE_MAX_NODES];
     int32_t n = 0;
-    for (int32_t j = i; j >= 0; j = parent[j]) rev[n++] = j;
+    if (i < 0 || i >= ORACLE_MAX_NODES) return -1;
+    for (int32_t j = i; j >= 0; j = parent[j]) {
+        if (j > 0 && parent[j] >= j) return -1;
+        rev[n++] = j;
+    }
     for (int32_t t = 0; t < n; ++t) path[t] = rev[n - 1 - t];
     return n;
 }
@@ -152,7 +165,7 @@ static void attention_row(const void *q, const void *k, const void *v, int dtype
     const int32_t L = prefix_len[b];
     const int32_t t0 = first_visible(L, window);
     const int32_t *par = parent + node_start[b];
-    int32_t path[1024];
+    int32_t path[ORACLE_MAX_NODES];
     int32_t np = oracle_ancestor_path(par, i, path);
     int64_t nvis = 0;
     for (int32_t t = t0; t < L; ++t) slots[nvis++] = token_slot(kv_start, bt, bt_stride, page, b, t);
@@ -282,12 +295,16 @@ void oracle_node_argmax(const void *logits, int32_t dtype, int64_t row_stride, i
 /* ---- Sampled verification (temperature T > 0) ----
    Reading: a drafted child is a point proposal for its parent's next token (the dynamic tree
    expands the drafter's best tokens).  Speculative sampling with point proposals tries a node's
-   children in turn, accepting child token x with the residual target probability of x and
-   removing x from the residual when it is rejected; the bonus token is then drawn from what is
-   left.  The result has the law of one draw y from the target distribution at the node, with the
-   walk descending into the child whose token is y and stopping with bonus y when no child holds
-   it (the target's output distribution is kept).  So the sampled step is a per-node draw
-   followed by the greedy acceptance rule applied to the draws.
+   children in index order, accepting child token x with the residual target probability of x
+   and removing x from the residual when it is rejected; the bonus token is then drawn from what
+   is left.  A token already rejected has residual probability 0, so a later sibling holding the
+   same token is never accepted.  The result has the law of one draw y from the target
+   distribution at the node, with the walk descending into the LOWEST-INDEX child whose token is
+   y and stopping with bonus y when no child holds it (the target's output distribution is kept:
+   the token emitted after reaching a node is that node's draw).  So the sampled step is a
+   per-node draw followed by that walk (oracle_sampled_accept).  Choosing among several children
+   holding y by what lies below them (the deepest-path rule of the greedy case) would select
+   between independent draws by their outcomes and change the emitted law.
 
    The draw is the Gumbel-max rule in base 2: with u_v uniform in (0, 1),
        y = argmax_v  z_v * log2(e) / T  -  log2(-log2(u_v)),
@@ -358,11 +375,43 @@ void oracle_node_sample(const void *logits, int32_t dtype, int64_t row_stride, i
     }
 }
 
-/* Greedy acceptance per sequence.
+/* Per-sequence checks shared by both acceptance rules: the tree rule, then (for a well-sized tree)
+   every target token and every compared draft token inside [0, vocab).  Outputs are reset to
+   "nothing accepted" (padding -1, len 0, bonus -1) first. */
+static int32_t accept_prologue(const int32_t *parent, const int32_t *draft, const int32_t *target, int32_t s,
+                               int32_t n, int32_t max_nodes, int32_t vocab, int32_t *path, int32_t *outt,
+                               int32_t *len, int32_t *bonus) {
+    for (int32_t t = 0; t < max_nodes; ++t) path[t] = outt[t] = -1;
+    *len = 0;
+    *bonus = -1;
+    int32_t err = oracle_tree_errors(parent + s, n, max_nodes);
+    if (!(err & 2)) {
+        for (int32_t i = 0; i < n; ++i) {
+            if (target[s + i] < 0 || target[s + i] >= vocab) err |= 4;
+            if (i > 0 && (draft[s + i] < 0 || draft[s + i] >= vocab)) err |= 4;
+        }
+    }
+    return err;
+}
+
+/* The round's outputs once the last accepted node `best` is known: path = anc(best) root first,
+   len = depth(best) + 1, bonus = target[best], out_tokens = drafts of path[1..len-1], bonus. */
+static void accept_emit(const int32_t *parent, const int32_t *draft, const int32_t *target, int32_t s,
+                        int32_t best, int32_t *path, int32_t *outt, int32_t *len, int32_t *bonus) {
+    const int32_t np = oracle_ancestor_path(parent + s, best, path);
+    *len = np;
+    *bonus = target[s + best];
+    for (int32_t t = 1; t < np; ++t) outt[t - 1] = draft[s + path[t]];
+    outt[np - 1] = *bonus;
+}
+
+/* Greedy acceptance per sequence (temperature 0).
    accepted(0) = true; for i >= 1 in index order accepted(i) = accepted(parent(i)) and
    draft[i] == target[parent(i)].  The chosen node i* maximises (depth, -index) over accepted
    nodes; the path is anc(i*) root first; len = depth(i*) + 1; bonus = target[i*];
-   out_tokens = draft of path[1..len-1] followed by the bonus.  Padding is -1. */
+   out_tokens = draft of path[1..len-1] followed by the bonus.  Padding is -1.  (At T = 0 the
+   target tokens are fixed, so taking the deepest of several accepted siblings that hold the same
+   token emits more tokens and changes no token's value.) */
 void oracle_greedy_accept(const int32_t *node_start, const int32_t *parent, const int32_t *draft,
                           const int32_t *target, int32_t batch, int32_t max_nodes, int32_t vocab,
                           int32_t *accept_len, int32_t *accept_path, int32_t *bonus_token,
@@ -372,20 +421,12 @@ void oracle_greedy_accept(const int32_t *node_start, const int32_t *parent, cons
         const int32_t n = node_start[b + 1] - s;
         int32_t *path = accept_path + (size_t)b * max_nodes;
         int32_t *outt = out_tokens + (size_t)b * max_nodes;
-        for (int32_t t = 0; t < max_nodes; ++t) path[t] = outt[t] = -1;
-        accept_len[b] = 0;
-        bonus_token[b] = -1;
-        int32_t err = oracle_tree_errors(parent + s, n, max_nodes);
-        if (!(err & 2)) {
-            for (int32_t i = 0; i < n; ++i) {
-                if (target[s + i] < 0 || target[s + i] >= vocab) err |= 4;
-                if (i > 0 && (draft[s + i] < 0 || draft[s + i] >= vocab)) err |= 4;
-            }
-        }
+        const int32_t err = accept_prologue(parent, draft, target, s, n, max_nodes, vocab, path, outt,
+                                            &accept_len[b], &bonus_token[b]);
         seq_err[b] = err;
         if (err) continue;
-        char acc[1024];
-        int32_t depth[1024];
+        char acc[ORACLE_MAX_NODES];
+        int32_t depth[ORACLE_MAX_NODES];
         acc[0] = 1;
         depth[0] = 0;
         int32_t best = 0;
@@ -395,11 +436,41 @@ void oracle_greedy_accept(const int32_t *node_start, const int32_t *parent, cons
             acc[i] = acc[p] && draft[s + i] == target[s + p];
             if (acc[i] && depth[i] > depth[best]) best = i; /* equal depth keeps the lower index */
         }
-        const int32_t len = oracle_ancestor_path(parent + s, best, path);
-        accept_len[b] = len;
-        bonus_token[b] = target[s + best];
-        for (int32_t t = 1; t < len; ++t) outt[t - 1] = draft[s + path[t]];
-        outt[len - 1] = bonus_token[b];
+        accept_emit(parent, draft, target, s, best, path, outt, &accept_len[b], &bonus_token[b]);
+    }
+}
+
+/* Sampled acceptance per sequence (temperature > 0; target[i] is node i's draw).
+   The walk starts at the root; at node x it enters the lowest-index child c of x with
+   draft[c] == target[x], and stops at x when there is none.  The node where it stops is the
+   last accepted one: path, len, bonus and out_tokens follow from it as in the greedy rule.
+   Arguments, checks and padding are those of oracle_greedy_accept. */
+void oracle_sampled_accept(const int32_t *node_start, const int32_t *parent, const int32_t *draft,
+                           const int32_t *target, int32_t batch, int32_t max_nodes, int32_t vocab,
+                           int32_t *accept_len, int32_t *accept_path, int32_t *bonus_token,
+                           int32_t *out_tokens, int32_t *seq_err) {
+    for (int32_t b = 0; b < batch; ++b) {
+        const int32_t s = node_start[b];
+        const int32_t n = node_start[b + 1] - s;
+        int32_t *path = accept_path + (size_t)b * max_nodes;
+        int32_t *outt = out_tokens + (size_t)b * max_nodes;
+        const int32_t err = accept_prologue(parent, draft, target, s, n, max_nodes, vocab, path, outt,
+                                            &accept_len[b], &bonus_token[b]);
+        seq_err[b] = err;
+        if (err) continue;
+        int32_t x = 0;
+        for (;;) {
+            int32_t next = -1;
+            for (int32_t c = x + 1; c < n; ++c) {
+                if (parent[s + c] == x && draft[s + c] == target[s + x]) {
+                    next = c;
+                    break; /* the first child holding the draw; later siblings are never tried */
+                }
+            }
+            if (next < 0) break;
+            x = next;
+        }
+        accept_emit(parent, draft, target, s, x, path, outt, &accept_len[b], &bonus_token[b]);
     }
 }
 

@@ -116,6 +116,37 @@ def accept_paths(parent, draft, target):
     return len(best), best, bonus, out
 
 
+def sampled_accept_paths(parent, draft, target):
+    """Sampled acceptance from the set of accepted nodes (not a walk): node c is accepted when its
+    parent p is, draft[c] == target[p], and no sibling j < c holds the same drafted token.  The
+    accepted nodes then form one root path (checked); its last node ends the round.
+    Returns (len, path, bonus, out_tokens)."""
+    parent = [int(x) for x in parent]
+    n = len(parent)
+    acc = [False] * n
+    acc[0] = True
+    for c in range(1, n):
+        p = parent[c]
+        first = all(not (parent[j] == p and int(draft[j]) == int(draft[c])) for j in range(1, c))
+        acc[c] = acc[p] and int(draft[c]) == int(target[p]) and first
+    nodes = [i for i in range(n) if acc[i]]
+    for c in nodes[1:]:
+        assert acc[parent[c]], "accepted set is not closed under parents"
+    kids = [sum(1 for c in nodes if c > 0 and parent[c] == u) for u in range(n)]
+    assert max(kids) <= 1, "more than one accepted child of a node"
+    last = max(nodes)
+    path = []
+    j = last
+    while j >= 0:
+        path.append(j)
+        j = parent[j]
+    path = path[::-1]
+    assert path == sorted(nodes), "accepted nodes are not one root path"
+    bonus = int(target[last])
+    out = [int(draft[j]) for j in path[1:]] + [bonus]
+    return len(path), path, bonus, out
+
+
 def load_cases(path: str):
     """Parse a ';'-separated golden file into lists of int lists (first column kept as text)."""
     rows = []

@@ -449,46 +449,152 @@ def pin_sample(lib):
     assert oracle.node_sample(nanrow, 1.0, seed=1, offset=1, lib=lib)[0][0] == 2
 
 
-def pin_sampled_verification_lossless(lib):
-    """Sampled draws followed by the greedy acceptance rule along a draft tree emit tokens with the
-    target's own law (the release note's claim that verification keeps the target's output
-    distribution): on a toy target whose next-token logits depend on the context, the first
-    emitted token follows p(. | prefix), the second follows p(. | prefix, first) whenever the first
-    was a drafted child, the third likewise below that child, and a round ends after one token
-    when the first draw matches no child."""
-    V, T = 5, 1.0
-    rng = np.random.default_rng(17)
+def _toy_target(V, seed, scale=1.3):
+    """A toy target whose next-token logits depend on the whole context (a tuple of tokens)."""
+    rng = np.random.default_rng(seed)
     table = {}
 
     def logits_of(ctx):
         if ctx not in table:
-            table[ctx] = rng.normal(0, 1.3, V).astype(np.float32)
+            table[ctx] = rng.normal(0, scale, V).astype(np.float32)
         return table[ctx]
+    return logits_of
 
-    # root; children tokens 2 (node 1) and 0 (node 2); under node 1: tokens 4 (node 3), 1 (node 4);
-    # under node 2: token 3 (node 5); under node 3: token 4 (node 6)
-    parent = np.array([-1, 0, 0, 1, 1, 2, 3], np.int32)
-    draft = np.array([-1, 2, 0, 4, 1, 3, 4], np.int32)
+
+def _contexts(parent, draft):
     ctx = [()]
     for i in range(1, len(parent)):
         ctx.append(ctx[parent[i]] + (int(draft[i]),))
-    rows = np.stack([logits_of(c) for c in ctx])
+    return ctx
+
+
+# Trees whose siblings repeat tokens (V = 3 forces repeats), plus one with distinct siblings:
+# (parent, draft), draft[0] unused.
+_REPEAT_TREES = (
+    ([-1, 0, 0, 1, 2], [0, 0, 0, 1, 2]),            # root -> {1: 0, 2: 0}, 1 -> {3: 1}, 2 -> {4: 2}
+    ([-1, 0, 0, 0, 1, 3, 3], [0, 1, 1, 1, 2, 0, 0]),  # a triple repeat, then a repeat one level down
+    ([-1, 0, 0, 1, 2, 2], [0, 2, 0, 1, 1, 0]),        # distinct siblings (the walk = the greedy rule)
+    ([-1, 0, 1, 0, 3, 3, 0], [0, 1, 2, 1, 0, 0, 2]),  # repeats at two levels, not in BFS order
+)
+
+
+def pin_sampled_accept(lib):
+    """Sampled acceptance against hand-built cases (tests/golden/sampled_accept_cases.txt), against
+    a set-based brute force on random trees full of repeated sibling tokens, and on data errors."""
+    cases = bf.load_cases(os.path.join(GOLDEN, "sampled_accept_cases.txt"))
+    maxn = max(len(c[1]) for c in cases)
+    for name, parent, draft, target, ln, path, bonus, outt in cases:
+        r = oracle.sampled_accept([0, len(parent)], parent, draft, target, maxn, 1000, lib=lib)
+        assert r["seq_err"][0] == 0, name
+        assert r["accept_len"][0] == ln[0], (name, r["accept_len"][0], ln[0])
+        assert list(r["accept_path"][0][:ln[0]]) == path and (r["accept_path"][0][ln[0]:] == -1).all(), name
+        assert r["bonus"][0] == bonus[0], name
+        assert list(r["out_tokens"][0][:ln[0]]) == outt and (r["out_tokens"][0][ln[0]:] == -1).all(), name
+    ns = np.cumsum([0] + [len(c[1]) for c in cases])
+    r = oracle.sampled_accept(ns, np.concatenate([c[1] for c in cases]), np.concatenate([c[2] for c in cases]),
+                              np.concatenate([c[3] for c in cases]), maxn, 1000, lib=lib)
+    assert list(r["accept_len"]) == [c[4][0] for c in cases]
+    rng = np.random.default_rng(31)
+    for trial in range(300):
+        n = int(rng.integers(1, 24))
+        parent = synth.random_tree(rng, n, max_depth=int(rng.integers(1, 8)))
+        target = rng.integers(0, 3, n).astype(np.int32)
+        draft = rng.integers(0, 3, n).astype(np.int32)
+        r = oracle.sampled_accept([0, n], parent, draft, target, 32, 3, lib=lib)
+        ln, path, bonus, outt = bf.sampled_accept_paths(parent, draft, target)
+        assert r["accept_len"][0] == ln and list(r["accept_path"][0][:ln]) == path, trial
+        assert r["bonus"][0] == bonus and list(r["out_tokens"][0][:ln]) == outt, trial
+    r = oracle.sampled_accept([0, 3, 5, 5, 8], [-1, 0, 2, -1, 0, -1, 0, 1], [0, 1, 2, 0, 1, 0, 1, 1000],
+                              [1, 1, 1, 1, 1, 1, 1, 1], 4, 1000, lib=lib)
+    assert list(r["seq_err"]) == [1, 0, 2, 4], list(r["seq_err"])
+    assert list(r["accept_len"]) == [0, 2, 0, 0]
+
+
+def pin_sampled_accept_exact_law(lib):
+    """The emitted tokens have exactly the target's law (the pages' claim that verification keeps
+    the target's output distribution), computed without sampling: every assignment of draws to
+    the nodes of a small tree is enumerated with its probability (each node's draw follows the
+    toy target at that node's context), the round's tokens come from the oracle's sampled
+    acceptance, and for every emitted position j and history h the conditional law of token j
+    given (tokens 1..j-1 = h, at least j tokens emitted) must equal the target's p(. | h) to
+    rounding.  Trees with repeated sibling tokens are included."""
+    import itertools
+    V, T = 3, 1.0
+    logits_of = _toy_target(V, 23, scale=1.1)
+    rng = np.random.default_rng(41)
+    trees = list(_REPEAT_TREES)
+    for _ in range(4):  # random trees with forced repeats (three tokens)
+        n = int(rng.integers(4, 8))
+        trees.append((list(synth.random_tree(rng, n, max_depth=3)), [0] + list(rng.integers(0, V, n - 1))))
+    for parent, draft in trees:
+        n = len(parent)
+        ctx = _contexts(parent, draft)
+        probs = [_softmax(logits_of(c).astype(np.float64) / T) for c in ctx]
+        combos = np.array(list(itertools.product(range(V), repeat=n)), np.int32)
+        weight = np.ones(len(combos))
+        for i in range(n):
+            weight *= probs[i][combos[:, i]]
+        M = len(combos)
+        r = oracle.sampled_accept(np.arange(M + 1, dtype=np.int32) * n, np.tile(parent, M),
+                                  np.tile(np.asarray(draft, np.int32), M), combos.reshape(-1), n, V, lib=lib)
+        out, ln = r["out_tokens"], r["accept_len"]
+        assert (r["seq_err"] == 0).all()
+        mass = {}  # (history, next token) -> probability
+        for k in range(M):
+            toks = tuple(int(x) for x in out[k, :ln[k]])
+            for j in range(len(toks)):
+                key = (toks[:j], toks[j])
+                mass[key] = mass.get(key, 0.0) + weight[k]
+        hists = {h for h, _ in mass}
+        for h in hists:
+            row = np.array([mass.get((h, y), 0.0) for y in range(V)])
+            want = _softmax(logits_of(h).astype(np.float64) / T)
+            assert np.allclose(row / row.sum(), want, rtol=0, atol=1e-12), \
+                (parent, draft, h, (row / row.sum()).tolist(), want.tolist())
+
+
+def pin_sampled_verification_lossless(lib):
+    """End to end through the draw: Philox Gumbel-max draws at every node followed by the sampled
+    acceptance emit tokens with the target's own law (chi-square).  On a toy target whose
+    next-token logits depend on the context, the first emitted token follows p(. | prefix), the
+    second follows p(. | prefix, first) whenever the first was a drafted child, the third likewise;
+    the trees include siblings that repeat a token."""
+    V, T = 5, 1.0
+    logits_of = _toy_target(V, 17)
+    trees = [
+        # distinct siblings: root -> {1: 2, 2: 0}, 1 -> {3: 4, 4: 1}, 2 -> {5: 3}, 3 -> {6: 4}
+        ([-1, 0, 0, 1, 1, 2, 3], [-1, 2, 0, 4, 1, 3, 4]),
+        # repeated siblings: root -> {1: 0, 2: 0}, 1 -> {3: 1}, 2 -> {4: 2}
+        ([-1, 0, 0, 1, 2], [0, 0, 0, 1, 2]),
+        # repeats at two levels: root -> {1: 3, 2: 3, 3: 1}, 1 -> {4: 2, 5: 2}, 2 -> {6: 0}, 3 -> {7: 4}
+        ([-1, 0, 0, 0, 1, 1, 2, 3], [0, 3, 3, 1, 2, 2, 0, 4]),
+    ]
     M = 40000
-    n = len(parent)
-    logits = np.tile(rows, (M, 1))
-    tok, _ = oracle.node_sample(logits, T, seed=99, offset=5, lib=lib)
-    node_start = np.arange(M + 1, dtype=np.int32) * n
-    acc = oracle.greedy_accept(node_start, np.tile(parent, M), np.tile(np.maximum(draft, 0), M), tok, n, V, lib=lib)
-    out, ln = acc["out_tokens"], acc["accept_len"]
-    first = out[:, 0]
-    _chi2_ok(np.bincount(first, minlength=V), _softmax(rows[0] / T), "first token")
-    assert (ln[~np.isin(first, (2, 0))] == 1).all()
-    for f, node in ((2, 1), (0, 2)):
-        sel = first == f
-        assert (ln[sel] >= 2).all()
-        _chi2_ok(np.bincount(out[sel, 1], minlength=V), _softmax(rows[node] / T), f"second token after {f}")
-    sel = (first == 2) & (out[:, 1] == 4)
-    _chi2_ok(np.bincount(out[sel, 2], minlength=V), _softmax(rows[3] / T), "third token after (2, 4)")
+    for ti, (parent, draft) in enumerate(trees):
+        parent = np.array(parent, np.int32)
+        draft = np.maximum(np.array(draft, np.int32), 0)
+        n = len(parent)
+        rows = np.stack([logits_of(c) for c in _contexts(parent, draft)])
+        tok, _ = oracle.node_sample(np.tile(rows, (M, 1)), T, seed=99, offset=5 + ti, lib=lib)
+        acc = oracle.sampled_accept(np.arange(M + 1, dtype=np.int32) * n, np.tile(parent, M), np.tile(draft, M),
+                                    tok, n, V, lib=lib)
+        out, ln = acc["out_tokens"], acc["accept_len"]
+        # chi-square of every emitted position's law for every history seen at least 2000 times
+        seen = {}
+        for k in range(M):
+            toks = tuple(int(x) for x in out[k, :ln[k]])
+            for j in range(len(toks)):
+                seen.setdefault(toks[:j], []).append(toks[j])
+        tested = 0
+        for h, ys in sorted(seen.items(), key=lambda kv: -len(kv[1])):
+            if len(ys) < 2000:
+                continue
+            _chi2_ok(np.bincount(ys, minlength=V), _softmax(logits_of(h).astype(np.float64) / T),
+                     f"tree {ti} token after {h}")
+            tested += 1
+        assert tested >= 2 and (ti != 1 or len(seen.get((0,), ())) >= 2000), (ti, tested)
 
 
-ALL_PINS = ALL_PINS + (pin_sample, pin_sampled_verification_lossless)
+ALL_PINS = ALL_PINS + (pin_sample, pin_sampled_accept, pin_sampled_accept_exact_law,
+                       pin_sampled_verification_lossless)
+

@@ -60,8 +60,9 @@ def _separate(d, k, v, c, temperature, seed, offset, block_table=None):
         tgt, _ = ev.node_sample(d["logits"], temperature=temperature, seed=seed, offset=offset, vocab=c["vocab"])
     else:
         tgt, _, _ = ev.node_argmax(d["logits"], vocab=c["vocab"])
-    acc = ev.greedy_accept(d["node_start"], d["parent"], d["draft"], tgt, max_nodes=c["max_nodes"],
-                           vocab=c["vocab"], err_flag=err)
+    accept = ev.sampled_accept if temperature > 0 else ev.greedy_accept
+    acc = accept(d["node_start"], d["parent"], d["draft"], tgt, max_nodes=c["max_nodes"], vocab=c["vocab"],
+                 err_flag=err)
     if block_table is None:
         nl = ev.compact_kv(k, v, d["kv_start"], d["prefix_len"], acc["accept_len"], acc["accept_path"], err_flag=err)
     else:
@@ -111,7 +112,8 @@ def _run(c, temperature=0.0, seed=0, offset=0, p_agree=0.8, what=""):
     assert gu.to_host(k1).tobytes() == gu.to_host(k2).tobytes(), f"{what}: K caches"
     assert gu.to_host(v1).tobytes() == gu.to_host(v2).tobytes(), f"{what}: V caches"
     tgt = fus[0].cpu().numpy()
-    r = oracle.greedy_accept(c["node_start"], c["parent"], draft, tgt, c["max_nodes"], c["vocab"])
+    accept = oracle.sampled_accept if temperature > 0 else oracle.greedy_accept
+    r = accept(c["node_start"], c["parent"], draft, tgt, c["max_nodes"], c["vocab"])
     for key in ("accept_len", "accept_path", "bonus", "out_tokens"):
         assert np.array_equal(fus[1][key].cpu().numpy(), r[key]), f"{what}: oracle {key}"
     layers, slots, H, D = c["k"].shape

@@ -96,8 +96,8 @@ def test_law_and_noise():
 
 
 def test_sampled_step_matches_oracle():
-    """Draws plus greedy acceptance on the 8-sequence workload: acceptance, path, bonus and tokens
-    bit-exact against the oracle's draws plus the oracle's acceptance."""
+    """Draws plus sampled acceptance on the 8-sequence workload: acceptance, path, bonus and tokens
+    bit-exact against the oracle's sampled acceptance of the same draws."""
     import torch
     from draft_tree_verification_amd import ev
     gu.log("[case] sampled step c8")
@@ -105,12 +105,12 @@ def test_sampled_step_matches_oracle():
     d = gu.dev_workload(w)
     for T, off in ((1.0, 11), (0.3, 12)):
         tgt, _ = ev.node_sample(d["logits"], temperature=T, seed=2024, offset=off)
-        acc = ev.greedy_accept(d["node_start"], d["parent"], d["draft"], tgt, max_nodes=w.max_nodes, vocab=w.vocab)
+        acc = ev.sampled_accept(d["node_start"], d["parent"], d["draft"], tgt, max_nodes=w.max_nodes, vocab=w.vocab)
         torch.cuda.synchronize()
         draws = tgt.cpu().numpy()
         # the draws against the oracle's (near ties aside), then acceptance on those same draws
         assert np.array_equal(draws, _check_draws(w.logits, T, 2024, off, what=f"step T={T}"))
-        ref = oracle.greedy_accept(w.node_start, w.parent, w.draft, draws, w.max_nodes, w.vocab)
+        ref = oracle.sampled_accept(w.node_start, w.parent, w.draft, draws, w.max_nodes, w.vocab)
         for k in ("accept_len", "accept_path", "bonus", "out_tokens"):
             assert np.array_equal(acc[k].cpu().numpy(), ref[k]), k
 

@@ -1,4 +1,5 @@
-"""GPU parity of ev_node_argmax, ev_greedy_accept and ev_compact_kv: bit-exact against the oracle."""
+"""GPU parity of ev_node_argmax, ev_greedy_accept, ev_sampled_accept and ev_compact_kv: bit-exact
+against the oracle."""
 import os
 
 import numpy as np
@@ -107,20 +108,21 @@ def test_argmax_full_rounds_placements(rows, vocab):
     _check_argmax(raw, what=f"placements {rows}x{vocab}")
 
 
-def _gpu_accept(node_start, parent, draft, target, max_nodes, vocab):
+def _gpu_accept(node_start, parent, draft, target, max_nodes, vocab, sampled=False):
     import torch
     from draft_tree_verification_amd import ev
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    out = ev.greedy_accept(t(node_start), t(parent), t(draft), t(target), max_nodes=max_nodes, vocab=vocab,
-                           err_flag=err)
+    fn = ev.sampled_accept if sampled else ev.greedy_accept
+    out = fn(t(node_start), t(parent), t(draft), t(target), max_nodes=max_nodes, vocab=vocab, err_flag=err)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}, int(err.item())
 
 
-def _check_accept(node_start, parent, draft, target, max_nodes, vocab, what=""):
-    g, err = _gpu_accept(node_start, parent, draft, target, max_nodes, vocab)
-    r = oracle.greedy_accept(node_start, parent, draft, target, max_nodes, vocab)
+def _check_accept(node_start, parent, draft, target, max_nodes, vocab, what="", sampled=False):
+    g, err = _gpu_accept(node_start, parent, draft, target, max_nodes, vocab, sampled)
+    r = (oracle.sampled_accept if sampled else oracle.greedy_accept)(node_start, parent, draft, target, max_nodes,
+                                                                      vocab)
     for k in ("accept_len", "accept_path", "bonus", "out_tokens"):
         assert np.array_equal(g[k], r[k]), f"{what}: {k} differs"
     flags = int(np.bitwise_or.reduce(r["seq_err"])) if len(r["seq_err"]) else 0
@@ -157,10 +159,53 @@ def test_accept_workloads(name):
     _check_accept(w.node_start, w.parent, w.draft, tgt, w.max_nodes, w.vocab, what=name)
 
 
-def test_accept_data_errors():
-    gu.log("[case] accept data errors")
+@pytest.mark.parametrize("sampled", [False, True], ids=["greedy", "sampled"])
+def test_accept_data_errors(sampled):
+    gu.log(f"[case] accept data errors sampled={sampled}")
     _check_accept([0, 3, 5, 5, 8, 9], [-1, 0, 2, -1, 0, -1, 0, 1, -1], [0, 1, 2, 0, 1, 0, 1, 1000, 3],
-                  [1, 1, 1, 1, 1, 1, 1, 1, 1000], 4, 1000, what="errors")
+                  [1, 1, 1, 1, 1, 1, 1, 1, 1000], 4, 1000, what="errors", sampled=sampled)
+
+
+def test_sampled_accept_golden_cases():
+    """The first-child rule of sampled verification on the hand-built cases, including repeated
+    sibling tokens whose later sibling leads deeper (never entered)."""
+    gu.log("[case] sampled accept golden")
+    cases = bf.load_cases(os.path.join(GOLDEN, "sampled_accept_cases.txt"))
+    ns = np.cumsum([0] + [len(c[1]) for c in cases])
+    g = _check_accept(ns, np.concatenate([c[1] for c in cases]), np.concatenate([c[2] for c in cases]),
+                      np.concatenate([c[3] for c in cases]), 8, 1000, what="sampled golden", sampled=True)
+    for b, c in enumerate(cases):
+        assert g["accept_len"][b] == c[4][0] and list(g["accept_path"][b][:c[4][0]]) == c[5], c[0]
+        assert g["bonus"][b] == c[6][0] and list(g["out_tokens"][b][:c[4][0]]) == c[7], c[0]
+
+
+@pytest.mark.parametrize("vocab", [2, 3, 50])
+def test_sampled_accept_random_repeats(vocab):
+    """700 random trees of 1-64 nodes whose drafted tokens repeat among siblings (vocabulary of 2
+    or 3 forces it): the GPU's first-child rule equals the oracle's walk bit for bit, and differs
+    from the greedy rule on some trees."""
+    gu.log(f"[case] sampled accept random vocab={vocab}")
+    rng = np.random.default_rng(100 + vocab)
+    B = 700
+    trees = [synth.random_tree(rng, int(rng.integers(1, 65)), int(rng.integers(1, 64))) for _ in range(B)]
+    ns = np.cumsum([0] + [len(t) for t in trees])
+    T = int(ns[-1])
+    draft, target = rng.integers(0, vocab, T), rng.integers(0, vocab, T)
+    gs = _check_accept(ns, np.concatenate(trees), draft, target, 64, vocab, what=f"sampled v{vocab}", sampled=True)
+    gg = _check_accept(ns, np.concatenate(trees), draft, target, 64, vocab, what=f"greedy v{vocab}")
+    if vocab <= 3:
+        assert (gs["accept_len"] != gg["accept_len"]).any(), "no tree separates the two rules"
+
+
+def test_sampled_accept_workload_draws():
+    """Sampled acceptance on the 8- and 512-sequence workloads' trees with the oracle's draws as
+    targets (planted drafts repeat the parent's token among siblings)."""
+    for name, T in (("c8", 1.0), ("c512", 0.7)):
+        gu.log(f"[case] sampled accept {name}")
+        w = gu.cached_config(name)
+        tgt, _ = oracle.node_sample(w.logits, T, 7, 3)
+        _check_accept(w.node_start, w.parent, w.draft, tgt, w.max_nodes, w.vocab, what=f"sampled {name}",
+                      sampled=True)
 
 
 def _gpu_compact(k, v, kv_start, prefix_len, lens, path):

@@ -97,7 +97,7 @@ def test_verify_step_sampled(T):
         s_g = oracle.sample_score(float(z[r, draws[r]]), T, 31, 4, int(r), int(draws[r]))
         assert s_g >= float(ref_score[r]) - 1e-5 - 8 * np.spacing(np.float32(max(1.0, abs(float(ref_score[r]))))), r
     assert len(bad) <= 1
-    r = oracle.greedy_accept(w.node_start, w.parent, w.draft, draws, w.max_nodes, w.vocab)
+    r = oracle.sampled_accept(w.node_start, w.parent, w.draft, draws, w.max_nodes, w.vocab)
     for key in ("accept_len", "accept_path", "bonus", "out_tokens"):
         assert np.array_equal(st["accept"][key].cpu().numpy(), r[key]), key
     kx, vx, nl, err = oracle.compact_kv(w.k[None], w.v[None], w.kv_start, w.prefix_len, r["accept_len"],

@@ -13,9 +13,8 @@ import oracle
 from . import pins
 
 MUTANTS = {
-    "self_not_in_ancestors": ("for (int32_t j = i; j >= 0; j = parent[j]) rev[n++] = j;",
-                              "for (int32_t j = parent[i]; j >= 0; j = parent[j]) rev[n++] = j;\n"
-                              "    if (n == 0) rev[n++] = i;"),
+    "self_not_in_ancestors": ("for (int32_t j = i; j >= 0; j = parent[j]) {",
+                              "if (i == 0) rev[n++] = 0;\n    for (int32_t j = parent[i]; j >= 0; j = parent[j]) {"),
     "gqa_modulo_mapping": ("const int32_t g = h / G;", "const int32_t g = h % hkv;"),
     "prefix_off_by_one": ("for (int32_t t = t0; t < L; ++t) slots[nvis++] = token_slot(",
                           "for (int32_t t = t0 + 1; t < L; ++t) slots[nvis++] = token_slot("),
@@ -54,7 +53,16 @@ MUTANTS = {
                                  "acc[i] = draft[s + i] == target[s + p];"),
     "accept_own_target": ("acc[i] = acc[p] && draft[s + i] == target[s + p];",
                           "acc[i] = acc[p] && draft[s + i] == target[s + i];"),
-    "bonus_from_root": ("bonus_token[b] = target[s + best];", "bonus_token[b] = target[s];"),
+    "bonus_from_root": ("*bonus = target[s + best];", "*bonus = target[s];"),
+    # sampled acceptance: the deepest-path rule of the greedy case applied to the draws, and the
+    # last (not the first) child holding the draw
+    "sampled_accept_deepest_rule": (
+        "                           int32_t *out_tokens, int32_t *seq_err) {\n",
+        "                           int32_t *out_tokens, int32_t *seq_err) {\n"
+        "    oracle_greedy_accept(node_start, parent, draft, target, batch, max_nodes, vocab, accept_len,\n"
+        "                         accept_path, bonus_token, out_tokens, seq_err);\n"
+        "    if (batch >= 0) return;\n"),
+    "sampled_accept_last_child": ("next = c;\n                    break;", "next = c;"),
     "compact_descending_in_place": (
         "            for (int32_t t = 0; t < len; ++t) {\n"
         "                const size_t dst = lo + (size_t)(base + t) * row;\n"
