@@ -234,19 +234,22 @@ constexpr int kSeqUnits = EV_MAX_BATCH / 2 + kAlignedMaxBatch;
 
 // Per-sequence stage counts of the whole batch and their inclusive scan into s_cum (identical
 // in every workgroup); returns the total stage count.  Sequences with bad geometry get no stages
-// and raise their error bit once.
+// and raise their error bit once.  The scan runs in 64 bits: a batch whose total reaches 2^31
+// stages (only possible when sequences share slot ranges, which the host's bound from
+// total_slots does not see) raises EV_DATA_BAD_SLOTS and gets no stages at all, so the 32-bit
+// prefix sums in s_cum never wrap.
 template <int R, int KST>
-__device__ __forceinline__ int64_t schedule_scan(const AttnArgs &a, int32_t *s_cum, int32_t *s_misc) {
+__device__ __forceinline__ int64_t schedule_scan(const AttnArgs &a, int32_t *s_cum, int64_t *s_misc) {
     constexpr int NT = kThreads;
     constexpr int NW = kWaves;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int G = a.group;
-    int carry = 0;
+    int64_t carry = 0;
     for (int b0 = 0; b0 < a.batch; b0 += NT) {
         const int b = b0 + tid;
-        int work = 0;
+        int64_t work = 0;
         if (b < a.batch) {
             const int ns0 = a.node_start[b], ns1 = a.node_start[b + 1];
             const int n = ns1 - ns0;
@@ -262,30 +265,34 @@ __device__ __forceinline__ int64_t schedule_scan(const AttnArgs &a, int32_t *s_c
                 if (blockIdx.x == 0) ev::flag_error(a.err_flag, err);
             } else {
                 const int Lv = (a.window > 0 && L > a.window) ? a.window : L;
-                st = (Lv + n + KST - 1) / KST;
+                st = static_cast<int>((static_cast<int64_t>(Lv) + n + KST - 1) / KST);
                 units = a.hkv * ((n * G + R - 1) / R);
-                work = units * st;
+                work = static_cast<int64_t>(units) * st;
             }
             if (a.batch <= kAlignedMaxBatch) {
                 s_cum[kSeqStages + b] = st;
                 s_cum[kSeqUnits + b] = units;
             }
         }
-        int x = work;
+        int64_t x = work;
         for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(x, o, 64);
+            const int64_t y = __shfl_up(x, o, 64);
             if (lane >= o) x += y;
         }
         if (lane == 63) s_misc[wave] = x;
         __syncthreads();
-        int wbase = 0, tot = 0;
+        int64_t wbase = 0, tot = 0;
         for (int w = 0; w < NW; ++w) {
             if (w < wave) wbase += s_misc[w];
             tot += s_misc[w];
         }
-        if (b < a.batch) s_cum[b] = carry + wbase + x;
+        if (b < a.batch) s_cum[b] = static_cast<int32_t>(min(carry + wbase + x, static_cast<int64_t>(INT32_MAX)));
         carry += tot;
         __syncthreads();
+    }
+    if (carry > INT32_MAX) {
+        if (blockIdx.x == 0 && tid == 0) ev::flag_error(a.err_flag, EV_DATA_BAD_SLOTS);
+        return 0;
     }
     return carry;
 }
@@ -342,7 +349,7 @@ __device__ __forceinline__ PieceMap map_pieces(const AttnArgs &a, const int32_t 
     PieceMap m{};
     m.k = -1;
     const int lane = threadIdx.x & 63;
-    if (a.batch <= kAlignedMaxBatch) {
+    if (S > 0 && a.batch <= kAlignedMaxBatch) {
         const int st = lane < a.batch ? s_cum[kSeqStages + lane] : 0;
         const int units = lane < a.batch ? s_cum[kSeqUnits + lane] : 0;
         const int utot = wave_sum(units);
@@ -392,8 +399,8 @@ __device__ __forceinline__ PieceMap map_pieces(const AttnArgs &a, const int32_t 
         m.k = 0;
         wl = (grid % 8 == 0) ? (blockIdx.x % 8) * (grid / 8) + blockIdx.x / 8 : blockIdx.x;
         m.P = static_cast<int>(S < grid ? S : grid);  // never more than stages: every range non-empty
-        m.begin = S * wl / m.P;
-        m.end = S * (wl + 1) / m.P;
+        m.begin = m.P ? S * wl / m.P : 0;              // (no stages: no workgroup has work)
+        m.end = m.P ? S * (wl + 1) / m.P : 0;
     }
     // uniform values: scalar registers and scalar branches in the piece loop
     m.begin = uniform64(m.begin);
@@ -423,7 +430,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::kTotal];
     int32_t *s_cum = reinterpret_cast<int32_t *>(smem);
-    int32_t *s_misc = reinterpret_cast<int32_t *>(smem + Lay::kScan);
+    int64_t *s_misc = reinterpret_cast<int64_t *>(smem + Lay::kScan);
     unsigned char *stage_buf = smem + Lay::kScan + Lay::kMisc;
 
     const int tid = threadIdx.x;
@@ -1068,7 +1075,7 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::kTotal];
     int32_t *s_cum = reinterpret_cast<int32_t *>(smem);
-    int32_t *s_misc = reinterpret_cast<int32_t *>(smem + Lay::kScan);
+    int64_t *s_misc = reinterpret_cast<int64_t *>(smem + Lay::kScan);
     unsigned char *pbufs = smem + Lay::kScan + Lay::kMisc;               // [wave][64] int32 parents
     unsigned char *qbuf = pbufs + Lay::kPar;                             // [80 rows][D] bf16
     unsigned char *bufs = qbuf + Lay::kQ;

@@ -187,3 +187,30 @@ def test_data_errors_skip_sequence():
                       max_nodes=3, sm_scale=w.sm_scale, out=out, err_flag=err)
     torch.cuda.synchronize()
     assert int(err.item()) & ev.DATA_BAD_NODES
+
+
+def test_stage_total_beyond_int32_is_flagged():
+    """2048 one-node sequences that all share one slot range of 2^25 prefix tokens: the host's bound
+    (from total_slots) passes, but the batch's total stage count exceeds 2^31.  The call raises
+    EV_DATA_BAD_SLOTS and writes no row, instead of wrapping its 32-bit stage prefix sums."""
+    import torch
+    from draft_tree_verification_amd import ev
+    gu.log("[case] attention stage total beyond 2^31")
+    B, L, D = 2048, 1 << 25, 64
+    slots = L + 1
+    k = torch.zeros((slots, 1, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    q = torch.zeros((B, 1, D), dtype=torch.bfloat16, device="cuda")
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    node_start = i32(list(range(B + 1)))
+    parent = i32([-1] * B)
+    kv_start = i32([0] * B)
+    prefix_len = i32([L] * B)
+    out = torch.full_like(q, float("nan"))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ev.tree_attention(q, k, v, node_start, parent, kv_start, prefix_len, max_nodes=1, sm_scale=0.125, out=out,
+                      err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == ev.DATA_BAD_SLOTS
+    assert torch.isnan(out.float()).all()
+    del k, v
