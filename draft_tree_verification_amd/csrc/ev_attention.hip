@@ -1638,6 +1638,14 @@ struct Plan {
     size_t bytes;
 };
 
+// Largest workspace any supported shape needs: the table plus 2 * kMaxGrid slots of 80-row,
+// 128-wide partials (the plan below depends on the row tile and head_dim, never on the batch):
+// 42,606,592 bytes.
+constexpr size_t kMaxWorkspaceBytes =
+    static_cast<size_t>(kMaxGrid) * sizeof(int4) +
+    2 * static_cast<size_t>(kMaxGrid) * (static_cast<size_t>(16 * kMaxRowTiles) * 128 + 2 * 16 * kMaxRowTiles) * 4;
+static_assert(kMaxWorkspaceBytes == 42606592, "the header states this size");
+
 Plan make_plan(int32_t batch, int32_t max_nodes, int32_t hq, int32_t hkv, int32_t head_dim) {
     Plan p{};
     const int G = hq / hkv;
@@ -1702,6 +1710,35 @@ extern "C" size_t ev_tree_attention_workspace_size(int32_t batch, int32_t max_no
     return make_plan(batch, max_nodes, num_q_heads, num_kv_heads, head_dim).bytes;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Allocation-free form of ev_tree_attention.  Its workspace is this file-scope device array: one
+// copy per GPU the library runs on, held until the process ends.  In host code the array's name
+// stands for a host-side shadow, not a device address, so the device address is looked up once
+// per device (hipGetSymbolAddress, with that device current) and only that pointer reaches the
+// kernels.  Every call on a GPU shares its copy: calls that overlap on one GPU (different
+// streams, or other host threads) race on it; calls ordered on one stream do not.  The attention
+// launches write every part of the workspace they later read, so nothing needs clearing.
+static __device__ __align__(256) unsigned char scratch[kMaxWorkspaceBytes];  // 42,606,592 bytes
+
+namespace {
+constexpr int kScratchDevices = 16;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices];
+
+ev_status scratch_of_current_device(void **ptr) {
+    const int dev = ev::current_device();
+    if (dev < 0 || dev >= kScratchDevices) return EV_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return EV_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return EV_OK;
+}
+}  // namespace
+
 namespace {
 ev_status launch_attention(const void *q, const void *k_cache, const void *v_cache, void *out, float *lse,
                            const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
@@ -1709,7 +1746,7 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
                            int64_t total_slots, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                            ev_dtype dtype, float sm_scale, int32_t window, const int32_t *block_table,
                            int32_t bt_stride, int32_t page_size, void *workspace, size_t workspace_bytes,
-                           int32_t *err_flag, hipStream_t stream) {
+                           int32_t *err_flag, hipStream_t stream, bool use_scratch = false) {
     const bool pg = page_size > 0;  // paged caches: total_slots = pool pages * page_size
     if (!q || !k_cache || !v_cache || !out || !node_start || !parent || !prefix_len || (pg ? !block_table : !kv_start))
         return EV_ERR_NULL;
@@ -1722,8 +1759,12 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
     if (!ev::aligned16(q) || !ev::aligned16(k_cache) || !ev::aligned16(v_cache) || !ev::aligned16(out))
         return EV_ERR_ALIGN;
     const Plan plan = make_plan(batch, max_nodes, num_q_heads, num_kv_heads, head_dim);
-    if (!workspace || workspace_bytes < plan.bytes) return EV_ERR_WORKSPACE;
-    if (!ev::aligned16(workspace)) return EV_ERR_ALIGN;
+    if (use_scratch) {
+        if (plan.bytes > kMaxWorkspaceBytes) return EV_ERR_WORKSPACE;  // beyond the static scratch
+    } else {
+        if (!workspace || workspace_bytes < plan.bytes) return EV_ERR_WORKSPACE;
+        if (!ev::aligned16(workspace)) return EV_ERR_ALIGN;
+    }
     // stage counts are 32-bit in the kernel (32-key stages bound them from above); token indices
     // of paged sequences are 32-bit
     const int64_t max_tokens = pg ? static_cast<int64_t>(bt_stride) * page_size * batch : total_slots;
@@ -1732,6 +1773,10 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
     if (pg && static_cast<int64_t>(bt_stride) * page_size >= (int64_t(1) << 31)) return EV_ERR_SHAPE;
     const ev_status dev = ev::check_device();
     if (dev != EV_OK) return dev;
+    if (use_scratch) {  // this device's copy of the static scratch (no allocation)
+        const ev_status st = scratch_of_current_device(&workspace);
+        if (st != EV_OK) return st;
+    }
     if (batch == 0 || total_nodes == 0) return EV_OK;
 
     const bool f32 = dtype == EV_F32;
@@ -1798,6 +1843,18 @@ extern "C" ev_status ev_tree_attention(const void *q, const void *k_cache, const
     return launch_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
                             total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype,
                             sm_scale, 0, nullptr, 0, 0, workspace, workspace_bytes, err_flag, stream);
+}
+
+extern "C" ev_status ev_tree_attention_noalloc(const void *q, const void *k_cache, const void *v_cache, void *out,
+                                               float *lse, const int32_t *node_start, const int32_t *parent,
+                                               const int32_t *kv_start, const int32_t *prefix_len, int32_t batch,
+                                               int32_t total_nodes, int32_t max_nodes, int64_t total_slots,
+                                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                               ev_dtype dtype, float sm_scale, int32_t *err_flag,
+                                               hipStream_t stream) {
+    return launch_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
+                            total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype,
+                            sm_scale, 0, nullptr, 0, 0, nullptr, 0, err_flag, stream, true);
 }
 
 extern "C" ev_status ev_tree_attention_window(const void *q, const void *k_cache, const void *v_cache, void *out,

@@ -29,7 +29,7 @@ EXPORTS = ("ev_status_string", "ev_tree_attention_workspace_size", "ev_tree_atte
            "ev_node_argmax", "ev_node_sample", "ev_greedy_accept", "ev_sampled_accept", "ev_compact_kv",
            "ev_compact_kv_paged",
            "ev_select_workspace_size", "ev_select_accept_compact", "ev_select_accept_compact_paged",
-           "ev_stream_read")
+           "ev_stream_read", "ev_tree_attention_noalloc")
 
 _lib = None
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -91,6 +91,9 @@ def load(path: str = LIB_PATH):
     lib.ev_select_accept_compact_paged.argtypes = [_P, ctypes.c_int, _I64, _I32, _F, _U64, _U64, _P, _P, _P, _I32,
                                                    _I32, _I32, _P, _P, _I32, _I32, _I64, _P, _I32, _I32, _P, _I32,
                                                    _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
+    lib.ev_tree_attention_noalloc.restype = ctypes.c_int
+    lib.ev_tree_attention_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32,
+                                              _I32, _I32, ctypes.c_int, _F, _P, _P]
     lib.ev_stream_read.restype = ctypes.c_int
     lib.ev_stream_read.argtypes = [_P, _SZ, _P, _P]
     if path == LIB_PATH:
@@ -113,6 +116,14 @@ def ev_tree_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_star
     return load().ev_tree_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
                                     total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype,
                                     sm_scale, workspace, workspace_bytes, err_flag, stream)
+
+
+def ev_tree_attention_noalloc(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
+                              total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype,
+                              sm_scale, err_flag, stream) -> int:
+    return load().ev_tree_attention_noalloc(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len,
+                                            batch, total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads,
+                                            head_dim, dtype, sm_scale, err_flag, stream)
 
 
 def ev_tree_attention_window(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,

@@ -181,6 +181,26 @@ ev_status ev_tree_attention_paged(const void *q, const void *k_pages, const void
                                   hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * ev_tree_attention_noalloc
+ *
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): ev_tree_attention with the same arguments, results
+ * and errors, minus the workspace, which is a static device array inside the library of
+ * 42,606,592 bytes (the largest workspace any supported shape needs, so every shape that
+ * ev_tree_attention accepts is accepted; a shape needing more would return EV_ERR_WORKSPACE).
+ * Each GPU the library runs on holds its own copy of that array from the first call on that
+ * device until the process ends.  The call allocates nothing and frees nothing.  All calls on
+ * one GPU share its copy: calls ordered on one stream are safe, calls that overlap on one GPU
+ * (other streams, other host threads) race on it and give wrong results.
+ * -------------------------------------------------------------------------------------------*/
+ev_status ev_tree_attention_noalloc(const void *q, const void *k_cache, const void *v_cache, void *out, float *lse,
+                                    const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                                    const int32_t *prefix_len, int32_t batch, int32_t total_nodes,
+                                    int32_t max_nodes, int64_t total_slots, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, ev_dtype dtype, float sm_scale,
+                                    int32_t *err_flag, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * ev_node_argmax
  *
  * target_token[r] = the LOWEST index v in [0, vocab) holding the maximum of logits row r (the

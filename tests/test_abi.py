@@ -76,6 +76,13 @@ def test_host_argument_checks_need_no_gpu(lib):
     assert ev.ev_node_argmax(P, 0, 12, 1, 8, P, None, None, 0, None) == 4       # 24-byte rows
     assert ev.ev_node_argmax(P, 2, 8, 1, 8, P, None, None, 0, None) == 3
     assert ev.ev_node_argmax(P, 0, 151936, 16, 151936, P, None, None, 0, None) == 5
+    # the allocation-free attention call checks its arguments before it looks for a device
+    assert ev.ev_tree_attention_noalloc(None, P, P, P, None, P, P, P, P, 1, 4, 4, 100, 8, 2, 64, 0, 0.1, None,
+                                        None) == 1
+    assert ev.ev_tree_attention_noalloc(P, P, P, P, None, P, P, P, P, 1, 4, 65, 100, 8, 2, 64, 0, 0.1, None,
+                                        None) == 2
+    assert ev.ev_tree_attention_noalloc(P, P, P, P, None, P, P, P, P, 1, 4, 4, 100, 8, 2, 64, 5, 0.1, None,
+                                        None) == 3
     assert ev.ev_greedy_accept(P, P, P, None, 1, 4, 4, 10, P, P, P, P, None, None) == 1
     assert ev.ev_greedy_accept(P, P, P, P, 1, 4, 65, 10, P, P, P, P, None, None) == 2
     assert ev.ev_compact_kv(P, P, 3, 1, 4096, P, P, P, P, 1, 4, 16, 8, 128, P + 64, None, None) == 3
