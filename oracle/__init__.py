@@ -122,10 +122,12 @@ def tree_errors(parent, max_nodes: int, lib=None) -> int:
 
 
 def ancestor_path(parent, i: int, lib=None) -> np.ndarray:
+    """Ancestors of node i, itself included, root first; empty when the chain is malformed or i is
+    beyond the oracle's work arrays."""
     parent = _i32(parent)
-    out = np.zeros(max(len(parent), 1), dtype=np.int32)
+    out = np.zeros(max(len(parent), MAX_NODES, 1), dtype=np.int32)
     n = (lib or load()).oracle_ancestor_path(_ptr(parent), int(i), _ptr(out))
-    return out[:n].copy()
+    return out[:max(n, 0)].copy()
 
 
 def _layout(kv_start, block_table, page_size):
