@@ -73,6 +73,17 @@ def oracle_attention(w, sm_scale=None, window=0):
                                  max_nodes=max(w.max_nodes, 1), window=window)
 
 
+@functools.lru_cache(maxsize=5)
+def oracle_full(name: str):
+    """The oracle's every row (out, lse) of a named workload at its own scale, computed once per
+    process (the large workloads take the host tens of seconds)."""
+    w = cached_config(name)
+    log(f"[oracle] all {w.total_nodes * w.num_q_heads} rows of {name}")
+    out, lse, err = oracle_attention(w)
+    assert (err == 0).all()
+    return out, lse
+
+
 def oracle_rows(w, rows, sm_scale=None, window=0):
     return oracle.tree_attention_rows(w.q, w.k, w.v, w.node_start, w.parent, w.kv_start, w.prefix_len, rows,
                                       num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,

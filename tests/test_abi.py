@@ -136,3 +136,24 @@ def test_stream_read_host_checks_need_no_gpu(lib):
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         ev.load(str(tmp_path / "libev.so"))
+
+
+def _prototypes(text):
+    """Every exported prototype in `text`, whitespace-normalised (comments removed first)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    found = re.findall(r"^((?:const char \*|size_t |ev_status )\s*ev_[a-z_]+\s*\([^;]*\));", text, flags=re.M)
+    return sorted(re.sub(r"\s+", " ", p) + ";" for p in found)
+
+
+def test_header_signatures_match_documented_block():
+    """include/ev.h declares exactly the prototypes that the design doc lists (its deviations from the
+    survey's boundary sketch are documented beside that block)."""
+    with open(os.path.join(ROOT, "include", "ev.h")) as f:
+        header = _prototypes(f.read())
+    with open(os.path.join(ROOT, "DESIGN.md")) as f:
+        design = f.read()
+    m = re.search(r"\*\*Signatures\.\*\*.*?```c\n(.*?)```", design, flags=re.S)
+    assert m, "DESIGN.md has no signature block"
+    documented = sorted(line.strip() for line in m.group(1).splitlines() if line.strip())
+    assert header == documented
+    assert len(header) == len(ev.EXPORTS)
