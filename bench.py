@@ -8,12 +8,14 @@ data already resident in HBM; several identical input sets sit at different addr
 steps rotate over them, so the 256 MB Infinity Cache cannot serve one step's reads from the
 previous step's.  Prints ONE JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload c8|c128k|c512|c1x4k|tiny] [--no-cpu]
-                  [--kv contiguous|paged|window] [--page-size P] [--window W] [--sample T] [--separate]
+  python bench.py [--steps K] [--warmup W] [--trials R] [--workload c8|c128k|c512|c1x4k|tiny]
+                  [--also WORKLOAD|''] [--no-cpu] [--kv contiguous|paged|window] [--page-size P]
+                  [--window W] [--sample T] [--separate]
   python bench.py --copy-calibration     (a plain device copy of known size, for counter scaling)
 
 The default workload is the 8-sequence batch (prefix lengths uniform in [1024, 8192], 16-node
-trees, 40 q heads / 8 KV heads, head_dim 128, bf16 KV, vocab 151936).
+trees, 40 q heads / 8 KV heads, head_dim 128, bf16 KV, vocab 151936); the 128K-context sequence
+(same heads, 16-node tree) is measured after it the same way and reported under "also".
 """
 from __future__ import annotations
 
@@ -32,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 MALL_BYTES = 256 << 20
 HBM_PEAK_GBPS = 8000.0
+BF16_DENSE_PEAK = 2.5e15  # MI355X dense bf16 matrix-core peak, FLOP/s
 METRIC = "verified tree-tokens/s + accepted tokens/s; KV-read HBM GB/s as % of peak"
 
 
@@ -41,6 +44,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="c8")
+    p.add_argument("--also", default="c128k",
+                   help="a second workload measured the same way and reported as a sub-record ('' for none)")
+    p.add_argument("--trials", type=int, default=5, help="timed runs the K steps are split into (median)")
     p.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0: enough to defeat the MALL)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -76,24 +82,6 @@ def lscpu_model() -> str:
         return m.group(1).strip() if m else platform.processor()
     except OSError:
         return platform.processor()
-
-
-def counters_for(kernel_src: str, workload: str):
-    """HBM traffic per attention launch from the committed counter summary, if it was taken on
-    the current kernel source (else None)."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"tree_attention_{workload}_counters.txt")
-    if not os.path.exists(path):
-        return None
-    vals = {}
-    for line in open(path):
-        m = re.match(r"\s*([a-z_]+)\s*[:=]\s*(\S+)", line)
-        if m:
-            vals[m.group(1)] = m.group(2)
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
-    if vals.get("kernel_source_sha") != sha or "traffic_bytes_per_launch" not in vals:
-        return None
-    return float(vals["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(w, target_seconds: float, temperature: float = 0.0):
@@ -141,25 +129,41 @@ def cpu_baseline(w, target_seconds: float, temperature: float = 0.0):
             "cpu_model": lscpu_model()}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the verification step "
-              "would shard by sequence or by KV head, with no exchange; only the one-GPU path is built)",
-              file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
+def counters_value(kernel_src: str, workload: str, suffix: str, key: str):
+    """A figure from a committed counter summary profiles/tree_attention_<workload>_<suffix>.txt, used
+    only if that summary was taken on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"tree_attention_{workload}_{suffix}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        m = re.match(r"\s*([a-z_]+)\s*[:=]\s*(\S+)", line)
+        if m:
+            vals[m.group(1)] = m.group(2)
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    if vals.get("kernel_source_sha") != sha or key not in vals:
+        return None
+    return float(vals[key])
 
+
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def measure(args, workload: str, with_cpu: bool) -> dict:
+    """One workload: warmup, then exactly args.steps timed steps split into `trials` equal runs (the
+    step time is the median of the runs' means), the attention call timed the same way, per-kernel
+    times, the read ceilings, and the oracle on the host cores."""
     import numpy as np
     import torch
 
     from draft_tree_verification_amd import ev, synth
 
-    torch.cuda.set_device(0)
-    w = synth.make_config(args.workload)
-    print(f"[bench] workload {args.workload}: {synth.describe(w)}", file=sys.stderr, flush=True)
+    w = synth.make_config(workload)
+    print(f"[bench] workload {workload}: {synth.describe(w)}", file=sys.stderr, flush=True)
     kv_bytes = w.kv_bytes()
     set_bytes = kv_bytes + w.logits.nbytes + w.q.nbytes
     nsets = args.sets or max(1, math.ceil(2 * MALL_BYTES / set_bytes))
@@ -269,51 +273,59 @@ def main():
     if int(err.item()):
         raise RuntimeError(f"data error flag {int(err.item())}")
 
+    # exactly K timed steps, in `trials` runs of equal length between event pairs (no marker inside
+    # a run); the step time is the median of the runs' means
     K = args.steps
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    trials = max(1, min(args.trials, K))
+    bounds = [K * j // trials for j in range(trials + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(trials + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    start.record()
     rc = 0
-    for i in range(K):
-        rc |= step(calls[i % nsets])
-    end.record()
+    for j in range(trials):
+        evs[j].record()
+        for i in range(bounds[j], bounds[j + 1]):
+            rc |= step(calls[i % nsets])
+    evs[trials].record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     if rc:
         raise RuntimeError("a launch failed in the timed region")
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / K
+    trial_ms = [evs[j].elapsed_time(evs[j + 1]) / (bounds[j + 1] - bounds[j]) for j in range(trials)]
+    ms_step = _median(trial_ms)
+    acc_sum = int(acc_len.sum().item())  # the last step's acceptance (every set holds the same inputs)
 
-    # The attention call's launch duration: a second timed region of K attention calls back to
-    # back on the same stream (rotating over the input sets like the steps), between one pair of
-    # HIP events.  Each call is the attention kernel and its merge launch; the average includes
-    # the gaps between launches.  (An event marker between launches costs stream time of its own,
-    # ~3 us here, so no region puts one between calls.)
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # The attention call's launch duration: K attention calls back to back on the same stream
+    # (rotating over the input sets like the steps), in `trials` runs between event pairs; the median
+    # of the runs' means.  A call is every launch of ev_tree_attention; the mean includes the gaps
+    # between launches.  (An event marker costs stream time of its own, ~3 us here, so no run has
+    # one between calls.)
     for i in range(min(K, 3)):
         rc |= fns[0](*calls[i % nsets][0])
     torch.cuda.synchronize()
-    a0.record()
-    for i in range(K):
-        rc |= fns[0](*calls[i % nsets][0])
-    a1.record()
+    aevs = [torch.cuda.Event(enable_timing=True) for _ in range(trials + 1)]
+    for j in range(trials):
+        aevs[j].record()
+        for i in range(bounds[j], bounds[j + 1]):
+            rc |= fns[0](*calls[i % nsets][0])
+    aevs[trials].record()
     torch.cuda.synchronize()
     if rc:
         raise RuntimeError("a launch failed in the attention timing region")
-    attn_ms = a0.elapsed_time(a1) / K
+    attn_trials = [aevs[j].elapsed_time(aevs[j + 1]) / (bounds[j + 1] - bounds[j]) for j in range(trials)]
+    attn_ms = _median(attn_trials)
 
-    # per-kernel breakdown (separate pass, not part of the timed region)
+    # per-call breakdown (separate pass, an event pair around every call; not part of the timed region)
     nf = len(fns)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nf + 1)] for _ in range(K)]
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(nf + 1)] for _ in range(K)]
     for i in range(K):
         c = calls[i % nsets]
         for j in range(nf):
-            evs[i][j].record()
+            kev[i][j].record()
             fns[j](*c[j])
-        evs[i][nf].record()
+        kev[i][nf].record()
     torch.cuda.synchronize()
-    kernel_ms = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K for j, n in enumerate(names)}
+    kernel_ms = {n: _median([kev[i][j].elapsed_time(kev[i][j + 1]) for i in range(K)]) for j, n in enumerate(names)}
 
     # streaming-read ceiling of this GPU: ev_stream_read over 2 GiB (8x the Infinity Cache)
     rbuf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
@@ -347,18 +359,23 @@ def main():
     same_size_read_ms = r0.elapsed_time(r1) / 20
     del sbufs
 
-    acc_sum = int(acc_len.sum().item())
+    vis_keys = [int(w.prefix_len[b]) for b in range(B)]
     if args.kv == "window":  # only the last `window` prefix tokens (and the tree) are read
-        vis = sum(min(int(w.prefix_len[b]), args.window) + int(w.nodes_per_seq[b]) for b in range(B))
-        kv_bytes = 2 * vis * Hkv * D * esz
+        vis_keys = [min(v, args.window) for v in vis_keys]
+        kv_bytes = 2 * sum(v + int(w.nodes_per_seq[b]) for b, v in enumerate(vis_keys)) * Hkv * D * esz
     tree_tps = T / (ms_step / 1e3)
-    # algorithmic bytes of one attention launch: every K/V row of every (sequence, KV head) once,
-    # Q read once, the output and the log-sum-exp written once
-    alg_bytes = kv_bytes + 2 * w.q.nbytes + T * Hq * 4
-    achieved = alg_bytes / (attn_ms * 1e-3) / 1e9
-    kv_gbps = kv_bytes / (attn_ms * 1e-3) / 1e9
-    traffic = counters_for(os.path.join(ROOT, "draft_tree_verification_amd", "csrc", "ev_attention.hip"),
-                           args.workload) if args.kv == "contiguous" else None
+    # Algorithmic bytes of one attention call: every K/V row of every (sequence, KV head) once (the
+    # roofline's bytes).  Q read once and the output and log-sum-exp written once are reported beside.
+    qo_bytes = 2 * w.q.nbytes + T * Hq * 4
+    achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
+    # matrix-core work of the call: every row of a (sequence, KV head) unit against every key the unit
+    # streams (prefix + tree, masked keys included), 2 products of 2*D flops per (row, key)
+    rows_per_unit = [int(w.nodes_per_seq[b]) * (Hq // Hkv) for b in range(B)]
+    mfma_flops = sum(4 * D * r * (vis_keys[b] + int(w.nodes_per_seq[b])) * Hkv for b, r in enumerate(rows_per_unit))
+    src = os.path.join(ROOT, "draft_tree_verification_amd", "csrc", "ev_attention.hip")
+    contiguous = args.kv == "contiguous"
+    traffic = counters_value(src, workload, "counters", "traffic_bytes_per_launch") if contiguous else None
+    mfma_busy = counters_value(src, workload, "mfma", "mfma_busy_frac") if contiguous else None
     rec = {
         "metric": METRIC,
         "value": round(tree_tps, 1),
@@ -376,12 +393,14 @@ def main():
                        kv_layout={"contiguous": "contiguous", "paged": f"paged{args.page_size}",
                                   "window": f"window{args.window}"}[args.kv],
                        verification=f"sampled T={args.sample}" if args.sample > 0 else "greedy T=0"),
+        "trials": trials,
+        "trial_ms_per_step": [round(x, 5) for x in trial_ms],
         "accepted_tokens_per_s": round(acc_sum / (ms_step / 1e3), 1),
         "accept_len_mean": acc_sum / B,
-        "kv_read_gbps": round(kv_gbps, 1),
-        "kv_read_pct_of_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
+        "kv_read_gbps": round(achieved, 1),
+        "kv_read_pct_of_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
         "read_ceiling_gbps": round(read_ceiling, 1),
-        "kv_read_pct_of_ceiling": round(100 * kv_gbps / read_ceiling, 2),
+        "kv_read_pct_of_ceiling": round(100 * achieved / read_ceiling, 2),
         "kv_sized_read_ms": round(same_size_read_ms, 5),
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
         "selection": "separate calls" if args.separate else "fused (ev_select_accept_compact)",
@@ -389,13 +408,44 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "tree_attention", "attention_ms": round(attn_ms, 5),
-                     "algorithmic_bytes_per_launch": alg_bytes},
+                     "attention_trial_ms": [round(x, 5) for x in attn_trials],
+                     "algorithmic_bytes_per_launch": kv_bytes, "q_o_lse_bytes_per_launch": qo_bytes,
+                     "mfma_tflops": round(mfma_flops / (attn_ms * 1e-3) / 1e12, 1),
+                     "mfma_frac_of_bf16_dense_peak": round(mfma_flops / (attn_ms * 1e-3) / BF16_DENSE_PEAK, 4),
+                     "mfma_busy_frac": mfma_busy},
         "cpu_baseline": None,
     }
-    if not args.no_cpu:
+    if with_cpu:
         del sets, out
         torch.cuda.empty_cache()
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.sample)
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the verification step "
+              "would shard by sequence or by KV head, with no exchange; only the one-GPU path is built)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+
+    torch.cuda.set_device(0)
+    rec = measure(args, args.workload, not args.no_cpu)
+    # the 128K-context configuration (the other configuration the bandwidth target names) as a
+    # sub-record of the same line, measured the same way
+    if args.also and args.also != args.workload:
+        torch.cuda.empty_cache()
+        sub = measure(args, args.also, not args.no_cpu)
+        keep = ("value", "unit", "ms_per_step", "trials", "trial_ms_per_step", "accepted_tokens_per_s",
+                "accept_len_mean", "config", "kv_read_gbps", "kv_read_pct_of_peak", "read_ceiling_gbps",
+                "kv_read_pct_of_ceiling", "kv_sized_read_ms", "kernel_ms", "roofline", "cpu_baseline")
+        rec["also"] = {args.also: {k: sub[k] for k in keep}}
     print(json.dumps(rec), flush=True)
 
 
