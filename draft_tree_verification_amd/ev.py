@@ -49,6 +49,12 @@ def load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m draft_tree_verification_amd.build` "
                            "(there is no non-HIP fallback)")
+    # torch first (when installed): loaded the other way round, the library binds a second copy of
+    # the HIP runtime and every call reports EV_ERR_DEVICE on the GPU
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     lib.ev_status_string.restype = ctypes.c_char_p
     lib.ev_status_string.argtypes = [ctypes.c_int]
