@@ -1072,6 +1072,7 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
     constexpr int SWZ = 16 / CPR;              // rows per 256-byte bank cycle
     constexpr int DTW = Lay::DTW;
     static_assert(PERW * (NB - 1) < 64, "vmcnt range");
+    static_assert(NB % 2 == 0, "the ring is consumed and refilled two stages at a time");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::kTotal];
     int32_t *s_cum = reinterpret_cast<int32_t *>(smem);
@@ -1258,13 +1259,11 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
         int par;
         asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(par) : "v"(lds_addr(pbuf) + 4 * lane) : "memory");
         if (lane >= n) par = -1;
-        bf16x8_t qop[RT][KS];
-        {
-            uint32_t qa[KS];
+        // the Q^T operands are read from the staged Q rows once per pair of blocks (held for the
+        // whole piece they would crowd the pair's operands out of the registers)
+        uint32_t qa[KS];
 #pragma unroll
-            for (int s = 0; s < KS; ++s) qa[s] = lds_addr(qbuf) + koff[s];
-            ReadQ<D>::run(qop, qa);
-        }
+        for (int s = 0; s < KS; ++s) qa[s] = lds_addr(qbuf) + koff[s];
         // ---- tree: validity and ancestor masks, while the loads are in flight
         const bool ok = lane >= n || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
         if (__any(!ok)) {
@@ -1288,97 +1287,138 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        // P^T operands (bf16) from the scores with the current maxima, per-lane row sums, and
-        // O^T += V^T P^T over the block's 16 keys
-        auto accumulate = [&](const f32x4_t (&sc)[RT], const u32x2_t (&vq)[DT]) {
-            u32x2_t pw[RT];
+        // The wave takes its 16-key blocks two at a time (block a of stage i, block b of stage
+        // i + 1).  Scores are S^T = K Q^T per block; the value product runs over both blocks' 32
+        // keys on v_mfma_f32_16x16x32_bf16 (half the instructions of two 16-key products).  Its k
+        // slots 8q + e (lane group q = lane / 16) hold keys 4q + e of block a for e < 4 and keys
+        // 4q + e - 4 of block b for e >= 4: exactly the four score rows each lane holds in both
+        // score tiles and the four keys each V^T transpose read returns, so no value moves between
+        // lanes.  A missing block b (odd stage count) enters with zero probabilities against a
+        // copy of block a's values.
+        auto accumulate = [&](const f32x4_t (&sa)[RT], const f32x4_t (&sb)[RT], const u32x2_t (&vqa)[DT],
+                              const u32x2_t (&vqb)[DT]) {
+            u32x4_t pw[RT];
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
                 const float mu = m_run[t] == -INFINITY ? 0.f : m_run[t];
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][0], c2, -mu));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][1], c2, -mu));
-                const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][2], c2, -mu));
-                const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][3], c2, -mu));
-                l_run[t] += (p0 + p1) + (p2 + p3);
-                pw[t] = u32x2_t{ev::pack_bf16x2(p0, p1), ev::pack_bf16x2(p2, p3)};
+                const float a0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[t][0], c2, -mu));
+                const float a1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[t][1], c2, -mu));
+                const float a2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[t][2], c2, -mu));
+                const float a3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[t][3], c2, -mu));
+                const float b0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[t][0], c2, -mu));
+                const float b1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[t][1], c2, -mu));
+                const float b2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[t][2], c2, -mu));
+                const float b3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[t][3], c2, -mu));
+                l_run[t] += ((a0 + a1) + (a2 + a3)) + ((b0 + b1) + (b2 + b3));
+                pw[t] = u32x4_t{ev::pack_bf16x2(a0, a1), ev::pack_bf16x2(a2, a3), ev::pack_bf16x2(b0, b1),
+                                ev::pack_bf16x2(b2, b3)};
             }
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const v4i16_t vop = __builtin_bit_cast(v4i16_t, vq[dt]);
+                const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, u32x4_t{vqa[dt][0], vqa[dt][1], vqb[dt][0], vqb[dt][1]});
 #pragma unroll
                 for (int t = 0; t < RT; ++t)
-                    o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, __builtin_bit_cast(v4i16_t, pw[t]),
-                                                                          o[t][dt], 0, 0, 0);
+                    o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, __builtin_bit_cast(bf16x8_t, pw[t]), o[t][dt],
+                                                                       0, 0, 0);
+            }
+        };
+        // scores of one block of 16 keys starting at unit-relative key kb: S^T = K Q^T, then the
+        // ancestor mask where the block reaches the tree slots
+        auto scores = [&](f32x4_t (&sc)[RT], const u32x4_t (&kq)[KS], const bf16x8_t (&qop)[RT][KS], int kb) {
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kq[s2]), qop[t][s2], acc,
+                                                                  0, 0, 0);
+                sc[t] = acc;
+            }
+            if (kb + 16 > L) {  // the block reaches the tree slots or the unit's end
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    // ancestor mask of this lane's row (rows past the unit see nothing)
+                    const int row = rg * R + 16 * t + lr;
+                    const int node = row < nrows ? row / G : 0;
+                    const uint32_t mlo = __shfl(static_cast<uint32_t>(anc), node, 64);
+                    const uint32_t mhi = __shfl(static_cast<uint32_t>(anc >> 32), node, 64);
+                    const uint64_t rmask = row < nrows ? ((static_cast<uint64_t>(mhi) << 32) | mlo) : 0ull;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int p = kb + 4 * lq + r;
+                        const bool vis = p < L || (p < kv_end && ((rmask >> (p - L)) & 1ull));
+                        if (!vis) sc[t][r] = -INFINITY;
+                    }
+                }
             }
         };
 
         // The hot loop never touches the accumulators outside the MFMAs (they stay in the matrix
-        // registers); a stage whose scores need new maxima leaves it, and the rescale runs below.
+        // registers); a pair whose scores need new maxima leaves it, and the rescale runs below.
         int i = 0;
         for (;;) {
-            f32x4_t sc[RT];
+            f32x4_t sa[RT], sb[RT];
             float mloc[RT];
-            u32x2_t vq[DT];
+            u32x2_t vqa[DT], vqb[DT];
             bool rescale = false;
-            for (; i < nst; ++i) {
-                const int later = min(NB - 1, nst - 1 - i);  // this wave's stages issued after stage i
-                if (later >= 3) vm_wait_n<3 * PERW>();
-                else if (later == 2) vm_wait_n<2 * PERW>();
+            for (; i < nst; i += 2) {
+                const bool two = i + 1 < nst;
+                // this wave's stages issued after the pair: the ring holds NB stages, refilled two
+                // at a time
+                const int later = min(nst, i + NB) - min(nst, i + 2);
+                if (later >= 2) vm_wait_n<2 * PERW>();
                 else if (later == 1) vm_wait_n<PERW>();
                 else vm_wait_n<0>();
-                const uint32_t base = wbuf_lds + (i % NB) * WBUF;
-                uint32_t ka[KS], va[DT];
+                // block a's operands, its refill and its scores, then block b's (one block's K
+                // operands live at a time); sa[t] / sb[t] hold raw scores of keys kb + 4*lq + r
+                // for row 16t + lr, kb the block's unit-relative first key
+                bf16x8_t qop[RT][KS];
+                ReadQ<D>::run(qop, qa);
+                {
+                    u32x4_t kq[KS];
+                    const uint32_t base = wbuf_lds + (i % NB) * WBUF;
+                    uint32_t ka[KS], va[DT];
 #pragma unroll
-                for (int s = 0; s < KS; ++s) ka[s] = base + koff[s];
+                    for (int s2 = 0; s2 < KS; ++s2) ka[s2] = base + koff[s2];
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) va[dt] = base + voff[dt];
-                u32x4_t kq[KS];
-                ReadKV<D>::run(kq, vq, ka, va);
-                if (i + NB < nst) issue(st0 + i + NB, i % NB);  // the buffer's operands are in registers
-
-                const int kb = (st0 + i) * KST + 16 * wave;     // unit-relative first key of the block
-                // S^T = K Q^T: sc[t] holds raw scores of keys kb + 4*lq + r for row 16t + lr
-#pragma unroll
-                for (int t = 0; t < RT; ++t) {
-                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < KS; ++s)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kq[s]), qop[t][s],
-                                                                      acc, 0, 0, 0);
-                    sc[t] = acc;
+                    for (int dt = 0; dt < DT; ++dt) va[dt] = base + voff[dt];
+                    ReadKV<D>::run(kq, vqa, ka, va);
+                    if (i + NB < nst) issue(st0 + i + NB, i % NB);  // the buffer's operands are in registers
+                    scores(sa, kq, qop, (st0 + i) * KST + 16 * wave);
                 }
-                if (kb + 16 > L) {  // the block reaches the tree slots or the unit's end
+                if (two) {
+                    u32x4_t kq[KS];
+                    const uint32_t base = wbuf_lds + ((i + 1) % NB) * WBUF;
+                    uint32_t ka[KS], va[DT];
 #pragma unroll
-                    for (int t = 0; t < RT; ++t) {
-                        // ancestor mask of this lane's row (rows past the unit see nothing)
-                        const int row = rg * R + 16 * t + lr;
-                        const int node = row < nrows ? row / G : 0;
-                        const uint32_t mlo = __shfl(static_cast<uint32_t>(anc), node, 64);
-                        const uint32_t mhi = __shfl(static_cast<uint32_t>(anc >> 32), node, 64);
-                        const uint64_t rmask = row < nrows ? ((static_cast<uint64_t>(mhi) << 32) | mlo) : 0ull;
+                    for (int s2 = 0; s2 < KS; ++s2) ka[s2] = base + koff[s2];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int p = kb + 4 * lq + r;
-                            const bool vis = p < L || (p < kv_end && ((rmask >> (p - L)) & 1ull));
-                            if (!vis) sc[t][r] = -INFINITY;
-                        }
-                    }
+                    for (int dt = 0; dt < DT; ++dt) va[dt] = base + voff[dt];
+                    ReadKV<D>::run(kq, vqb, ka, va);
+                    if (i + 1 + NB < nst) issue(st0 + i + 1 + NB, (i + 1) % NB);
+                    scores(sb, kq, qop, (st0 + i + 1) * KST + 16 * wave);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < RT; ++t) sb[t] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) vqb[dt] = vqa[dt];
                 }
                 // running maxima move only when a score exceeds them by more than the slack
                 bool need = false;
 #pragma unroll
                 for (int t = 0; t < RT; ++t) {
-                    mloc[t] = fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3]));
+                    mloc[t] = fmaxf(fmaxf(fmaxf(sa[t][0], sa[t][1]), fmaxf(sa[t][2], sa[t][3])),
+                                    fmaxf(fmaxf(sb[t][0], sb[t][1]), fmaxf(sb[t][2], sb[t][3])));
                     need |= mloc[t] * c2 > m_run[t] + kRescaleSlack;
                 }
                 if (__any(need)) {
                     rescale = true;
                     break;
                 }
-                accumulate(sc, vq);
+                accumulate(sa, sb, vqa, vqb);
             }
             if (!rescale) break;
-            // new maxima for stage i: rescale the states, then finish the stage
+            // new maxima for the pair at i: rescale the states, then finish the pair
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
                 float mx = mloc[t];
@@ -1393,8 +1433,8 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
                 l_run[t] *= alpha;
                 m_run[t] = m_new;
             }
-            accumulate(sc, vq);
-            ++i;
+            accumulate(sa, sb, vqa, vqb);
+            i += 2;
         }
 
         // ---- row sums over the four lanes that share a row
