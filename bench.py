@@ -51,9 +51,10 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", action="store_true")
-    p.add_argument("--kv", default="contiguous", choices=("contiguous", "paged", "window"),
-                   help="K/V layout of the step: contiguous slots (default), a paged pool through a block "
-                        "table (--page-size), or a sliding window over the prefix (--window)")
+    p.add_argument("--kv", default="contiguous", choices=("contiguous", "headmajor", "paged", "window"),
+                   help="K/V layout of the step: contiguous [slots][Hkv][D] (default), head-major [Hkv][slots][D] "
+                        "(ev_tree_attention_strided; compaction per head), a paged pool through a block table "
+                        "(--page-size), or a sliding window over the prefix (--window)")
     p.add_argument("--page-size", type=int, default=16)
     p.add_argument("--window", type=int, default=4096)
     p.add_argument("--separate", action="store_true",
@@ -185,6 +186,8 @@ def measure(args, workload: str, with_cpu: bool) -> dict:
         meta["block_table"] = dev(bt)
         num_pages = pk.shape[0] // args.page_size
         del pk, pv
+    elif args.kv == "headmajor":  # [Hkv][slots][D]: each KV head's rows contiguous
+        host["k"], host["v"] = dev(w.k.transpose(1, 0, 2)), dev(w.v.transpose(1, 0, 2))
     else:
         host["k"], host["v"] = dev(w.k), dev(w.v)
     sets = [host] + [{n: t.clone() for n, t in host.items()} for _ in range(nsets - 1)]
@@ -218,6 +221,12 @@ def measure(args, workload: str, with_cpu: bool) -> dict:
             cmp = (p(s["k"]), p(s["v"]), esz, 1, num_pages * args.page_size * Hkv * D * esz, m["block_table"], bts,
                    args.page_size, m["prefix_len"], p(acc_len), p(acc_path), B, maxn, num_pages, Hkv, D,
                    p(new_len), p(err), stream)
+        elif args.kv == "headmajor":  # compaction sees Hkv one-head layers of [slots][D]
+            attn = (p(s["q"]), p(s["k"]), p(s["v"]), p(out[i]), p(lse), m["node_start"], m["parent"],
+                    m["kv_start"], m["prefix_len"], B, T, maxn, w.total_slots, Hq, Hkv, D, D, w.total_slots * D, dt,
+                    w.sm_scale, aws.ptr, aws.nbytes, p(err), stream)
+            cmp = (p(s["k"]), p(s["v"]), esz, Hkv, w.total_slots * D * esz, m["kv_start"], m["prefix_len"],
+                   p(acc_len), p(acc_path), B, maxn, w.total_slots, 1, D, p(new_len), p(err), stream)
         else:
             attn = (p(s["q"]), p(s["k"]), p(s["v"]), p(out[i]), p(lse), m["node_start"], m["parent"],
                     m["kv_start"], m["prefix_len"], B, T, maxn, w.total_slots, Hq, Hkv, D, dt, w.sm_scale) + \
@@ -225,13 +234,16 @@ def measure(args, workload: str, with_cpu: bool) -> dict:
             cmp = (p(s["k"]), p(s["v"]), esz, 1, w.total_slots * Hkv * D * esz, m["kv_start"], m["prefix_len"],
                    p(acc_len), p(acc_path), B, maxn, w.total_slots, Hkv, D, p(new_len), p(err), stream)
         if not args.separate:  # token, acceptance and compaction in one call (noise offset = the set's index)
+            hm = args.kv == "headmajor"
             head = (p(s["logits"]), dt, w.vocab, w.vocab, args.sample, 0x5EED, i, m["node_start"], m["parent"],
-                    m["draft"], B, T, maxn, p(s["k"]), p(s["v"]), esz, 1)
+                    m["draft"], B, T, maxn, p(s["k"]), p(s["v"]), esz, Hkv if hm else 1)
             out_args = (p(target), p(acc_len), p(acc_path), p(bonus), p(out_tok), p(new_len), sws.ptr, sws.nbytes,
                         p(err), stream)
             if args.kv == "paged":
                 fused = head + (num_pages * args.page_size * Hkv * D * esz, m["block_table"],
                                 meta["block_table"].shape[1], args.page_size, m["prefix_len"], num_pages, Hkv, D)
+            elif hm:
+                fused = head + (w.total_slots * D * esz, m["kv_start"], m["prefix_len"], w.total_slots, 1, D)
             else:
                 fused = head + (w.total_slots * Hkv * D * esz, m["kv_start"], m["prefix_len"], w.total_slots, Hkv, D)
             calls.append((attn, fused + out_args))
@@ -247,8 +259,8 @@ def measure(args, workload: str, with_cpu: bool) -> dict:
             (m["node_start"], m["parent"], m["draft"], p(target), B, T, maxn, w.vocab, p(acc_len), p(acc_path),
              p(bonus), p(out_tok), p(err), stream),
             cmp))
-    f_attn = {"contiguous": lib.ev_tree_attention, "paged": lib.ev_tree_attention_paged,
-              "window": lib.ev_tree_attention_window}[args.kv]
+    f_attn = {"contiguous": lib.ev_tree_attention, "headmajor": lib.ev_tree_attention_strided,
+              "paged": lib.ev_tree_attention_paged, "window": lib.ev_tree_attention_window}[args.kv]
     if args.separate:
         f_arg = lib.ev_node_sample if args.sample > 0 else lib.ev_node_argmax
         f_acc = lib.ev_sampled_accept if args.sample > 0 else lib.ev_greedy_accept
@@ -373,9 +385,9 @@ def measure(args, workload: str, with_cpu: bool) -> dict:
     rows_per_unit = [int(w.nodes_per_seq[b]) * (Hq // Hkv) for b in range(B)]
     mfma_flops = sum(4 * D * r * (vis_keys[b] + int(w.nodes_per_seq[b])) * Hkv for b, r in enumerate(rows_per_unit))
     src = os.path.join(ROOT, "draft_tree_verification_amd", "csrc", "ev_attention.hip")
-    contiguous = args.kv == "contiguous"
-    traffic = counters_value(src, workload, "counters", "traffic_bytes_per_launch") if contiguous else None
-    mfma_busy = counters_value(src, workload, "mfma", "mfma_busy_frac") if contiguous else None
+    tag = {"contiguous": workload, "headmajor": f"{workload}_headmajor"}.get(args.kv)
+    traffic = counters_value(src, tag, "counters", "traffic_bytes_per_launch") if tag else None
+    mfma_busy = counters_value(src, tag, "mfma", "mfma_busy_frac") if tag else None
     rec = {
         "metric": METRIC,
         "value": round(tree_tps, 1),
@@ -390,8 +402,8 @@ def measure(args, workload: str, with_cpu: bool) -> dict:
         "dtype": "bf16" if w.dtype == synth.BF16 else "f32",
         "data": "synthetic (seeded; shapes of the workload, no dataset or weights)",
         "config": dict(synth.describe(w), input_sets=nsets, kv_bytes=kv_bytes,
-                       kv_layout={"contiguous": "contiguous", "paged": f"paged{args.page_size}",
-                                  "window": f"window{args.window}"}[args.kv],
+                       kv_layout={"contiguous": "contiguous [slots][Hkv][D]", "headmajor": "head-major [Hkv][slots][D]",
+                                  "paged": f"paged{args.page_size}", "window": f"window{args.window}"}[args.kv],
                        verification=f"sampled T={args.sample}" if args.sample > 0 else "greedy T=0"),
         "trials": trials,
         "trial_ms_per_step": [round(x, 5) for x in trial_ms],

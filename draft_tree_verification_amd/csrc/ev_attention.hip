@@ -61,6 +61,7 @@ struct AttnArgs {
     const int32_t *kv_start;
     const int32_t *prefix_len;
     int64_t total_slots;
+    int64_t kv_slot_stride, kv_head_stride;  // elements between a K/V cache's slots / KV heads
     int32_t batch, total_nodes, max_nodes, hq, hkv, group, row_groups;
     int32_t window;    // > 0: only the last `window` prefix tokens are visible (sliding window)
     const int32_t *block_table;  // paged caches (else NULL): [batch][bt_stride] pool page of each
@@ -534,9 +535,9 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
         }
 
         const int kv_end = L + n;  // unit-relative key positions below this exist
-        const size_t slot_stride = static_cast<size_t>(a.hkv) * D;  // elements between slots
+        const size_t slot_stride = static_cast<size_t>(a.kv_slot_stride);  // elements between slots
         // paged caches: rows are found per load through the block table, s0 is a token index
-        const size_t head_off = (PG ? 0 : static_cast<size_t>(s0) * slot_stride) + static_cast<size_t>(g) * D;
+        const size_t head_off = (PG ? 0 : static_cast<size_t>(s0) * slot_stride) + static_cast<size_t>(g) * a.kv_head_stride;
         const int32_t *bt = nullptr;
         if constexpr (PG) bt = a.block_table + static_cast<size_t>(__builtin_amdgcn_readfirstlane(b)) * a.bt_stride;
 
@@ -1132,9 +1133,9 @@ __device__ __forceinline__ void attention_ks_body(const AttnArgs &a) {
         const int nrows = n * G;
         const int kv_end = L + n;
         const int nst = st1 - st0;
-        const size_t slot_stride = static_cast<size_t>(a.hkv) * D;
+        const size_t slot_stride = static_cast<size_t>(a.kv_slot_stride);  // elements between slots
         // paged caches: rows are found per block through the block table, s0 is a token index
-        const size_t head_off = (PG ? 0 : static_cast<size_t>(s0) * slot_stride) + static_cast<size_t>(g) * D;
+        const size_t head_off = (PG ? 0 : static_cast<size_t>(s0) * slot_stride) + static_cast<size_t>(g) * a.kv_head_stride;
         const uint16_t *kbase = static_cast<const uint16_t *>(a.k) + head_off;
         const uint16_t *vbase = static_cast<const uint16_t *>(a.v) + head_off;
         const int32_t *bt = nullptr;
@@ -1786,8 +1787,14 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
                            int64_t total_slots, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                            ev_dtype dtype, float sm_scale, int32_t window, const int32_t *block_table,
                            int32_t bt_stride, int32_t page_size, void *workspace, size_t workspace_bytes,
-                           int32_t *err_flag, hipStream_t stream, bool use_scratch = false) {
+                           int32_t *err_flag, hipStream_t stream, bool use_scratch = false,
+                           int64_t slot_stride = 0, int64_t head_stride = -1) {
     const bool pg = page_size > 0;  // paged caches: total_slots = pool pages * page_size
+    // K/V element strides: [slot][kv_head][dim] unless the caller gives its own
+    if (slot_stride == 0 && head_stride == -1) {
+        slot_stride = static_cast<int64_t>(num_kv_heads) * head_dim;
+        head_stride = head_dim;
+    }
     if (!q || !k_cache || !v_cache || !out || !node_start || !parent || !prefix_len || (pg ? !block_table : !kv_start))
         return EV_ERR_NULL;
     if (batch < 0 || batch > EV_MAX_BATCH || total_nodes < 0 || max_nodes < 1 || max_nodes > EV_MAX_NODES ||
@@ -1798,6 +1805,11 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
     if (pg && dtype != EV_BF16) return EV_ERR_DTYPE;
     if (!ev::aligned16(q) || !ev::aligned16(k_cache) || !ev::aligned16(v_cache) || !ev::aligned16(out))
         return EV_ERR_ALIGN;
+    // strides: one slot's rows must stay under 2^26 bytes apart (32-bit lane offsets over 16 rows)
+    // and every row must start on 16 bytes
+    const int64_t esz = dtype == EV_F32 ? 4 : 2;
+    if (slot_stride < 1 || head_stride < 0 || slot_stride * esz > (int64_t(1) << 26)) return EV_ERR_SHAPE;
+    if ((slot_stride * esz) % 16 || (head_stride * esz) % 16) return EV_ERR_ALIGN;
     const Plan plan = make_plan(batch, max_nodes, num_q_heads, num_kv_heads, head_dim);
     if (use_scratch) {
         if (plan.bytes > kMaxWorkspaceBytes) return EV_ERR_WORKSPACE;  // beyond the static scratch
@@ -1841,6 +1853,8 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
     args.kv_start = kv_start;
     args.prefix_len = prefix_len;
     args.total_slots = total_slots;
+    args.kv_slot_stride = slot_stride;
+    args.kv_head_stride = head_stride;
     args.batch = batch;
     args.total_nodes = total_nodes;
     args.max_nodes = max_nodes;
@@ -1895,6 +1909,21 @@ extern "C" ev_status ev_tree_attention_noalloc(const void *q, const void *k_cach
     return launch_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
                             total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype,
                             sm_scale, 0, nullptr, 0, 0, nullptr, 0, err_flag, stream, true);
+}
+
+extern "C" ev_status ev_tree_attention_strided(const void *q, const void *k_cache, const void *v_cache, void *out,
+                                               float *lse, const int32_t *node_start, const int32_t *parent,
+                                               const int32_t *kv_start, const int32_t *prefix_len, int32_t batch,
+                                               int32_t total_nodes, int32_t max_nodes, int64_t total_slots,
+                                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                               int64_t kv_slot_stride, int64_t kv_head_stride, ev_dtype dtype,
+                                               float sm_scale, void *workspace, size_t workspace_bytes,
+                                               int32_t *err_flag, hipStream_t stream) {
+    if (kv_slot_stride < 1 || kv_head_stride < 0) return EV_ERR_SHAPE;
+    return launch_attention(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
+                            total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, dtype,
+                            sm_scale, 0, nullptr, 0, 0, workspace, workspace_bytes, err_flag, stream, false,
+                            kv_slot_stride, kv_head_stride);
 }
 
 extern "C" ev_status ev_tree_attention_window(const void *q, const void *k_cache, const void *v_cache, void *out,

@@ -29,7 +29,7 @@ EXPORTS = ("ev_status_string", "ev_tree_attention_workspace_size", "ev_tree_atte
            "ev_node_argmax", "ev_node_sample", "ev_greedy_accept", "ev_sampled_accept", "ev_compact_kv",
            "ev_compact_kv_paged",
            "ev_select_workspace_size", "ev_select_accept_compact", "ev_select_accept_compact_paged",
-           "ev_stream_read", "ev_tree_attention_noalloc")
+           "ev_stream_read", "ev_tree_attention_noalloc", "ev_tree_attention_strided")
 
 _lib = None
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -97,6 +97,9 @@ def load(path: str = LIB_PATH):
     lib.ev_select_accept_compact_paged.argtypes = [_P, ctypes.c_int, _I64, _I32, _F, _U64, _U64, _P, _P, _P, _I32,
                                                    _I32, _I32, _P, _P, _I32, _I32, _I64, _P, _I32, _I32, _P, _I32,
                                                    _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
+    lib.ev_tree_attention_strided.restype = ctypes.c_int
+    lib.ev_tree_attention_strided.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32,
+                                              _I32, _I32, _I64, _I64, ctypes.c_int, _F, _P, _SZ, _P, _P]
     lib.ev_tree_attention_noalloc.restype = ctypes.c_int
     lib.ev_tree_attention_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32,
                                               _I32, _I32, ctypes.c_int, _F, _P, _P]
@@ -130,6 +133,15 @@ def ev_tree_attention_noalloc(q, k_cache, v_cache, out, lse, node_start, parent,
     return load().ev_tree_attention_noalloc(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len,
                                             batch, total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads,
                                             head_dim, dtype, sm_scale, err_flag, stream)
+
+
+def ev_tree_attention_strided(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
+                              total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, kv_slot_stride,
+                              kv_head_stride, dtype, sm_scale, workspace, workspace_bytes, err_flag, stream) -> int:
+    return load().ev_tree_attention_strided(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len,
+                                            batch, total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads,
+                                            head_dim, kv_slot_stride, kv_head_stride, dtype, sm_scale, workspace,
+                                            workspace_bytes, err_flag, stream)
 
 
 def ev_tree_attention_window(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
@@ -316,10 +328,11 @@ class Workspace:
 
 def tree_attention(q, k_cache, v_cache, node_start, parent, kv_start, prefix_len, *, max_nodes: int,
                    sm_scale: float, window: int = None, out=None, lse=None, workspace: Workspace = None,
-                   err_flag=None, stream=None):
+                   err_flag=None, stream=None, head_major: bool = False):
     """Tree-masked GQA attention (ev_tree_attention; ev_tree_attention_window when `window` is given:
-    only the last `window` prefix tokens are visible).  q [T, Hq, D]; caches [slots, Hkv, D];
-    metadata int32.  Returns (out, lse, workspace)."""
+    only the last `window` prefix tokens are visible; ev_tree_attention_strided for head-major
+    caches).  q [T, Hq, D]; caches [slots, Hkv, D], or [Hkv, slots, D] with head_major; metadata
+    int32.  Returns (out, lse, workspace)."""
     torch = _torch()
     _need(q, "q", ndim=3)
     _need(k_cache, "k_cache", q.dtype, 3)
@@ -327,8 +340,13 @@ def tree_attention(q, k_cache, v_cache, node_start, parent, kv_start, prefix_len
     for name, t in (("node_start", node_start), ("parent", parent), ("kv_start", kv_start),
                     ("prefix_len", prefix_len)):
         _need(t, name, torch.int32, 1)
+    if head_major and window is not None:
+        raise ValueError("the sliding window reads [slots, Hkv, D] caches only")
     T, Hq, D = q.shape
-    slots, Hkv, Dk = k_cache.shape
+    if head_major:
+        Hkv, slots, Dk = k_cache.shape
+    else:
+        slots, Hkv, Dk = k_cache.shape
     if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("q / k_cache / v_cache shapes disagree")
     B = prefix_len.shape[0]
@@ -349,7 +367,9 @@ def tree_attention(q, k_cache, v_cache, node_start, parent, kv_start, prefix_len
     ptrs = (_addr(q), _addr(k_cache), _addr(v_cache), _addr(out), _addr(lse), _addr(node_start), _addr(parent),
             _addr(kv_start), _addr(prefix_len), B, T, max_nodes, slots, Hq, Hkv, D, _dtype_code(q), float(sm_scale))
     tail = (workspace.ptr, workspace.nbytes, _addr(err_flag), _stream(stream))
-    if window is None:
+    if head_major:
+        _check(ev_tree_attention_strided(*ptrs[:16], D, slots * D, *ptrs[16:], *tail), "ev_tree_attention_strided")
+    elif window is None:
         _check(ev_tree_attention(*ptrs, *tail), "ev_tree_attention")
     else:
         _check(ev_tree_attention_window(*ptrs, int(window), *tail), "ev_tree_attention_window")

@@ -125,6 +125,32 @@ ev_status ev_tree_attention(const void *q, const void *k_cache, const void *v_ca
                             int32_t *err_flag, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * ev_tree_attention_strided
+ *
+ * ev_tree_attention over K/V caches with caller-given element strides: cache row (slot s, KV head
+ * g) starts at element s * kv_slot_stride + g * kv_head_stride of k_cache / v_cache (head_dim
+ * contiguous elements).  ev_tree_attention is the case kv_slot_stride = num_kv_heads * head_dim,
+ * kv_head_stride = head_dim ([slot][kv_head][dim]); kv_slot_stride = head_dim, kv_head_stride =
+ * total_slots * head_dim is the head-major cache [kv_head][slot][dim], whose rows of one KV head
+ * are contiguous and stream faster (a unit reads whole runs of its own head's rows).  Every other
+ * argument, the arithmetic, the workspace and the error behaviour are those of ev_tree_attention;
+ * results are bit-identical to ev_tree_attention on the same values in its layout.
+ *   kv_slot_stride   >= 1;  kv_head_stride >= 0;  both times the element size must be multiples
+ *                    of 16 bytes (EV_ERR_ALIGN) and kv_slot_stride * element size <= 2^26
+ *                    (EV_ERR_SHAPE).  The caches must hold (total_slots - 1) * kv_slot_stride +
+ *                    (num_kv_heads - 1) * kv_head_stride + head_dim elements.
+ * A head-major cache is compacted by ev_compact_kv (or the fused call) with num_layers = KV heads
+ * per layer, layer_stride_bytes = total_slots * head_dim * element size and num_kv_heads = 1.
+ * -------------------------------------------------------------------------------------------*/
+ev_status ev_tree_attention_strided(const void *q, const void *k_cache, const void *v_cache, void *out, float *lse,
+                                    const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                                    const int32_t *prefix_len, int32_t batch, int32_t total_nodes,
+                                    int32_t max_nodes, int64_t total_slots, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int64_t kv_slot_stride,
+                                    int64_t kv_head_stride, ev_dtype dtype, float sm_scale, void *workspace,
+                                    size_t workspace_bytes, int32_t *err_flag, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * ev_tree_attention_window
  *
  * ev_tree_attention with a sliding window over the prefix: the EAGLE-4 drafter's layers attend

@@ -76,6 +76,10 @@ def test_host_argument_checks_need_no_gpu(lib):
     assert ev.ev_node_argmax(P, 0, 12, 1, 8, P, None, None, 0, None) == 4       # 24-byte rows
     assert ev.ev_node_argmax(P, 2, 8, 1, 8, P, None, None, 0, None) == 3
     assert ev.ev_node_argmax(P, 0, 151936, 16, 151936, P, None, None, 0, None) == 5
+    # strided caches: strides checked before any device work
+    for ss, hs, want in ((0, 64, 2), (128, -1, 2), (100, 64, 4), (128, 4, 4), (1 << 26, 64, 2)):
+        assert ev.ev_tree_attention_strided(P, P, P, P, None, P, P, P, P, 1, 4, 4, 100, 8, 2, 64, ss, hs, 0, 0.1, P,
+                                            1 << 30, None, None) == want, (ss, hs)
     # the allocation-free attention call checks its arguments before it looks for a device
     assert ev.ev_tree_attention_noalloc(None, P, P, P, None, P, P, P, P, 1, 4, 4, 100, 8, 2, 64, 0, 0.1, None,
                                         None) == 1

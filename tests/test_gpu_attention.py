@@ -269,3 +269,37 @@ def test_relabeling_moves_rows_with_their_nodes(scale_mult):
     gu.check_attention(o1[back], ref, l1[back], ref_lse, vmax=vmax, what=f"relabelled x{scale_mult:.3g}")
     diff = np.abs(gu.widen(o1[back]) - gu.widen(o0))
     assert diff.max() <= gu.TIGHT_FRAC * vmax, diff.max()
+
+
+def _head_major(a):
+    return np.ascontiguousarray(np.asarray(a).transpose(1, 0, 2))
+
+
+@pytest.mark.parametrize("name", ["c8", "mixed", "tiny"])
+def test_head_major_caches(name):
+    """ev_tree_attention_strided over head-major caches [Hkv][slots][D]: bit-identical to
+    ev_tree_attention over the same values in [slots][Hkv][D], and within the bar of the oracle
+    (which reads the slot-major arrays); bf16 80-row units (key-split kernel), ragged batches with
+    short prefixes and a peaked softmax (row-tile kernels), and fp32 inputs."""
+    import torch
+    from draft_tree_verification_amd import ev
+    gu.log(f"[case] attention head-major {name}")
+    if name == "mixed":
+        w = synth.make_workload("hm", 91, prefix_lens=[0, 3, 700, 129, 2049, 64], nodes=[16, 1, 9, 16, 4, 12],
+                                vocab=64, slot_gap=2)
+        scale = w.sm_scale * 8 * math.sqrt(128)
+    else:
+        w = gu.cached_config(name)
+        scale = w.sm_scale
+    d = gu.dev_workload(w)
+    o_sm, l_sm = gu.gpu_attention(w, d, scale)
+    k_hm, v_hm = gu.to_dev(_head_major(w.k)), gu.to_dev(_head_major(w.v))
+    o_hm, l_hm, _ = ev.tree_attention(d["q"], k_hm, v_hm, d["node_start"], d["parent"], d["kv_start"], d["prefix_len"],
+                                      max_nodes=max(w.max_nodes, 1), sm_scale=scale, head_major=True)
+    torch.cuda.synchronize()
+    assert gu.to_host(o_hm).tobytes() == gu.to_host(o_sm).tobytes(), "outputs differ from the slot-major call"
+    assert gu.to_host(l_hm).tobytes() == gu.to_host(l_sm).tobytes(), "lse differs from the slot-major call"
+    ref, ref_lse, err = gu.oracle_attention(w, scale)
+    assert (err == 0).all()
+    gu.check_attention(gu.to_host(o_hm), ref, gu.to_host(l_hm), ref_lse, vmax=_vmax(w), what=f"head-major {name}",
+                       tight=w.dtype == BF16)

@@ -356,3 +356,26 @@ def test_randomized_against_separate_calls():
         assert gu.to_host(k1).tobytes() == gu.to_host(k2).tobytes(), what
         assert gu.to_host(v1).tobytes() == gu.to_host(v2).tobytes(), what
     gu.log("[fused] 40 random configurations bit-exact")
+
+
+def test_head_major_compaction_as_per_head_layers():
+    """Head-major caches [layers][Hkv][slots][D] are compacted by the fused call with one 'layer' per
+    (layer, KV head) and one head per layer: the result, read back as [layers][slots][Hkv][D], equals
+    the slot-major compaction of the same values, and the acceptance outputs agree."""
+    import torch
+    gu.log("[case] fused head-major compaction")
+    c = _case(123, 6, 16, 5000, 5000, BF16, 2, 4, 64, np.uint16, max_prefix=40)
+    tref, _ = oracle.node_argmax(c["logits"], vocab=c["vocab"], row_stride=c["logits"].shape[1])
+    draft = _planted(c["rng"], c["trees"], tref, c["vocab"], 0.9)
+    d = _dev(c, draft)
+    layers, slots, H, D = c["k"].shape
+    k1, v1 = gu.to_dev(c["k"]), gu.to_dev(c["v"])
+    sm = _fused(d, k1, v1, c, 0.0, 0, 0)
+    hm = lambda a: np.ascontiguousarray(a.transpose(0, 2, 1, 3))            # [layers][H][slots][D]
+    k2, v2 = gu.to_dev(hm(c["k"]).reshape(layers * H, slots, 1, D)), gu.to_dev(hm(c["v"]).reshape(layers * H, slots, 1, D))
+    c2 = dict(c, k=hm(c["k"]).reshape(layers * H, slots, 1, D))
+    hd = _fused(d, k2, v2, c2, 0.0, 0, 0)
+    _compare(sm, hd, "head-major compaction")
+    back = lambda t: gu.to_host(t).reshape(layers, H, slots, D).transpose(0, 2, 1, 3)
+    assert np.array_equal(back(k2), gu.to_host(k1)) and np.array_equal(back(v2), gu.to_host(v1))
+    assert hd[1]["accept_len"].float().mean().item() > 1.0
