@@ -15,7 +15,8 @@ previous step's.  Prints ONE JSON line.
 
 The default workload is the 8-sequence batch (prefix lengths uniform in [1024, 8192], 16-node
 trees, 40 q heads / 8 KV heads, head_dim 128, bf16 KV, vocab 151936); the 128K-context sequence
-(same heads, 16-node tree) is measured after it the same way and reported under "also".
+(same heads, 16-node tree) is measured after it the same way and reported under "also"; both are
+measured again over head-major caches [Hkv][slots][D] and reported under "head_major".
 """
 from __future__ import annotations
 
@@ -47,6 +48,8 @@ def parse():
     p.add_argument("--also", default="c128k",
                    help="a second workload measured the same way and reported as a sub-record ('' for none)")
     p.add_argument("--trials", type=int, default=5, help="timed runs the K steps are split into (median)")
+    p.add_argument("--no-head-major", dest="head_major_too", action="store_false",
+                   help="skip the extra measurement of the same workloads over head-major caches")
     p.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0: enough to defeat the MALL)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -451,13 +454,22 @@ def main():
     rec = measure(args, args.workload, not args.no_cpu)
     # the 128K-context configuration (the other configuration the bandwidth target names) as a
     # sub-record of the same line, measured the same way
+    keep = ("value", "unit", "ms_per_step", "trials", "trial_ms_per_step", "accepted_tokens_per_s",
+            "accept_len_mean", "config", "kv_read_gbps", "kv_read_pct_of_peak", "read_ceiling_gbps",
+            "kv_read_pct_of_ceiling", "kv_sized_read_ms", "kernel_ms", "roofline", "cpu_baseline")
     if args.also and args.also != args.workload:
         torch.cuda.empty_cache()
         sub = measure(args, args.also, not args.no_cpu)
-        keep = ("value", "unit", "ms_per_step", "trials", "trial_ms_per_step", "accepted_tokens_per_s",
-                "accept_len_mean", "config", "kv_read_gbps", "kv_read_pct_of_peak", "read_ceiling_gbps",
-                "kv_read_pct_of_ceiling", "kv_sized_read_ms", "kernel_ms", "roofline", "cpu_baseline")
         rec["also"] = {args.also: {k: sub[k] for k in keep}}
+    # the same workloads over head-major caches [Hkv][slots][D] (ev_tree_attention_strided): the
+    # layout whose rows stream fastest; same values, same step, the oracle leg not repeated
+    if args.kv == "contiguous" and args.head_major_too:
+        hm_args = argparse.Namespace(**dict(vars(args), kv="headmajor"))
+        rec["head_major"] = {}
+        for wl in [args.workload] + ([args.also] if args.also and args.also != args.workload else []):
+            torch.cuda.empty_cache()
+            sub = measure(hm_args, wl, False)
+            rec["head_major"][wl] = {k: sub[k] for k in keep if k != "cpu_baseline"}
     print(json.dumps(rec), flush=True)
 
 
