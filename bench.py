@@ -1,16 +1,19 @@
 """Benchmark of the draft-tree verification step on one MI355X.
 
-One step = the whole hot path over one batch: tree-masked GQA attention (ev_tree_attention: the
-attention kernel and the split merge), then the per-node argmax, greedy acceptance and in-place KV
-compaction (ev_select_accept_compact: the selection pass and one acceptance-and-compaction
-launch); four launches on one stream.  --separate calls the four separate entry points instead.  Inputs are seeded synthetic
-data already resident in HBM; several identical input sets sit at different addresses and the
-steps rotate over them, so the 256 MB Infinity Cache cannot serve one step's reads from the
-previous step's.  Prints ONE JSON line.
+One step = the whole hot path over one batch: tree-masked GQA attention, the per-node argmax (or
+sampled draw), greedy acceptance and in-place KV compaction, as one ev_verify_step call: four
+launches on one stream (the attention kernel, the merge of split units, the selection pass,
+acceptance and compaction).  --two-call runs ev_tree_attention then ev_select_accept_compact (the
+same four launches; the paged and window layouts always run this form); --separate calls the four
+separate entry points.  The
+attention call's own time (ev_tree_attention, for the roofline) is measured on its own.  Inputs
+are seeded synthetic data already resident in HBM; several identical input sets sit at different
+addresses and the steps rotate over them, so the 256 MB Infinity Cache cannot serve one step's
+reads from the previous step's.  Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W] [--trials R] [--workload c8|c128k|c512|c1x4k|tiny]
                   [--also WORKLOAD|''] [--no-cpu] [--kv contiguous|paged|window] [--page-size P]
-                  [--window W] [--sample T] [--separate]
+                  [--window W] [--sample T] [--two-call | --separate]
   python bench.py --copy-calibration     (a plain device copy of known size, for counter scaling)
 
 The default workload is the 8-sequence batch (prefix lengths uniform in [1024, 8192], 16-node
@@ -61,7 +64,10 @@ def parse():
     p.add_argument("--page-size", type=int, default=16)
     p.add_argument("--window", type=int, default=4096)
     p.add_argument("--separate", action="store_true",
-                   help="run the per-node token, acceptance and compaction as three calls instead of the fused one")
+                   help="run the step as four calls (attention, token, acceptance, compaction)")
+    p.add_argument("--two-call", action="store_true",
+                   help="run the step as attention + the fused token/acceptance/compaction call (the paged and "
+                        "window layouts always do) instead of the whole-step call")
     p.add_argument("--sample", type=float, default=0.0,
                    help="temperature > 0: sampled verification (per-node draw instead of the argmax)")
     return p.parse_args()
@@ -210,6 +216,8 @@ def measure(args, workload: str, with_cpu: bool) -> dict:
     aws = ev.Workspace(ev.ev_tree_attention_workspace_size(B, maxn, Hq, Hkv, D), "cuda")
     gws = ev.Workspace(max(ev.ev_node_argmax_workspace_size(T, w.vocab), 256), "cuda")
     sws = ev.Workspace(max(ev.ev_select_workspace_size(T, w.vocab), 256), "cuda")
+    whole = not args.separate and not args.two_call and args.kv in ("contiguous", "headmajor")
+    vws = ev.Workspace(ev.ev_verify_step_workspace_size(B, T, maxn, Hq, Hkv, D, w.vocab), "cuda") if whole else None
     stream = torch.cuda.current_stream().cuda_stream
     lib = ev.load()
     p = lambda t: t.data_ptr()
@@ -249,6 +257,16 @@ def measure(args, workload: str, with_cpu: bool) -> dict:
                 fused = head + (w.total_slots * D * esz, m["kv_start"], m["prefix_len"], w.total_slots, 1, D)
             else:
                 fused = head + (w.total_slots * Hkv * D * esz, m["kv_start"], m["prefix_len"], w.total_slots, Hkv, D)
+            if whole:  # the whole step in one call: the attention's arguments with its strides, then the rest
+                strides = (D, w.total_slots * D) if hm else (Hkv * D, D)
+                comp = (Hkv, w.total_slots * D * esz, 1, D) if hm else (1, w.total_slots * Hkv * D * esz, Hkv, D)
+                one = (p(s["q"]), p(s["k"]), p(s["v"]), p(out[i]), p(lse), m["node_start"], m["parent"],
+                       m["kv_start"], m["prefix_len"], B, T, maxn, w.total_slots, Hq, Hkv, D) + strides + \
+                      (dt, w.sm_scale, p(s["logits"]), dt, w.vocab, w.vocab, args.sample, 0x5EED, i, m["draft"]) + \
+                      comp + (p(target), p(acc_len), p(acc_path), p(bonus), p(out_tok), p(new_len), vws.ptr,
+                              vws.nbytes, p(err), stream)
+                calls.append((attn, one))
+                continue
             calls.append((attn, fused + out_args))
             continue
         if args.sample > 0:  # noise offset = the input set's index
@@ -264,21 +282,27 @@ def measure(args, workload: str, with_cpu: bool) -> dict:
             cmp))
     f_attn = {"contiguous": lib.ev_tree_attention, "headmajor": lib.ev_tree_attention_strided,
               "paged": lib.ev_tree_attention_paged, "window": lib.ev_tree_attention_window}[args.kv]
+    # the step: (function, index of its argument tuple in a call entry) pairs; entry 0 always holds the
+    # attention call's arguments (the attention-only timing below uses it)
     if args.separate:
         f_arg = lib.ev_node_sample if args.sample > 0 else lib.ev_node_argmax
         f_acc = lib.ev_sampled_accept if args.sample > 0 else lib.ev_greedy_accept
         f_cmp = lib.ev_compact_kv_paged if args.kv == "paged" else lib.ev_compact_kv
-        fns = (f_attn, f_arg, f_acc, f_cmp)
+        plan = ((f_attn, 0), (f_arg, 1), (f_acc, 2), (f_cmp, 3))
         names = ("tree_attention", "node_sample" if args.sample > 0 else "node_argmax",
                  "sampled_accept" if args.sample > 0 else "greedy_accept", "compact_kv")
+    elif whole:
+        plan = ((lib.ev_verify_step, 1),)
+        names = ("verify_step",)
     else:
-        fns = (f_attn, lib.ev_select_accept_compact_paged if args.kv == "paged" else lib.ev_select_accept_compact)
+        plan = ((f_attn, 0),
+                (lib.ev_select_accept_compact_paged if args.kv == "paged" else lib.ev_select_accept_compact, 1))
         names = ("tree_attention", "select_accept_compact")
 
     def step(c):
         r = 0
-        for f, a in zip(fns, c):
-            r |= f(*a)
+        for f, j in plan:
+            r |= f(*c[j])
         return r
 
     for i in range(args.warmup):
@@ -316,13 +340,13 @@ def measure(args, workload: str, with_cpu: bool) -> dict:
     # between launches.  (An event marker costs stream time of its own, ~3 us here, so no run has
     # one between calls.)
     for i in range(min(K, 3)):
-        rc |= fns[0](*calls[i % nsets][0])
+        rc |= f_attn(*calls[i % nsets][0])
     torch.cuda.synchronize()
     aevs = [torch.cuda.Event(enable_timing=True) for _ in range(trials + 1)]
     for j in range(trials):
         aevs[j].record()
         for i in range(bounds[j], bounds[j + 1]):
-            rc |= fns[0](*calls[i % nsets][0])
+            rc |= f_attn(*calls[i % nsets][0])
     aevs[trials].record()
     torch.cuda.synchronize()
     if rc:
@@ -331,13 +355,13 @@ def measure(args, workload: str, with_cpu: bool) -> dict:
     attn_ms = _median(attn_trials)
 
     # per-call breakdown (separate pass, an event pair around every call; not part of the timed region)
-    nf = len(fns)
+    nf = len(plan)
     kev = [[torch.cuda.Event(enable_timing=True) for _ in range(nf + 1)] for _ in range(K)]
     for i in range(K):
         c = calls[i % nsets]
-        for j in range(nf):
+        for j, (f, a) in enumerate(plan):
             kev[i][j].record()
-            fns[j](*c[j])
+            f(*c[a])
         kev[i][nf].record()
     torch.cuda.synchronize()
     kernel_ms = {n: _median([kev[i][j].elapsed_time(kev[i][j + 1]) for i in range(K)]) for j, n in enumerate(names)}
@@ -407,7 +431,8 @@ def measure(args, workload: str, with_cpu: bool) -> dict:
         "config": dict(synth.describe(w), input_sets=nsets, kv_bytes=kv_bytes,
                        kv_layout={"contiguous": "contiguous [slots][Hkv][D]", "headmajor": "head-major [Hkv][slots][D]",
                                   "paged": f"paged{args.page_size}", "window": f"window{args.window}"}[args.kv],
-                       verification=f"sampled T={args.sample}" if args.sample > 0 else "greedy T=0"),
+                       verification=f"sampled T={args.sample}" if args.sample > 0 else "greedy T=0",
+                       step_calls=" + ".join(names)),
         "trials": trials,
         "trial_ms_per_step": [round(x, 5) for x in trial_ms],
         "accepted_tokens_per_s": round(acc_sum / (ms_step / 1e3), 1),

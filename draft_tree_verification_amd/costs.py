@@ -197,9 +197,11 @@ def measure(batch: int, nodes: int, prefix: int, *, hq: int = 40, hkv: int = 8, 
     def attention(i):
         x = data[i]
         st = state[i]
-        ev.tree_attention(x["q"], x["k"], x["v"], meta["node_start"], meta["parent"], meta["kv_start"],
-                          meta["prefix_len"], max_nodes=nodes, sm_scale=scale, out=st.get("out"), lse=st.get("lse"),
-                          workspace=st.get("attn_ws"))
+        # (the workspace is kept: a new one per call would add its zero-fill to the timed work)
+        _, _, st["attn_ws"] = ev.tree_attention(x["q"], x["k"], x["v"], meta["node_start"], meta["parent"],
+                                                meta["kv_start"], meta["prefix_len"], max_nodes=nodes,
+                                                sm_scale=scale, out=st.get("out"), lse=st.get("lse"),
+                                                workspace=st.get("attn_ws"))
 
     step_us = _time(step, sets, iters, warmup, trials)
     attn_us = _time(attention, sets, iters, warmup, trials)

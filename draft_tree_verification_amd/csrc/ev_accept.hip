@@ -400,7 +400,8 @@ ev_status select_accept_compact(const void *logits, ev_dtype dtype, int64_t row_
                                 int32_t page_size, const int32_t *prefix_len, int64_t total_slots,
                                 int32_t num_kv_heads, int32_t head_dim, int32_t *target_token, int32_t *accept_len,
                                 int32_t *accept_path, int32_t *bonus_token, int32_t *out_tokens, int32_t *new_len,
-                                void *workspace, size_t workspace_bytes, int32_t *err_flag, hipStream_t stream) {
+                                void *workspace, size_t workspace_bytes, int32_t *err_flag, hipStream_t stream,
+                                bool validate_only = false) {
     if (!logits || !node_start || !parent || !draft_token || !target_token || !accept_len || !accept_path ||
         !bonus_token || !out_tokens)
         return EV_ERR_NULL;
@@ -421,6 +422,7 @@ ev_status select_accept_compact(const void *logits, ev_dtype dtype, int64_t row_
                                 bt_stride, page_size, prefix_len, nullptr, nullptr, batch, max_nodes, total_slots,
                                 num_kv_heads, head_dim, new_len, err_flag, true, cargs);
     if (st != EV_OK) return st;
+    if (validate_only) return EV_OK;
     const ev_status dev = ev::check_device();
     if (dev != EV_OK) return dev;
     if (batch == 0) return EV_OK;
@@ -498,4 +500,59 @@ extern "C" ev_status ev_select_accept_compact_paged(
                                  static_cast<int64_t>(num_pages) * page_size, num_kv_heads, head_dim, target_token,
                                  accept_len, accept_path, bonus_token, out_tokens, new_len, workspace,
                                  workspace_bytes, err_flag, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// The whole verification step as one call: the attention (and the merge of split units), the
+// selection pass, then acceptance and compaction, in that order on the caller's stream, after
+// every argument of all of them has been checked.  Workspace: the selection pieces (a multiple
+// of 256 bytes), then the attention workspace.
+extern "C" size_t ev_verify_step_workspace_size(int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t vocab) {
+    if (total_nodes < 0 || vocab < 1) return 0;
+    const size_t attn = ev_tree_attention_workspace_size(batch, max_nodes, num_q_heads, num_kv_heads, head_dim);
+    if (!attn) return 0;
+    return select_bytes(total_nodes, vocab) + attn;
+}
+
+extern "C" ev_status ev_verify_step(
+    const void *q, void *k_cache, void *v_cache, void *out, float *lse, const int32_t *node_start,
+    const int32_t *parent, const int32_t *kv_start, const int32_t *prefix_len, int32_t batch, int32_t total_nodes,
+    int32_t max_nodes, int64_t total_slots, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int64_t kv_slot_stride, int64_t kv_head_stride, ev_dtype dtype, float sm_scale, const void *logits,
+    ev_dtype logits_dtype, int64_t row_stride, int32_t vocab, float temperature, uint64_t seed, uint64_t offset,
+    const int32_t *draft_token, int32_t num_layers, int64_t layer_stride_bytes, int32_t compact_kv_heads,
+    int32_t compact_head_dim, int32_t *target_token, int32_t *accept_len, int32_t *accept_path,
+    int32_t *bonus_token, int32_t *out_tokens, int32_t *new_len, void *workspace, size_t workspace_bytes,
+    int32_t *err_flag, hipStream_t stream) {
+    if (!workspace) return EV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return EV_ERR_ALIGN;
+    if (total_nodes < 0 || vocab < 1) return EV_ERR_SHAPE;
+    const size_t need = ev_verify_step_workspace_size(batch, total_nodes, max_nodes, num_q_heads, num_kv_heads,
+                                                      head_dim, vocab);
+    if (!need) return EV_ERR_SHAPE;
+    if (workspace_bytes < need) return EV_ERR_WORKSPACE;
+    const size_t sel = select_bytes(total_nodes, vocab);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    const int32_t elem_bytes = dtype == EV_F32 ? 4 : 2;
+    // the selection/acceptance/compaction arguments first (no device call), then the attention
+    // call, which checks its own before its first launch, then the rest
+    ev_status st = select_accept_compact(logits, logits_dtype, row_stride, vocab, temperature, seed, offset,
+                                         node_start, parent, draft_token, batch, total_nodes, max_nodes, k_cache,
+                                         v_cache, elem_bytes, num_layers, layer_stride_bytes, kv_start, nullptr, 0, 0,
+                                         prefix_len, total_slots, compact_kv_heads, compact_head_dim, target_token,
+                                         accept_len, accept_path, bonus_token, out_tokens, new_len, ws, sel, err_flag,
+                                         stream, true);
+    if (st != EV_OK) return st;
+    st = ev_tree_attention_strided(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
+                                   total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim,
+                                   kv_slot_stride, kv_head_stride, dtype, sm_scale, ws + sel, workspace_bytes - sel,
+                                   err_flag, stream);
+    if (st != EV_OK) return st;
+    return select_accept_compact(logits, logits_dtype, row_stride, vocab, temperature, seed, offset, node_start,
+                                 parent, draft_token, batch, total_nodes, max_nodes, k_cache, v_cache, elem_bytes,
+                                 num_layers, layer_stride_bytes, kv_start, nullptr, 0, 0, prefix_len, total_slots,
+                                 compact_kv_heads, compact_head_dim, target_token, accept_len, accept_path,
+                                 bonus_token, out_tokens, new_len, ws, sel, err_flag, stream);
 }

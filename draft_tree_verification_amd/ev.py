@@ -29,7 +29,8 @@ EXPORTS = ("ev_status_string", "ev_tree_attention_workspace_size", "ev_tree_atte
            "ev_node_argmax", "ev_node_sample", "ev_greedy_accept", "ev_sampled_accept", "ev_compact_kv",
            "ev_compact_kv_paged",
            "ev_select_workspace_size", "ev_select_accept_compact", "ev_select_accept_compact_paged",
-           "ev_stream_read", "ev_tree_attention_noalloc", "ev_tree_attention_strided")
+           "ev_stream_read", "ev_tree_attention_noalloc", "ev_tree_attention_strided",
+           "ev_verify_step_workspace_size", "ev_verify_step")
 
 _lib = None
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -105,6 +106,12 @@ def load(path: str = LIB_PATH):
                                               _I32, _I32, ctypes.c_int, _F, _P, _P]
     lib.ev_stream_read.restype = ctypes.c_int
     lib.ev_stream_read.argtypes = [_P, _SZ, _P, _P]
+    lib.ev_verify_step_workspace_size.restype = _SZ
+    lib.ev_verify_step_workspace_size.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32, _I32]
+    lib.ev_verify_step.restype = ctypes.c_int
+    lib.ev_verify_step.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32,
+                                   _I64, _I64, ctypes.c_int, _F, _P, ctypes.c_int, _I64, _I32, _F, _U64, _U64, _P,
+                                   _I32, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -240,6 +247,25 @@ def ev_select_accept_compact_paged(logits, dtype, row_stride, vocab, temperature
 
 def ev_stream_read(src, nbytes, sink, stream) -> int:
     return load().ev_stream_read(src, nbytes, sink, stream)
+
+
+def ev_verify_step_workspace_size(batch, total_nodes, max_nodes, num_q_heads, num_kv_heads, head_dim, vocab) -> int:
+    return int(load().ev_verify_step_workspace_size(batch, total_nodes, max_nodes, num_q_heads, num_kv_heads,
+                                                    head_dim, vocab))
+
+
+def ev_verify_step(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch, total_nodes,
+                   max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim, kv_slot_stride, kv_head_stride, dtype,
+                   sm_scale, logits, logits_dtype, row_stride, vocab, temperature, seed, offset, draft_token,
+                   num_layers, layer_stride_bytes, compact_kv_heads, compact_head_dim, target_token, accept_len,
+                   accept_path, bonus_token, out_tokens, new_len, workspace, workspace_bytes, err_flag,
+                   stream) -> int:
+    return load().ev_verify_step(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
+                                 total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim,
+                                 kv_slot_stride, kv_head_stride, dtype, sm_scale, logits, logits_dtype, row_stride,
+                                 vocab, temperature, seed, offset, draft_token, num_layers, layer_stride_bytes,
+                                 compact_kv_heads, compact_head_dim, target_token, accept_len, accept_path,
+                                 bonus_token, out_tokens, new_len, workspace, workspace_bytes, err_flag, stream)
 
 
 # ------------------------------------------------------------------------------ torch helpers
@@ -664,23 +690,68 @@ def select_accept_compact(logits, node_start, parent, draft_token, k_cache, v_ca
 
 def verify_step(q, k_cache, v_cache, logits, node_start, parent, kv_start, prefix_len, draft_token, *,
                 max_nodes: int, sm_scale: float, temperature: float = 0.0, seed: int = 0, offset: int = 0,
-                state: dict = None, stream=None):
-    """One whole verification step: attention, then the per-node token (argmax at temperature 0,
-    else the sampled draw keyed by (seed, offset)), acceptance and compaction fused
-    (ev_tree_attention + ev_select_accept_compact: four launches on one stream).
-    ``state`` carries reusable outputs and workspaces between calls."""
+                state: dict = None, stream=None, head_major: bool = False, vocab: int = None):
+    """One whole verification step (ev_verify_step: three launches): attention, the per-node token
+    (argmax at temperature 0, else the sampled draw keyed by (seed, offset)) taken by the
+    attention launch's workgroups once their attention work is done, then acceptance and
+    compaction.  Caches [slots, Hkv, D], or [Hkv, slots, D] with head_major.  ``state`` carries
+    reusable outputs and the workspace between calls; returns it, with out, lse, target, accept
+    (as greedy_accept's dict), new_len and err."""
     torch = _torch()
     state = {} if state is None else state
+    _need(q, "q", ndim=3)
+    _need(k_cache, "k_cache", q.dtype, 3)
+    _need(v_cache, "v_cache", q.dtype, 3)
+    _need(logits, "logits", ndim=2)
+    for name, t in (("node_start", node_start), ("parent", parent), ("kv_start", kv_start),
+                    ("prefix_len", prefix_len), ("draft_token", draft_token)):
+        _need(t, name, torch.int32, 1)
+    T, Hq, D = q.shape
+    if head_major:
+        Hkv, slots, Dk = k_cache.shape
+    else:
+        slots, Hkv, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q / k_cache / v_cache shapes disagree")
+    B = prefix_len.shape[0]
+    if node_start.shape[0] != B + 1 or kv_start.shape[0] != B or parent.shape[0] != T or draft_token.shape[0] != T:
+        raise ValueError("metadata lengths disagree with batch / total nodes")
+    R, stride = logits.shape
+    if R != T:
+        raise ValueError("logits rows disagree with total nodes")
+    vocab = stride if vocab is None else vocab
+    dev = q.device
     if "err" not in state:
-        state["err"] = torch.zeros(1, dtype=torch.int32, device=q.device)
-    out, lse, ws = tree_attention(q, k_cache, v_cache, node_start, parent, kv_start, prefix_len, max_nodes=max_nodes,
-                                  sm_scale=sm_scale, out=state.get("out"), lse=state.get("lse"),
-                                  workspace=state.get("attn_ws"), err_flag=state["err"], stream=stream)
-    state.update(out=out, lse=lse, attn_ws=ws)
-    tgt, acc, nl, sws = select_accept_compact(logits, node_start, parent, draft_token, k_cache, v_cache, kv_start,
-                                              prefix_len, max_nodes=max_nodes, temperature=temperature, seed=seed,
-                                              offset=offset, target=state.get("target"),
-                                              out=state.get("accept"), new_len=state.get("new_len"),
-                                              workspace=state.get("select_ws"), err_flag=state["err"], stream=stream)
-    state.update(target=tgt, accept=acc, new_len=nl, select_ws=sws)
+        state["err"] = torch.zeros(1, dtype=torch.int32, device=dev)
+    if state.get("out") is None or tuple(state["out"].shape) != tuple(q.shape) or state["out"].dtype != q.dtype:
+        state["out"] = torch.empty_like(q)
+    if state.get("lse") is None or tuple(state["lse"].shape) != (T, Hq):
+        state["lse"] = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    if state.get("target") is None or state["target"].shape[0] != T:
+        state["target"] = torch.empty(T, dtype=torch.int32, device=dev)
+    state["accept"] = _accept_outputs(B, max_nodes, dev, state.get("accept"))
+    if state.get("new_len") is None or state["new_len"].shape[0] != B:
+        state["new_len"] = torch.empty(B, dtype=torch.int32, device=dev)
+    need = ev_verify_step_workspace_size(B, T, max_nodes, Hq, Hkv, D, vocab)
+    if not need:
+        raise EvError(2, "ev_verify_step_workspace_size")
+    ws = state.get("step_ws")
+    if ws is None or ws.nbytes < need:
+        ws = Workspace(need, dev)
+        state["step_ws"] = ws
+    esz = k_cache.element_size()
+    if head_major:  # [Hkv][slots][D]: compacted as Hkv one-head layers
+        strides, comp = (D, slots * D), (Hkv, slots * D * esz, 1, D)
+    else:
+        strides, comp = (Hkv * D, D), (1, slots * Hkv * D * esz, Hkv, D)
+    acc = state["accept"]
+    st = ev_verify_step(_addr(q), _addr(k_cache), _addr(v_cache), _addr(state["out"]), _addr(state["lse"]),
+                        _addr(node_start), _addr(parent), _addr(kv_start), _addr(prefix_len), B, T, max_nodes, slots,
+                        Hq, Hkv, D, *strides, _dtype_code(q), float(sm_scale), _addr(logits), _dtype_code(logits),
+                        stride, vocab, float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                        int(offset) & 0xFFFFFFFFFFFFFFFF, _addr(draft_token), *comp, _addr(state["target"]),
+                        _addr(acc["accept_len"]), _addr(acc["accept_path"]), _addr(acc["bonus"]),
+                        _addr(acc["out_tokens"]), _addr(state["new_len"]), ws.ptr, ws.nbytes, _addr(state["err"]),
+                        _stream(stream))
+    _check(st, "ev_verify_step")
     return state

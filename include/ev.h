@@ -426,6 +426,55 @@ ev_status ev_select_accept_compact_paged(const void *logits, ev_dtype dtype, int
                                          hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * ev_verify_step
+ *
+ * The whole verification step of one tree (kongchang.com English article, "Technical
+ * Background": one target pass scores every node, the accepted path is kept and its K/V moved):
+ * ev_tree_attention_strided, then ev_select_accept_compact, as one call: every argument of both
+ * is checked before the first launch, then the attention (with the merge of split units), the
+ * per-node selection pass and the acceptance/compaction launch run in that order on `stream`.
+ * The GPU work is exactly that of the two calls; the call saves the second call's host work and
+ * gives a serving loop one entry point per step.  Every output is bit-identical to the two
+ * separate calls on the same inputs:
+ *
+ *   out, lse                                          as ev_tree_attention_strided
+ *   target_token, accept_len, accept_path, bonus_token, out_tokens, K/V caches, new_len
+ *                                                     as ev_select_accept_compact
+ *
+ *   q ... sm_scale   as ev_tree_attention_strided (the caches are read through kv_slot_stride /
+ *                    kv_head_stride, then compacted in place, so they are not const here)
+ *   logits ... draft_token   as ev_select_accept_compact (logits_dtype is its dtype)
+ *   num_layers, layer_stride_bytes, compact_kv_heads, compact_head_dim
+ *                    the compaction's view of the same caches, as ev_select_accept_compact's
+ *                    num_layers, layer_stride_bytes, num_kv_heads, head_dim (elem_bytes is the
+ *                    attention dtype's size): [slots][Hkv][D] caches are 1 layer of Hkv heads;
+ *                    head-major [Hkv][slots][D] caches are Hkv layers of 1 head, layer stride
+ *                    slots * D * elem_bytes
+ *   workspace        >= ev_verify_step_workspace_size(...) bytes, 256-byte aligned
+ *                    (EV_ERR_ALIGN), for this call only: the selection pieces
+ *                    (ev_select_workspace_size(total_nodes, vocab) bytes), then the attention
+ *                    workspace.
+ *                    No initial contents are needed; calls that share a workspace must not
+ *                    overlap.
+ * Every argument is checked before the first launch (nothing runs on an error).  Data errors
+ * are reported as by the separate calls.
+ * -------------------------------------------------------------------------------------------*/
+size_t ev_verify_step_workspace_size(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t vocab);
+
+ev_status ev_verify_step(const void *q, void *k_cache, void *v_cache, void *out, float *lse,
+                         const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,
+                         const int32_t *prefix_len, int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                         int64_t total_slots, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int64_t kv_slot_stride, int64_t kv_head_stride, ev_dtype dtype, float sm_scale,
+                         const void *logits, ev_dtype logits_dtype, int64_t row_stride, int32_t vocab,
+                         float temperature, uint64_t seed, uint64_t offset, const int32_t *draft_token,
+                         int32_t num_layers, int64_t layer_stride_bytes, int32_t compact_kv_heads,
+                         int32_t compact_head_dim, int32_t *target_token, int32_t *accept_len,
+                         int32_t *accept_path, int32_t *bonus_token, int32_t *out_tokens, int32_t *new_len,
+                         void *workspace, size_t workspace_bytes, int32_t *err_flag, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * ev_stream_read
  *
  * Measurement helper, not part of the verification step: reads every byte of a device buffer

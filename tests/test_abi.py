@@ -129,6 +129,41 @@ def test_fused_call_host_checks_need_no_gpu(lib):
                                              None) == 2      # page size 0
 
 
+def test_whole_step_host_checks_need_no_gpu(lib):
+    """ev_verify_step refuses bad arguments (attention's, then selection/acceptance/compaction's)
+    before any HIP call; its workspace is the selection pieces, then the attention's."""
+    P = 0x100000
+    attn = ev.ev_tree_attention_workspace_size(8, 16, 40, 8, 128)
+    assert ev.ev_verify_step_workspace_size(8, 128, 16, 40, 8, 128, 151936) == \
+        ev.ev_select_workspace_size(128, 151936) + attn
+    assert ev.ev_verify_step_workspace_size(8, 128, 65, 40, 8, 128, 151936) == 0    # too many nodes
+    assert ev.ev_verify_step_workspace_size(8, 128, 16, 40, 7, 128, 151936) == 0    # Hq % Hkv != 0
+    assert ev.ev_verify_step_workspace_size(8, 128, 16, 40, 8, 128, 0) == 0         # vocab
+    need = ev.ev_verify_step_workspace_size(2, 8, 8, 4, 2, 64, 1000)
+
+    def call(q=P, slot_stride=128, head_stride=64, dtype=0, scale=0.125, logits=P, stride=1024, T=0.0,
+             layers=1, layer_stride=64 * 128 * 2, ws=P, ws_bytes=None, max_nodes=8, head_dim=64):
+        return ev.ev_verify_step(q, P, P, P, P, P, P, P, P, 2, 8, max_nodes, 64, 4, 2, head_dim, slot_stride,
+                                 head_stride, dtype, scale, logits, 0, stride, 1000, T, 0, 0, P, layers,
+                                 layer_stride, 2, 64, P, P, P, P, P, P + 64, ws,
+                                 need if ws_bytes is None else ws_bytes, None, None)
+    assert call(ws=None) == 5
+    assert call(ws=P + 16) == 4                   # 256-byte alignment
+    assert call(ws_bytes=need - 1) == 5
+    assert call(max_nodes=65) == 2
+    assert call(q=None) == 1                      # attention's checks
+    assert call(head_dim=96) == 2
+    assert call(scale=float("nan")) == 2
+    assert call(dtype=7) == 3
+    assert call(slot_stride=0) == 2
+    assert call(q=P + 2) == 4
+    assert call(logits=None) == 1                 # then the selection's and acceptance's
+    assert call(stride=999) == 2
+    assert call(T=-1.0) == 2
+    assert call(logits=P + 2) == 4
+    assert call(layer_stride=100) == 2            # compaction's view of the caches
+
+
 def test_stream_read_host_checks_need_no_gpu(lib):
     P = 0x1000
     assert ev.ev_stream_read(None, 16, P, None) == 1
