@@ -40,7 +40,7 @@ struct ArgmaxArgs {
     int32_t *counters;         // [rows]
     unsigned long long *pieces;  // [rows][splits] each piece's winner (fused step), else NULL
     float c;                   // sampling: log2(e) / temperature
-    uint64_t seed, offset;     // sampling: Philox key
+    uint64_t seed, offset;     // sampling: Philox key (seed) and counter words 2-3 (offset)
 };
 
 // Order-preserving key of a bf16 value (16 bits, in a uint32): +-0 -> 0x8000, NaN -> 0xFFFF.
@@ -246,34 +246,39 @@ __global__ __launch_bounds__(kThreads) void node_argmax_kernel(const ArgmaxArgs 
 // greedy acceptance rule as the argmax: with drafted children taken as point proposals, a walk
 // that descends into the child holding the node's draw is speculative sampling along the tree
 // (the target's sampling distribution is kept; arex-research.com release note, opening section).
-// Uniforms: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) keyed by (seed, offset) on the
-// counter (v / 8, row, 0, 0); output k feeds elements 8j + 2k (low word) and 8j + 2k + 1 (high
-// word); word w -> u = ((w >> 9) + 1/2) * 2^-23.  One Philox block per thread per 16-byte load of
-// eight bf16 logits.  The scores are fp32: the logit times c fused with the noise subtraction.
-// Bound by the ALU (about 30 integer ops of Philox and two hardware log2 per element), not HBM.
-constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull, kPhiloxM1 = 0xCA5A826395121157ull;
-constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull, kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+// Uniforms: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) under the 64-bit key seed (low word
+// first) on the 128-bit counter (v / 4, row, low and high words of offset); output word k feeds
+// element 4j + k; word w -> u = ((w >> 9) + 1/2) * 2^-23.  Two Philox blocks per thread per
+// 16-byte load of eight bf16 logits.  The scores are fp32: the logit times c fused with the noise
+// subtraction.  Bound by the ALU (Philox's 32x32->64 products run on v_mad_u64_u32, five per
+// element, and two hardware log2 per element), not HBM.
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
 
-__device__ __forceinline__ void philox4x64_10(uint64_t (&x)[4], uint64_t k0, uint64_t k1) {
+__device__ __forceinline__ void philox4x32_10(uint32_t (&x)[4], uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
         if (r) {
             k0 += kPhiloxW0;
             k1 += kPhiloxW1;
         }
-        const uint64_t lo0 = kPhiloxM0 * x[0], hi0 = __umul64hi(kPhiloxM0, x[0]);
-        const uint64_t lo1 = kPhiloxM1 * x[2], hi1 = __umul64hi(kPhiloxM1, x[2]);
-        const uint64_t y0 = hi1 ^ x[1] ^ k0, y2 = hi0 ^ x[3] ^ k1;
+        const uint64_t p0 = static_cast<uint64_t>(kPhiloxM0) * x[0];  // one v_mad_u64_u32 each
+        const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * x[2];
+        // three-way XORs in one v_bitop3_b32 each (truth table 0x96)
+        const uint32_t y0 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p1 >> 32), x[1], k0, 0x96);
+        const uint32_t y2 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p0 >> 32), x[3], k1, 0x96);
         x[0] = y0;
-        x[1] = lo1;
+        x[1] = static_cast<uint32_t>(p1);
         x[2] = y2;
-        x[3] = lo0;
+        x[3] = static_cast<uint32_t>(p0);
     }
 }
 
-// Score of one element from its logit and its 32-bit random word.
+// Score of one element from its logit and its 32-bit random word.  The uniform is built from its
+// bits: 0x3F800000 | (w >> 9) is 1 + (w >> 9) * 2^-23, and subtracting 1 - 2^-24 is exact
+// (Sterbenz), giving ((w >> 9) + 1/2) * 2^-23 in two operations.
 __device__ __forceinline__ float sample_score(float z, uint32_t word, float c) {
-    const float u = (static_cast<float>(word >> 9) + 0.5f) * 0x1p-23f;  // exact: 24 significant bits
+    const float u = __builtin_bit_cast(float, __builtin_amdgcn_alignbit(0x7Fu, word, 9u)) - 0x1.fffffep-1f;
     const float e = -__builtin_amdgcn_logf(u);                          // -log2(u) > 0
     return __builtin_fmaf(z, c, -__builtin_amdgcn_logf(e));
 }
@@ -284,20 +289,46 @@ __global__ __launch_bounds__(kThreads) void node_sample_kernel(const ArgmaxArgs 
     const int v0 = split * a.seg;
     const int v1 = min(a.vocab, v0 + a.seg);
     const int tid = threadIdx.x;
-    uint32_t best = 0;
-    int32_t bidx = 0x7FFFFFFF;
     const float c = a.c;
-    auto take = [&](float z, uint32_t word, int idx) {
-        const uint32_t k = key_f32(__builtin_bit_cast(uint32_t, sample_score(z, word, c)));
-        if (k > best) { best = k; bidx = idx; }
+    // The thread's best score and its index.  Scores are compared as floats: a score is NaN only
+    // where its logit is NaN (u lies strictly inside (0, 1) and c is finite and positive), so a
+    // load whose eight logits hold no NaN takes the plain strict comparison (earliest index on
+    // ties, +0 == -0), and only a load holding a NaN takes the NaN-aware one (a NaN above every
+    // number, the first NaN kept).  Starting from -inf at the thread's first index covers a
+    // thread whose every score is -inf.
+    float bs = -__builtin_inff();
+    int32_t bidx = v0 + tid * kChunk < v1 ? v0 + tid * kChunk : 0x7FFFFFFF;
+    auto take_plain = [&](float z, uint32_t word, int idx) {
+        const float sc = sample_score(z, word, c);
+        if (sc > bs) { bs = sc; bidx = idx; }
     };
+    auto take_nan = [&](float z, uint32_t word, int idx) {
+        const float sc = sample_score(z, word, c);
+        if (sc > bs || (__builtin_isnan(sc) && !__builtin_isnan(bs))) { bs = sc; bidx = idx; }
+    };
+    auto take8 = [&](const float (&z)[8], const uint32_t (&w)[8], int at) {
+        // NaN if a logit is NaN (or if +inf and -inf meet: then the exact path runs needlessly)
+        const float zs = ((z[0] + z[1]) + (z[2] + z[3])) + ((z[4] + z[5]) + (z[6] + z[7]));
+        if (__builtin_isnan(zs)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) take_nan(z[e], w[e], at + e);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) take_plain(z[e], w[e], at + e);
+        }
+    };
+    // the eight words of elements 8j .. 8j + 7: Philox blocks 2j and 2j + 1
+    const uint32_t klo = static_cast<uint32_t>(a.seed), khi = static_cast<uint32_t>(a.seed >> 32);
+    const uint32_t olo = static_cast<uint32_t>(a.offset), ohi = static_cast<uint32_t>(a.offset >> 32);
     auto block = [&](int j, uint32_t (&w)[8]) {
-        uint64_t x[4] = {static_cast<uint64_t>(j), static_cast<uint64_t>(row), 0ull, 0ull};
-        philox4x64_10(x, a.seed, a.offset);
+        uint32_t x[4] = {static_cast<uint32_t>(2 * j), static_cast<uint32_t>(row), olo, ohi};
+        uint32_t y[4] = {static_cast<uint32_t>(2 * j + 1), static_cast<uint32_t>(row), olo, ohi};
+        philox4x32_10(x, klo, khi);
+        philox4x32_10(y, klo, khi);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            w[2 * k] = static_cast<uint32_t>(x[k]);
-            w[2 * k + 1] = static_cast<uint32_t>(x[k] >> 32);
+            w[k] = x[k];
+            w[4 + k] = y[k];
         }
     };
     const unsigned char *rp = static_cast<const unsigned char *>(a.logits) +
@@ -328,29 +359,32 @@ __global__ __launch_bounds__(kThreads) void node_sample_kernel(const ArgmaxArgs 
             const int at = base + h * kSegQuantum;
             uint32_t w[8];
             block(at >> 3, w);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) take(z[h][e], w[e], at + e);
+            take8(z[h], w, at);
         }
     }
     for (; base + kChunk <= v1; base += kSegQuantum) {
         uint32_t w[8];
         block(base >> 3, w);
+        float z[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float z = F32IN ? reinterpret_cast<const float *>(rp)[base + e]
-                                  : __builtin_bit_cast(float, static_cast<uint32_t>(reinterpret_cast<const uint16_t *>(rp)[base + e]) << 16);
-            take(z, w[e], base + e);
-        }
+        for (int e = 0; e < 8; ++e)
+            z[e] = F32IN ? reinterpret_cast<const float *>(rp)[base + e]
+                         : __builtin_bit_cast(float, static_cast<uint32_t>(reinterpret_cast<const uint16_t *>(rp)[base + e]) << 16);
+        take8(z, w, base);
     }
     if (base < v1) {  // ragged end of the row (fewer than eight elements): one block for all of them
         uint32_t w[8];
         block(base >> 3, w);
-        for (int e = base; e < v1; ++e) {
-            const float z = F32IN ? reinterpret_cast<const float *>(rp)[e]
-                                  : __builtin_bit_cast(float, static_cast<uint32_t>(reinterpret_cast<const uint16_t *>(rp)[e]) << 16);
-            take(z, w[e - base], e);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {  // (unrolled: the words stay in registers)
+            if (base + e < v1) {
+                const float z = F32IN ? reinterpret_cast<const float *>(rp)[base + e]
+                                      : __builtin_bit_cast(float, static_cast<uint32_t>(reinterpret_cast<const uint16_t *>(rp)[base + e]) << 16);
+                take_nan(z, w[e], base + e);
+            }
         }
     }
+    const uint32_t best = bidx == 0x7FFFFFFF ? 0u : key_f32(__builtin_bit_cast(uint32_t, bs));
     finish_row(a, row, best, bidx, F32IN);
 }
 

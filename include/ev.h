@@ -253,9 +253,10 @@ ev_status ev_node_argmax(const void *logits, ev_dtype dtype, int64_t row_stride,
  *     y = argmax_v  fma(z_v, c, -log2(-log2(u_v))),   c = log2(e) / T
  * (Gumbel-max in base 2), fp32 scores, largest score wins, lowest index on ties, a NaN logit
  * above every number.  u_v = ((w >> 9) + 1/2) * 2^-23 with w the 32-bit word of element v from
- * Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) under key (seed, offset) and counter
- * (v / 8, r, 0, 0): 64-bit output k gives elements 8j + 2k (low half) and 8j + 2k + 1 (high
- * half).  Use a fresh (seed, offset) per call (e.g. offset = decoding round) for fresh noise.
+ * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) under the 64-bit key seed (low word first)
+ * and the 128-bit counter (v / 4, r, low word of offset, high word of offset): output word k
+ * gives element 4j + k.  Use a fresh (seed, offset) per call (e.g. offset = decoding round) for
+ * fresh noise.
  * Fed to ev_sampled_accept as target_token, the draws make the accept step speculative
  * sampling along the tree with the drafted children as point proposals: a sequence descends
  * into the lowest-index child holding its node's draw and otherwise stops with the draw as

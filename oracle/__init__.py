@@ -76,8 +76,8 @@ def _bind(lib):
                                             _I32, _I64, _I32, _I32, _P, _P]
     lib.oracle_node_argmax.restype = None
     lib.oracle_node_argmax.argtypes = [_P, _I32, _I64, _I32, _I32, _P, _P]
-    lib.oracle_philox4x64_10.restype = None
-    lib.oracle_philox4x64_10.argtypes = [_P, _P, _P]
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_philox4x32_10.argtypes = [_P, _P, _P]
     lib.oracle_sample_uniform.restype = ctypes.c_float
     lib.oracle_sample_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64, _I64, _I64]
     lib.oracle_sample_score.restype = ctypes.c_float
@@ -208,13 +208,13 @@ def node_argmax(logits, vocab: int = None, row_stride: int = None, lib=None):
     return tgt[:R], mx[:R]
 
 
-def philox4x64_10(ctr, key, lib=None) -> np.ndarray:
-    """Philox4x64-10 of a 256-bit counter (4 words) under a 128-bit key (2 words)."""
+def philox4x32_10(ctr, key, lib=None) -> np.ndarray:
+    """Philox4x32-10 of a 128-bit counter (4 words) under a 64-bit key (2 words)."""
     lib = lib or load()
-    c = np.ascontiguousarray(ctr, dtype=np.uint64)
-    k = np.ascontiguousarray(key, dtype=np.uint64)
-    out = np.zeros(4, dtype=np.uint64)
-    lib.oracle_philox4x64_10(_ptr(c), _ptr(k), _ptr(out))
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib.oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
     return out
 
 

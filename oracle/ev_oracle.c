@@ -309,41 +309,41 @@ void oracle_node_argmax(const void *logits, int32_t dtype, int64_t row_stride, i
    The draw is the Gumbel-max rule in base 2: with u_v uniform in (0, 1),
        y = argmax_v  z_v * log2(e) / T  -  log2(-log2(u_v)),
    which equals argmax_v (z_v / T + g_v) / ln 2 + const with g_v = -ln(-ln u_v) standard Gumbel
-   noise, hence y ~ softmax(z / T).  The uniforms come from Philox4x64-10 (Salmon, Moraes, Dror
-   and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11): key (seed, offset), counter
-   (v / 8, row, 0, 0); of the four 64-bit outputs, output k gives elements 8j + 2k (low 32 bits)
-   and 8j + 2k + 1 (high 32 bits); a 32-bit word w maps to u = ((w >> 9) + 1/2) * 2^-23 (exact in
-   fp32, strictly inside (0, 1)).
+   noise, hence y ~ softmax(z / T).  The uniforms come from Philox4x32-10 (Salmon, Moraes, Dror
+   and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11: ten rounds of two 32x32->64
+   multiplications by 0xD2511F53 and 0xCD9E8D57, the key bumped by 0x9E3779B9 and 0xBB67AE85
+   between rounds): 64-bit key = seed (low word first), 128-bit counter = (v / 4, row, low word of
+   offset, high word of offset); output word k gives element 4j + k; a 32-bit word w maps to
+   u = ((w >> 9) + 1/2) * 2^-23 (exact in fp32, strictly inside (0, 1)).
    The decision is taken in fp32 as the library computes it: c = (float)(log2(e) / T) rounded
    from double, s_v = fmaf(z_v, c, -log2f(-log2f(u_v))); largest s wins, lowest index on ties, a
    NaN score (NaN logit) above every number. */
-static void philox_round(uint64_t x[4], const uint64_t k[2]) {
-    const unsigned __int128 p0 = (unsigned __int128)0xD2E7470EE14C6C93ull * x[0];
-    const unsigned __int128 p1 = (unsigned __int128)0xCA5A826395121157ull * x[2];
-    const uint64_t y0 = (uint64_t)(p1 >> 64) ^ x[1] ^ k[0];
-    const uint64_t y1 = (uint64_t)p1;
-    const uint64_t y2 = (uint64_t)(p0 >> 64) ^ x[3] ^ k[1];
-    const uint64_t y3 = (uint64_t)p0;
+static void philox_round(uint32_t x[4], const uint32_t k[2]) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * x[2];
+    const uint32_t y0 = (uint32_t)(p1 >> 32) ^ x[1] ^ k[0];
+    const uint32_t y1 = (uint32_t)p1;
+    const uint32_t y2 = (uint32_t)(p0 >> 32) ^ x[3] ^ k[1];
+    const uint32_t y3 = (uint32_t)p0;
     x[0] = y0; x[1] = y1; x[2] = y2; x[3] = y3;
 }
 
-void oracle_philox4x64_10(const uint64_t *ctr, const uint64_t *key, uint64_t *out) {
-    uint64_t x[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
-    uint64_t k[2] = {key[0], key[1]};
+void oracle_philox4x32_10(const uint32_t *ctr, const uint32_t *key, uint32_t *out) {
+    uint32_t x[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+    uint32_t k[2] = {key[0], key[1]};
     for (int r = 0; r < 10; ++r) {
-        if (r) { k[0] += 0x9E3779B97F4A7C15ull; k[1] += 0xBB67AE8584CAA73Bull; }
+        if (r) { k[0] += 0x9E3779B9u; k[1] += 0xBB67AE85u; }
         philox_round(x, k);
     }
     for (int i = 0; i < 4; ++i) out[i] = x[i];
 }
 
 float oracle_sample_uniform(uint64_t seed, uint64_t offset, int64_t row, int64_t v) {
-    const uint64_t ctr[4] = {(uint64_t)v / 8, (uint64_t)row, 0, 0};
-    const uint64_t key[2] = {seed, offset};
-    uint64_t out[4];
-    oracle_philox4x64_10(ctr, key, out);
-    const int w = (int)(v % 8);
-    const uint32_t word = (w & 1) ? (uint32_t)(out[w / 2] >> 32) : (uint32_t)out[w / 2];
+    const uint32_t ctr[4] = {(uint32_t)(v / 4), (uint32_t)row, (uint32_t)offset, (uint32_t)(offset >> 32)};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    const uint32_t word = out[v % 4];
     return ((float)(word >> 9) + 0.5f) * 0x1p-23f;
 }
 

@@ -384,19 +384,33 @@ ALL_PINS = ALL_PINS + (pin_window, pin_paged, pin_paged_compact)
 
 
 # ------------------------------------------------------------------ sampled verification (T > 0)
-_M64 = (1 << 64) - 1
+_GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
-def _numpy_philox(ctr, key):
-    """numpy's Philox4x64-10 (an independent implementation) for one counter: numpy advances its
-    256-bit counter before each block, so it starts one below."""
-    bg = np.random.Philox(key=np.array(key, dtype=np.uint64))
-    st = bg.state
-    cm1 = (sum(int(v) << (64 * i) for i, v in enumerate(ctr)) - 1) % (1 << 256)
-    st["state"]["counter"] = np.array([(cm1 >> (64 * i)) & _M64 for i in range(4)], dtype=np.uint64)
-    st["buffer_pos"] = 4
-    bg.state = st
-    return [int(x) for x in bg.random_raw(4)]
+def _philox_kat():
+    """(counter, key, output) triples of Philox4x32-10 from tests/golden/philox4x32_10_kat.txt."""
+    rows = []
+    with open(os.path.join(_GOLDEN, "philox4x32_10_kat.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            w = [int(x, 16) for x in line.split()]
+            rows.append((tuple(w[0:4]), tuple(w[4:6]), tuple(w[6:10])))
+    return rows
+
+
+def _philox4x32_py(ctr, key):
+    """Philox4x32-10 written from the SC'11 definition, for counters the vectors do not cover
+    (itself checked against the known-answer vectors before use)."""
+    M = 0xFFFFFFFF
+    x, k = list(ctr), list(key)
+    for r in range(10):
+        if r:
+            k = [(k[0] + 0x9E3779B9) & M, (k[1] + 0xBB67AE85) & M]
+        p0, p1 = 0xD2511F53 * x[0], 0xCD9E8D57 * x[2]
+        x = [(p1 >> 32) ^ x[1] ^ k[0], p1 & M, (p0 >> 32) ^ x[3] ^ k[1], p0 & M]
+    return x
 
 
 def _chi2_ok(counts, probs, what, alpha=1e-4):
@@ -417,19 +431,21 @@ def _softmax(z):
 
 
 def pin_sample(lib):
-    """Sampled draws.  The generator against numpy's Philox4x64-10; the per-element uniforms
-    against numpy's words under the documented layout; the law of the draw against softmax(z/T)
-    (chi-square, fp32 and bf16 rows, three temperatures); equal logits give uniform draws; a tiny
-    temperature gives the argmax; a NaN logit wins its row."""
-    for ctr, key in (((0, 0, 0, 0), (0, 0)), ((5, 7, 11, 13), (0x1234, 0xABCDEF)),
-                     ((_M64, _M64, _M64, _M64), (_M64, _M64)), ((_M64, 3, 0, 0), (9, 10))):
-        assert [int(x) for x in oracle.philox4x64_10(ctr, key, lib=lib)] == _numpy_philox(ctr, key), (ctr, key)
-    seed, offset = 0x0123456789ABCDEF, 42
-    for row, v in ((0, 0), (0, 1), (0, 7), (3, 8), (17, 151935), (5, 12345), (1 << 20, 6)):
-        words = _numpy_philox((v // 8, row, 0, 0), (seed, offset))
-        k = v % 8
-        w32 = (words[k // 2] >> 32) if k & 1 else (words[k // 2] & 0xFFFFFFFF)
-        assert oracle.sample_uniform(seed, offset, row, v, lib=lib) == ((w32 >> 9) + 0.5) * 2.0 ** -23, (row, v)
+    """Sampled draws.  The generator against the published Philox4x32-10 known-answer vectors; the
+    per-element uniforms against the generator's words under the documented layout; the law of
+    the draw against softmax(z/T) (chi-square, fp32 and bf16 rows, three temperatures); equal
+    logits give uniform draws; a tiny temperature gives the argmax; a NaN logit wins its row."""
+    kat = _philox_kat()
+    assert len(kat) == 3
+    for ctr, key, want in kat:
+        assert tuple(int(x) for x in oracle.philox4x32_10(ctr, key, lib=lib)) == want, (ctr, key)
+        assert tuple(_philox4x32_py(ctr, key)) == want, (ctr, key)
+    seed, offset = 0x0123456789ABCDEF, 0xFEDCBA9800000042
+    for row, v in ((0, 0), (0, 1), (0, 3), (0, 7), (3, 8), (17, 151935), (5, 12345), (1 << 20, 6)):
+        words = _philox4x32_py((v // 4, row, offset & 0xFFFFFFFF, offset >> 32),
+                               (seed & 0xFFFFFFFF, seed >> 32))
+        assert oracle.sample_uniform(seed, offset, row, v, lib=lib) == ((words[v % 4] >> 9) + 0.5) * 2.0 ** -23, \
+            (row, v)
     z = np.array([0.3, -1.2, 2.0, 0.0, 1.1, -0.4], np.float32)
     R = 30000
     for T, dtype in ((0.5, F32), (1.0, BF16), (2.5, F32)):

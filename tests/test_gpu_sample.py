@@ -79,6 +79,31 @@ def test_special_values():
     assert got[0] == 40 and got[1] == 10 and got[2] == 0
 
 
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_special_values_across_loads(dtype):
+    """Special logits in rows of several 16-byte loads per thread: the first NaN wins wherever it
+    sits; +inf logits win (the first of them); +inf and -inf in one load of eight; a row of -inf
+    with one finite logit; the ragged end of a row that is not a multiple of eight."""
+    gu.log(f"[case] sample special values across loads dtype={dtype}")
+    V = 4099  # (rows padded to 4104: a row's bytes must be a multiple of 16)
+    x = np.random.default_rng(8).normal(0, 1, (6, 4104)).astype(np.float32)
+    x[:, V:] = np.nan  # past the vocabulary: never read
+    x[0, 3000] = np.nan
+    x[0, 1000] = np.nan
+    x[1, 2000] = np.inf
+    x[1, 17] = np.inf
+    x[2, 9] = np.inf
+    x[2, 10] = -np.inf
+    x[3, :V] = -np.inf
+    x[3, 4097] = 0.0
+    x[4, 4098] = np.nan
+    x[5, 8:16] = np.array([np.inf, -np.inf, 0, 0, 0, 0, 0, 0], np.float32)
+    x[5, 2] = np.nan
+    raw = synth.f32_to_bf16_bits(x) if dtype == BF16 else x
+    got = _check_draws(raw, 1.0, seed=21, offset=4, vocab=V, what="special across loads")
+    assert got.tolist() == [1000, 17, 9, 4097, 4098, 2]
+
+
 def test_law_and_noise():
     """The GPU draws follow softmax(z/T) (chi-square), repeat for the same (seed, offset) and
     change with the offset."""

@@ -32,10 +32,12 @@ MUTANTS = {
         "                const size_t src = lo + (size_t)token_slot(NULL, block_table, bt_stride, page_size, b, L + path[t]) * row;\n"
         "                memcpy((char *)k_out + dst, (const char *)k_out + src, row);\n"
         "                memcpy((char *)v_out + dst, (const char *)v_out + src, row);"),
-    "philox_weyl_constant": ("k[0] += 0x9E3779B97F4A7C15ull;", "k[0] += 0x9E3779B97F4A7C17ull;"),
+    "philox_weyl_constant": ("k[0] += 0x9E3779B9u;", "k[0] += 0x9E3779BBu;"),
     "philox_nine_rounds": ("for (int r = 0; r < 10; ++r) {\n        if (r) {", "for (int r = 0; r < 9; ++r) {\n        if (r) {"),
-    "sample_word_halves_swapped": ("(w & 1) ? (uint32_t)(out[w / 2] >> 32) : (uint32_t)out[w / 2];",
-                                   "(w & 1) ? (uint32_t)out[w / 2] : (uint32_t)(out[w / 2] >> 32);"),
+    "philox_multiplier": ("(uint64_t)0xCD9E8D57u * x[2]", "(uint64_t)0xCD9E8D55u * x[2]"),
+    "sample_word_order_reversed": ("const uint32_t word = out[v % 4];", "const uint32_t word = out[3 - v % 4];"),
+    "sample_offset_words_swapped": ("(uint32_t)row, (uint32_t)offset, (uint32_t)(offset >> 32)}",
+                                    "(uint32_t)row, (uint32_t)(offset >> 32), (uint32_t)offset}"),
     "sample_noise_sign": ("fmaf(z, c, -log2f(-log2f(u)))", "fmaf(z, c, log2f(-log2f(u)))"),
     "sample_temperature_ignored": ("return (float)(1.4426950408889634 / (double)temperature);",
                                    "return 1.4426950408889634f;"),
