@@ -443,7 +443,8 @@ def measure(args, workload: str, with_cpu: bool) -> dict:
         "kv_read_pct_of_ceiling": round(100 * achieved / read_ceiling, 2),
         "kv_sized_read_ms": round(same_size_read_ms, 5),
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
-        "selection": "separate calls" if args.separate else "fused (ev_select_accept_compact)",
+        "selection": ("separate calls" if args.separate else "whole step (ev_verify_step)" if whole
+                      else "fused (ev_select_accept_compact)"),
         "wall_s_timed": round(t_wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
