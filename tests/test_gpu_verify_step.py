@@ -92,3 +92,47 @@ def test_repeated_calls_on_one_workspace():
             state = {"step_ws": state["step_ws"]}  # other shapes: keep only the workspace
         st, k, v = _whole(w, d, T, 3, i, False, state=state)
         _compare(sep, st, k, v, f"call {i} {name}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case,T,head_major", [("bf16 edges", 0.0, False), ("bf16 edges", 0.8, True),
+                                               ("fp32 d64", 0.0, False), ("fp32 d64", 1.3, True)])
+def test_whole_step_edge_shapes(case, T, head_major):
+    """Shapes the workloads do not reach: an empty prefix, single-node and 64-node trees, unused
+    slots between sequences, fp32 Q/K/V and logits at head_dim 64 with 4 q heads per KV head, a
+    vocabulary that is not a multiple of the load width.  The whole step equals the separate
+    calls bit for bit; at T = 0 its tokens, acceptance, new lengths and compacted caches equal
+    the oracle's, and its attention is within 2e-2 absolute + 1e-2 relative of the oracle's."""
+    from draft_tree_verification_amd import synth
+    from draft_tree_verification_amd.synth import F32
+    gu.log(f"[case] whole step edges {case} T={T} head_major={head_major}")
+    if case == "bf16 edges":
+        w = synth.make_workload("edges", 31, prefix_lens=[0, 5, 700, 64], nodes=[1, 64, 7, 16], vocab=4104,
+                                slot_gap=3)
+    else:
+        w = synth.make_workload("edges32", 32, prefix_lens=[256, 0, 33], nodes=[4, 9, 1], num_q_heads=8,
+                                num_kv_heads=2, head_dim=64, dtype=F32, vocab=1000)
+    d = _inputs(w, head_major)
+    sep = _separate(w, d, T, 19, 2, head_major)
+    st, k, v = _whole(w, d, T, 19, 2, head_major)
+    _compare(sep, st, k, v, case)
+    if T != 0.0:
+        return
+    ref_out, _, _ = oracle.tree_attention(w.q, w.k, w.v, w.node_start, w.parent, w.kv_start, w.prefix_len,
+                                          num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                                          head_dim=w.head_dim, sm_scale=w.sm_scale, total_slots=w.total_slots)
+    out = gu.widen(gu.to_host(st["out"]))
+    assert (np.abs(out - ref_out) <= 2e-2 + 1e-2 * np.abs(ref_out)).all(), f"{case}: attention vs oracle"
+    tgt, _ = oracle.node_argmax(w.logits)
+    assert np.array_equal(st["target"].cpu().numpy(), tgt)
+    acc = oracle.greedy_accept(w.node_start, w.parent, w.draft, tgt, w.max_nodes, w.vocab)
+    for key in ("accept_len", "accept_path", "bonus", "out_tokens"):
+        assert np.array_equal(st["accept"][key].cpu().numpy(), acc[key]), key
+    kx, vx, nl, _ = oracle.compact_kv(w.k[None], w.v[None], w.kv_start, w.prefix_len, acc["accept_len"],
+                                      acc["accept_path"], num_layers=1, total_slots=w.total_slots,
+                                      num_kv_heads=w.num_kv_heads, head_dim=w.head_dim)
+    assert np.array_equal(st["new_len"].cpu().numpy(), nl)
+    kh, vh = gu.to_host(k), gu.to_host(v)
+    if head_major:
+        kh, vh = kh.transpose(1, 0, 2), vh.transpose(1, 0, 2)
+    assert np.array_equal(kh, kx[0]) and np.array_equal(vh, vx[0]), f"{case}: compacted caches vs oracle"
