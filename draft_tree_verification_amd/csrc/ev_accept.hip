@@ -401,7 +401,7 @@ ev_status select_accept_compact(const void *logits, ev_dtype dtype, int64_t row_
                                 int32_t num_kv_heads, int32_t head_dim, int32_t *target_token, int32_t *accept_len,
                                 int32_t *accept_path, int32_t *bonus_token, int32_t *out_tokens, int32_t *new_len,
                                 void *workspace, size_t workspace_bytes, int32_t *err_flag, hipStream_t stream,
-                                bool validate_only = false) {
+                                bool validate_only = false, bool selection_launched = false) {
     if (!logits || !node_start || !parent || !draft_token || !target_token || !accept_len || !accept_path ||
         !bonus_token || !out_tokens)
         return EV_ERR_NULL;
@@ -433,7 +433,7 @@ ev_status select_accept_compact(const void *logits, ev_dtype dtype, int64_t row_
     sel.splits = total_nodes > 0 ? ev::select_splits(total_nodes, vocab) : 1;
     sel.target_out = target_token;
     sel.sampled = temperature > 0.f;
-    if (total_nodes > 0) {
+    if (total_nodes > 0 && !selection_launched) {
         st = ev::launch_select_pieces(logits, dtype, row_stride, total_nodes, vocab, temperature, seed, offset,
                                       static_cast<unsigned long long *>(workspace), stream);
         if (st != EV_OK) return st;
@@ -537,7 +537,9 @@ extern "C" ev_status ev_verify_step(
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     const int32_t elem_bytes = dtype == EV_F32 ? 4 : 2;
     // the selection/acceptance/compaction arguments first (no device call), then the attention
-    // call, which checks its own before its first launch, then the rest
+    // launcher checks its own before its first launch and runs the selection pass with it (beside
+    // the merge of split units when there is a merge at head_dim 128), then the acceptance and
+    // compaction launch
     ev_status st = select_accept_compact(logits, logits_dtype, row_stride, vocab, temperature, seed, offset,
                                          node_start, parent, draft_token, batch, total_nodes, max_nodes, k_cache,
                                          v_cache, elem_bytes, num_layers, layer_stride_bytes, kv_start, nullptr, 0, 0,
@@ -545,14 +547,37 @@ extern "C" ev_status ev_verify_step(
                                          accept_len, accept_path, bonus_token, out_tokens, new_len, ws, sel, err_flag,
                                          stream, true);
     if (st != EV_OK) return st;
-    st = ev_tree_attention_strided(q, k_cache, v_cache, out, lse, node_start, parent, kv_start, prefix_len, batch,
-                                   total_nodes, max_nodes, total_slots, num_q_heads, num_kv_heads, head_dim,
-                                   kv_slot_stride, kv_head_stride, dtype, sm_scale, ws + sel, workspace_bytes - sel,
-                                   err_flag, stream);
+    ev::AttentionCall attn{};
+    attn.q = q;
+    attn.k_cache = k_cache;
+    attn.v_cache = v_cache;
+    attn.out = out;
+    attn.lse = lse;
+    attn.node_start = node_start;
+    attn.parent = parent;
+    attn.kv_start = kv_start;
+    attn.prefix_len = prefix_len;
+    attn.batch = batch;
+    attn.total_nodes = total_nodes;
+    attn.max_nodes = max_nodes;
+    attn.total_slots = total_slots;
+    attn.num_q_heads = num_q_heads;
+    attn.num_kv_heads = num_kv_heads;
+    attn.head_dim = head_dim;
+    attn.slot_stride = kv_slot_stride;
+    attn.head_stride = kv_head_stride;
+    attn.dtype = dtype;
+    attn.sm_scale = sm_scale;
+    attn.workspace = ws + sel;
+    attn.workspace_bytes = workspace_bytes - sel;
+    attn.err_flag = err_flag;
+    const ev::SelectJob job{logits, logits_dtype, row_stride, total_nodes, vocab, temperature, seed, offset,
+                            reinterpret_cast<unsigned long long *>(ws)};
+    st = ev::launch_attention_step(attn, &job, stream);
     if (st != EV_OK) return st;
     return select_accept_compact(logits, logits_dtype, row_stride, vocab, temperature, seed, offset, node_start,
                                  parent, draft_token, batch, total_nodes, max_nodes, k_cache, v_cache, elem_bytes,
                                  num_layers, layer_stride_bytes, kv_start, nullptr, 0, 0, prefix_len, total_slots,
                                  compact_kv_heads, compact_head_dim, target_token, accept_len, accept_path,
-                                 bonus_token, out_tokens, new_len, ws, sel, err_flag, stream);
+                                 bonus_token, out_tokens, new_len, ws, sel, err_flag, stream, false, true);
 }

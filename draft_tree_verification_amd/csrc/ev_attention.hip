@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "ev_internal.h"
+#include "ev_select.h"
 
 namespace {
 
@@ -1583,8 +1584,20 @@ __device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int
     const int r = 16 * t + rr;                 // row within the unit (every slot has R rows)
     const int d0 = half * (D / 2) + 4 * c;
     const int slot_floats = R * D + 2 * R;
-    // one pass in batches of independent loads; the running maximum moves between batches
+    // The maximum over all the unit's pieces comes first: from the loads of the one round when a
+    // round holds every piece, else from a pass over the pieces' maxima.  The sums then run in
+    // piece order under that one scale, so the result has the same bits for any round size.
     float M = -INFINITY, l = 0.f;
+    if (npieces > BATCH) {
+        for (int i0 = 0; i0 < npieces; i0 += BATCH) {
+            float mi[BATCH];
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k)
+                mi[k] = slot_of_piece(a.part, w1, i0 + k < npieces ? i0 + k : i0, slot_floats)[R * D + r];
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) M = fmaxf(M, i0 + k < npieces ? mi[k] : -INFINITY);
+        }
+    }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int i0 = 0; i0 < npieces; i0 += BATCH) {
         const float *slot[BATCH];
@@ -1601,20 +1614,17 @@ __device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int
         // (an empty asm that takes every loaded value: no use of one moves above a later load)
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) asm volatile("" : "+v"(x[k]), "+v"(mi[k]), "+v"(li[k]));
-        float mb = M;
+        if (npieces <= BATCH) {
 #pragma unroll
-        for (int k = 0; k < BATCH; ++k) mb = fmaxf(mb, i0 + k < npieces ? mi[k] : -INFINITY);
-        const float mu = mb == -INFINITY ? 0.f : mb;
-        const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mu);
-        acc *= alpha;
-        l *= alpha;
+            for (int k = 0; k < BATCH; ++k) M = fmaxf(M, i0 + k < npieces ? mi[k] : -INFINITY);
+        }
+        const float mu = M == -INFINITY ? 0.f : M;
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
             const float f = i0 + k < npieces ? __builtin_amdgcn_exp2f(mi[k] - mu) : 0.f;
             acc += f * x[k];
             l += f * li[k];
         }
-        M = mb;
     }
     const int row = rg * R + r;
     if (row >= n * G) return;                  // rows past the unit's nodes
@@ -1630,8 +1640,10 @@ __device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int
     if (a.lse && half == 0 && c == 0) a.lse[orow] = (M + __log2f(l)) * kLn2;
 }
 
-template <int D, bool F32OUT>
-__global__ __launch_bounds__(2 * D, 2) void tree_attention_merge_kernel(const AttnArgs a, int R, int RT, int entries) {
+// The merge items of blocks mb, mb + nb, mb + 2 nb, ...  MAXB caps the pieces loaded in one
+// round (fewer registers; a unit of more pieces takes several rounds).
+template <int D, bool F32OUT, int MAXB>
+__device__ __forceinline__ void merge_blocks(const AttnArgs &a, int R, int RT, int entries, int mb, int nb) {
     constexpr int NT = 2 * D;
     __shared__ int s_idx[kMaxGrid];
     __shared__ int4 s_ent[kMaxGrid];
@@ -1659,16 +1671,44 @@ __global__ __launch_bounds__(2 * D, 2) void tree_attention_merge_kernel(const At
         __syncthreads();
     }
     const int items = base * RT * 2;
-    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    for (int it = mb; it < items; it += nb) {
         const int u = it / (RT * 2), t = (it / 2) % RT, half = it % 2;
         const int w1 = s_idx[u];
         const int4 e = s_ent[u];
         if (e.x <= 2) merge_item<D, 2, F32OUT>(a, R, w1, e, t, half);
-        else if (e.x <= 4) merge_item<D, 4, F32OUT>(a, R, w1, e, t, half);
-        else if (e.x <= 8) merge_item<D, 8, F32OUT>(a, R, w1, e, t, half);
-        else if (e.x <= 16) merge_item<D, 16, F32OUT>(a, R, w1, e, t, half);
+        else if (e.x <= 4 || MAXB <= 4) merge_item<D, 4, F32OUT>(a, R, w1, e, t, half);
+        else if (e.x <= 8 || MAXB <= 8) merge_item<D, 8, F32OUT>(a, R, w1, e, t, half);
+        else if (e.x <= 16 || MAXB <= 16) merge_item<D, 16, F32OUT>(a, R, w1, e, t, half);
         else merge_item<D, 32, F32OUT>(a, R, w1, e, t, half);
     }
+}
+
+template <int D, bool F32OUT>
+__global__ __launch_bounds__(2 * D, 2) void tree_attention_merge_kernel(const AttnArgs a, int R, int RT, int entries) {
+    merge_blocks<D, F32OUT, 32>(a, R, RT, entries, static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+}
+
+// The whole-step call's second launch at head_dim 128: the selection pass's row pieces (blocks
+// [0, sel_pieces), one piece each; sel_mode 1 argmax of bf16 logits, 2 of fp32 logits, 3 / 4 the
+// sampled draw) beside the merge of the split units (the kMergeBlocks blocks after them).  The
+// two read disjoint data and write disjoint outputs; one launch lets the selection stream while
+// the merge combines, instead of after it.  Merge rounds load at most 4 pieces (registers for a
+// full occupancy of the selection blocks).
+template <bool F32OUT>
+__global__ __launch_bounds__(256, 8) void tree_attention_merge_select_kernel(const AttnArgs a, const ev::sel::ArgmaxArgs s,
+                                                                          int sel_pieces, int sel_mode, int R, int RT,
+                                                                          int entries) {
+    const int b = static_cast<int>(blockIdx.x);
+    if (b < sel_pieces) {
+        switch (sel_mode) {
+            case 1: ev::sel::argmax_piece<false>(s, b); break;
+            case 2: ev::sel::argmax_piece<true>(s, b); break;
+            case 3: ev::sel::sample_piece<false>(s, b); break;
+            default: ev::sel::sample_piece<true>(s, b); break;
+        }
+        return;
+    }
+    merge_blocks<128, F32OUT, 4>(a, R, RT, entries, b - sel_pieces, kMergeBlocks);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1788,7 +1828,8 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
                            ev_dtype dtype, float sm_scale, int32_t window, const int32_t *block_table,
                            int32_t bt_stride, int32_t page_size, void *workspace, size_t workspace_bytes,
                            int32_t *err_flag, hipStream_t stream, bool use_scratch = false,
-                           int64_t slot_stride = 0, int64_t head_stride = -1) {
+                           int64_t slot_stride = 0, int64_t head_stride = -1, const ev::SelectJob *job = nullptr,
+                           bool validate_only = false) {
     const bool pg = page_size > 0;  // paged caches: total_slots = pool pages * page_size
     // K/V element strides: [slot][kv_head][dim] unless the caller gives its own
     if (slot_stride == 0 && head_stride == -1) {
@@ -1823,6 +1864,7 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
     const int64_t max_stages = static_cast<int64_t>(num_kv_heads) * plan.RG * (max_tokens / 32 + 2 * batch);
     if (max_stages >= (int64_t(1) << 31)) return EV_ERR_SHAPE;
     if (pg && static_cast<int64_t>(bt_stride) * page_size >= (int64_t(1) << 31)) return EV_ERR_SHAPE;
+    if (validate_only) return EV_OK;
     const ev_status dev = ev::check_device();
     if (dev != EV_OK) return dev;
     if (use_scratch) {  // this device's copy of the static scratch (no allocation)
@@ -1872,6 +1914,34 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
     args.part = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + plan.table_bytes);
     args.err_flag = err_flag;
     hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, args);
+    // whole-step calls: the selection pass shares the merge launch when there is one at head_dim
+    // 128, and is launched after the attention otherwise
+    const bool sel = job && job->rows > 0;
+    if (sel && grid > 1 && head_dim == 128) {
+        ev::sel::ArgmaxArgs sa{};
+        int32_t splits = 0, seg = 0;
+        ev::select_plan(job->rows, job->vocab, splits, seg);
+        sa.logits = job->logits;
+        sa.row_stride = job->row_stride;
+        sa.rows = job->rows;
+        sa.vocab = job->vocab;
+        sa.splits = splits;
+        sa.seg = seg;
+        sa.pieces = job->pieces;
+        const bool sampled = job->temperature > 0.f;
+        if (sampled) {
+            sa.c = static_cast<float>(1.4426950408889634 / static_cast<double>(job->temperature));
+            sa.seed = job->seed;
+            sa.offset = job->offset;
+        }
+        const int pieces = job->rows * splits;
+        const int mode = (sampled ? 3 : 1) + (job->dtype == EV_F32 ? 1 : 0);
+        const dim3 fgrid(static_cast<unsigned>(pieces + kMergeBlocks));
+        const int g32 = static_cast<int>(grid);
+        if (f32) hipLaunchKernelGGL((tree_attention_merge_select_kernel<true>), fgrid, dim3(256), 0, stream, args, sa, pieces, mode, plan.R, plan.RT, g32);
+        else hipLaunchKernelGGL((tree_attention_merge_select_kernel<false>), fgrid, dim3(256), 0, stream, args, sa, pieces, mode, plan.R, plan.RT, g32);
+        return ev::launch_status();
+    }
     if (grid > 1) {  // units split over workgroups: combine their pieces
         const dim3 mgrid(static_cast<unsigned>(kMergeBlocks));
         const int g32 = static_cast<int>(grid);
@@ -1883,9 +1953,23 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
             else hipLaunchKernelGGL((tree_attention_merge_kernel<128, false>), mgrid, dim3(256), 0, stream, args, plan.R, plan.RT, g32);
         }
     }
+    if (sel) {
+        const ev_status st = ev::launch_select_pieces(job->logits, job->dtype, job->row_stride, job->rows, job->vocab,
+                                                      job->temperature, job->seed, job->offset, job->pieces, stream);
+        if (st != EV_OK) return st;
+    }
     return ev::launch_status();
 }
 }  // namespace
+
+namespace ev {
+ev_status launch_attention_step(const AttentionCall &c, const SelectJob *job, hipStream_t stream, bool validate_only) {
+    return launch_attention(c.q, c.k_cache, c.v_cache, c.out, c.lse, c.node_start, c.parent, c.kv_start, c.prefix_len,
+                            c.batch, c.total_nodes, c.max_nodes, c.total_slots, c.num_q_heads, c.num_kv_heads,
+                            c.head_dim, c.dtype, c.sm_scale, 0, nullptr, 0, 0, c.workspace, c.workspace_bytes,
+                            c.err_flag, stream, false, c.slot_stride, c.head_stride, job, validate_only);
+}
+}  // namespace ev
 
 extern "C" ev_status ev_tree_attention(const void *q, const void *k_cache, const void *v_cache, void *out, float *lse,
                                        const int32_t *node_start, const int32_t *parent, const int32_t *kv_start,

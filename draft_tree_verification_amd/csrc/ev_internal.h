@@ -28,6 +28,40 @@ int select_splits(int32_t rows, int32_t vocab);
 ev_status launch_select_pieces(const void *logits, ev_dtype dtype, int64_t row_stride, int32_t rows, int32_t vocab,
                                float temperature, uint64_t seed, uint64_t offset, unsigned long long *pieces,
                                hipStream_t stream);
+void select_plan(int32_t rows, int32_t vocab, int32_t &splits, int32_t &seg);
+
+// The whole-step call (ev_verify_step): its attention arguments, as ev_tree_attention_strided
+// takes them, and its selection pass, which the attention launcher runs beside the merge of
+// split units when it can (one launch) and launches after the attention otherwise.
+struct AttentionCall {
+    const void *q, *k_cache, *v_cache;
+    void *out;
+    float *lse;
+    const int32_t *node_start, *parent, *kv_start, *prefix_len;
+    int32_t batch, total_nodes, max_nodes;
+    int64_t total_slots;
+    int32_t num_q_heads, num_kv_heads, head_dim;
+    int64_t slot_stride, head_stride;
+    ev_dtype dtype;
+    float sm_scale;
+    void *workspace;
+    size_t workspace_bytes;
+    int32_t *err_flag;
+};
+struct SelectJob {
+    const void *logits;
+    ev_dtype dtype;
+    int64_t row_stride;
+    int32_t rows, vocab;
+    float temperature;
+    uint64_t seed, offset;
+    unsigned long long *pieces;  // [rows * select_splits(rows, vocab)]
+};
+// Checks every attention argument before its first launch (nothing is launched on an error);
+// with validate_only, returns after the checks (no device call).  job: the selection pass to run
+// with it (arguments already checked), or NULL.
+ev_status launch_attention_step(const AttentionCall &c, const SelectJob *job, hipStream_t stream,
+                                bool validate_only = false);
 
 // ---------------------------------------------------------------- device side
 __device__ __forceinline__ u32x4_t ld16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
