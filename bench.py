@@ -1,11 +1,11 @@
 """Benchmark of the draft-tree verification step on one MI355X.
 
 One step = the whole hot path over one batch: tree-masked GQA attention, the per-node argmax (or
-sampled draw), greedy acceptance and in-place KV compaction, as one ev_verify_step call: four
-launches on one stream (the attention kernel, the merge of split units, the selection pass,
-acceptance and compaction).  --two-call runs ev_tree_attention then ev_select_accept_compact (the
-same four launches; the paged and window layouts always run this form); --separate calls the four
-separate entry points.  The
+sampled draw), greedy acceptance and in-place KV compaction, as one ev_verify_step call: three
+launches on one stream (the attention kernel; the merge of split units together with the
+selection pass; acceptance and compaction).  --two-call runs ev_tree_attention then
+ev_select_accept_compact (four launches; the paged and window layouts always run this form);
+--separate calls the four separate entry points.  The
 attention call's own time (ev_tree_attention, for the roofline) is measured on its own.  Inputs
 are seeded synthetic data already resident in HBM; several identical input sets sit at different
 addresses and the steps rotate over them, so the 256 MB Infinity Cache cannot serve one step's

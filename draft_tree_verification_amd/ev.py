@@ -691,9 +691,9 @@ def select_accept_compact(logits, node_start, parent, draft_token, k_cache, v_ca
 def verify_step(q, k_cache, v_cache, logits, node_start, parent, kv_start, prefix_len, draft_token, *,
                 max_nodes: int, sm_scale: float, temperature: float = 0.0, seed: int = 0, offset: int = 0,
                 state: dict = None, stream=None, head_major: bool = False, vocab: int = None):
-    """One whole verification step (ev_verify_step: four launches on one stream): attention and
-    its split merge, the per-node token (argmax at temperature 0, else the sampled draw keyed by
-    (seed, offset)), then acceptance and compaction.  Caches [slots, Hkv, D], or [Hkv, slots, D] with head_major.  ``state`` carries
+    """One whole verification step (ev_verify_step, one stream): attention, its split merge with
+    the per-node token pass in the same launch (argmax at temperature 0, else the sampled draw
+    keyed by (seed, offset)), then acceptance and compaction.  Caches [slots, Hkv, D], or [Hkv, slots, D] with head_major.  ``state`` carries
     reusable outputs and the workspace between calls; returns it, with out, lse, target, accept
     (as greedy_accept's dict), new_len and err."""
     torch = _torch()

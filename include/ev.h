@@ -432,11 +432,12 @@ ev_status ev_select_accept_compact_paged(const void *logits, ev_dtype dtype, int
  * The whole verification step of one tree (kongchang.com English article, "Technical
  * Background": one target pass scores every node, the accepted path is kept and its K/V moved):
  * ev_tree_attention_strided, then ev_select_accept_compact, as one call: every argument of both
- * is checked before the first launch, then the attention (with the merge of split units), the
- * per-node selection pass and the acceptance/compaction launch run in that order on `stream`.
- * The GPU work is exactly that of the two calls; the call saves the second call's host work and
- * gives a serving loop one entry point per step.  Every output is bit-identical to the two
- * separate calls on the same inputs:
+ * is checked before the first launch, then the attention, the merge of split units, the per-node
+ * selection pass and the acceptance/compaction launch run in that order on `stream`.  When the
+ * attention splits units over workgroups and head_dim is 128, the selection pass's row pieces run
+ * as workgroups of the merge launch (the two read and write disjoint data), which saves a launch
+ * and lets the logits stream while the merge combines: three launches instead of four.  Every
+ * output is bit-identical to the two separate calls on the same inputs:
  *
  *   out, lse                                          as ev_tree_attention_strided
  *   target_token, accept_len, accept_path, bonus_token, out_tokens, K/V caches, new_len
