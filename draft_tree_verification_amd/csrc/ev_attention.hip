@@ -1575,7 +1575,8 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel_ks(const At
 constexpr int kMergeBlocks = 512;
 
 template <int D, int BATCH, bool F32OUT>
-__device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int4 e, int t, int half) {
+__device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int4 e, int t, int half, bool given,
+                                           float Mg) {
     constexpr int CT = D / 8;                  // threads per row (float4 chunks per half row)
     const int rr = threadIdx.x / CT, c = threadIdx.x % CT;
     const int npieces = e.x, ns0 = e.y, n = e.z, ui = e.w;
@@ -1585,19 +1586,10 @@ __device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int
     const int d0 = half * (D / 2) + 4 * c;
     const int slot_floats = R * D + 2 * R;
     // The maximum over all the unit's pieces comes first: from the loads of the one round when a
-    // round holds every piece, else from a pass over the pieces' maxima.  The sums then run in
-    // piece order under that one scale, so the result has the same bits for any round size.
-    float M = -INFINITY, l = 0.f;
-    if (npieces > BATCH) {
-        for (int i0 = 0; i0 < npieces; i0 += BATCH) {
-            float mi[BATCH];
-#pragma unroll
-            for (int k = 0; k < BATCH; ++k)
-                mi[k] = slot_of_piece(a.part, w1, i0 + k < npieces ? i0 + k : i0, slot_floats)[R * D + r];
-#pragma unroll
-            for (int k = 0; k < BATCH; ++k) M = fmaxf(M, i0 + k < npieces ? mi[k] : -INFINITY);
-        }
-    }
+    // round holds every piece, else (given) from a pass over the pieces' maxima before the call.
+    // The sums then run in piece order under that one scale, so the result has the same bits for
+    // any round size.
+    float M = given ? Mg : -INFINITY, l = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int i0 = 0; i0 < npieces; i0 += BATCH) {
         const float *slot[BATCH];
@@ -1614,7 +1606,7 @@ __device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int
         // (an empty asm that takes every loaded value: no use of one moves above a later load)
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) asm volatile("" : "+v"(x[k]), "+v"(mi[k]), "+v"(li[k]));
-        if (npieces <= BATCH) {
+        if (!given) {
 #pragma unroll
             for (int k = 0; k < BATCH; ++k) M = fmaxf(M, i0 + k < npieces ? mi[k] : -INFINITY);
         }
@@ -1640,8 +1632,25 @@ __device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int
     if (a.lse && half == 0 && c == 0) a.lse[orow] = (M + __log2f(l)) * kLn2;
 }
 
-// The merge items of blocks mb, mb + nb, mb + 2 nb, ...  MAXB caps the pieces loaded in one
-// round (fewer registers; a unit of more pieces takes several rounds).
+// The maximum of row 16t + threadIdx.x / (D / 8) of a unit over all its pieces (for units of
+// more pieces than one round loads), eight independent loads at a time.
+template <int D>
+__device__ __forceinline__ float unit_row_max(const AttnArgs &a, int R, int w1, int npieces, int t) {
+    const int r = 16 * t + static_cast<int>(threadIdx.x) / (D / 8);
+    const int slot_floats = R * D + 2 * R;
+    float M = -INFINITY;
+    for (int i0 = 0; i0 < npieces; i0 += 8) {
+        float mi[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) mi[k] = slot_of_piece(a.part, w1, i0 + k < npieces ? i0 + k : i0, slot_floats)[R * D + r];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) M = fmaxf(M, i0 + k < npieces ? mi[k] : -INFINITY);
+    }
+    return M;
+}
+
+// The merge items of blocks mb, mb + nb, mb + 2 nb, ...  MAXB (4 or 32) caps the pieces loaded
+// in one round (fewer registers; a unit of more pieces takes several rounds).
 template <int D, bool F32OUT, int MAXB>
 __device__ __forceinline__ void merge_blocks(const AttnArgs &a, int R, int RT, int entries, int mb, int nb) {
     constexpr int NT = 2 * D;
@@ -1675,11 +1684,15 @@ __device__ __forceinline__ void merge_blocks(const AttnArgs &a, int R, int RT, i
         const int u = it / (RT * 2), t = (it / 2) % RT, half = it % 2;
         const int w1 = s_idx[u];
         const int4 e = s_ent[u];
-        if (e.x <= 2) merge_item<D, 2, F32OUT>(a, R, w1, e, t, half);
-        else if (e.x <= 4 || MAXB <= 4) merge_item<D, 4, F32OUT>(a, R, w1, e, t, half);
-        else if (e.x <= 8 || MAXB <= 8) merge_item<D, 8, F32OUT>(a, R, w1, e, t, half);
-        else if (e.x <= 16 || MAXB <= 16) merge_item<D, 16, F32OUT>(a, R, w1, e, t, half);
-        else merge_item<D, 32, F32OUT>(a, R, w1, e, t, half);
+        // round size: every piece in one round when MAXB allows, else MAXB pieces per round after
+        // a pass over the pieces' maxima
+        const bool given = e.x > MAXB;
+        const float Mg = given ? unit_row_max<D>(a, R, w1, e.x, t) : 0.f;
+        if (e.x <= 2) merge_item<D, 2, F32OUT>(a, R, w1, e, t, half, false, Mg);
+        else if (e.x <= 4 || MAXB == 4) merge_item<D, 4, F32OUT>(a, R, w1, e, t, half, given, Mg);
+        else if (e.x <= 8) merge_item<D, 8, F32OUT>(a, R, w1, e, t, half, false, Mg);
+        else if (e.x <= 16) merge_item<D, 16, F32OUT>(a, R, w1, e, t, half, false, Mg);
+        else merge_item<D, 32, F32OUT>(a, R, w1, e, t, half, given, Mg);
     }
 }
 
