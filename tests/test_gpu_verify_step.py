@@ -96,11 +96,16 @@ def test_repeated_calls_on_one_workspace():
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("case,T,head_major", [("bf16 edges", 0.0, False), ("bf16 edges", 0.8, True),
-                                               ("fp32 d64", 0.0, False), ("fp32 d64", 1.3, True)])
+                                               ("fp32 d64", 0.0, False), ("fp32 d64", 1.3, True),
+                                               ("fp32 d128", 0.0, False), ("fp32 d128", 0.9, True),
+                                               ("bf16 kv fp32 logits", 0.0, False),
+                                               ("bf16 kv fp32 logits", 0.9, False)])
 def test_whole_step_edge_shapes(case, T, head_major):
     """Shapes the workloads do not reach: an empty prefix, single-node and 64-node trees, unused
-    slots between sequences, fp32 Q/K/V and logits at head_dim 64 with 4 q heads per KV head, a
-    vocabulary that is not a multiple of the load width.  The whole step equals the separate
+    slots between sequences, fp32 Q/K/V and logits at head_dim 64 with 4 q heads per KV head and
+    at head_dim 128 (split units: the merge-plus-selection launch with fp32 outputs), bf16 K/V
+    with fp32 logits (that launch's fp32 argmax and draw), a vocabulary that is not a multiple of
+    the load width.  The whole step equals the separate
     calls bit for bit; at T = 0 its tokens, acceptance, new lengths and compacted caches equal
     the oracle's, and its attention is within 2e-2 absolute + 1e-2 relative of the oracle's."""
     from draft_tree_verification_amd import synth
@@ -109,9 +114,14 @@ def test_whole_step_edge_shapes(case, T, head_major):
     if case == "bf16 edges":
         w = synth.make_workload("edges", 31, prefix_lens=[0, 5, 700, 64], nodes=[1, 64, 7, 16], vocab=4104,
                                 slot_gap=3)
-    else:
+    elif case == "fp32 d64":
         w = synth.make_workload("edges32", 32, prefix_lens=[256, 0, 33], nodes=[4, 9, 1], num_q_heads=8,
                                 num_kv_heads=2, head_dim=64, dtype=F32, vocab=1000)
+    elif case == "fp32 d128":
+        w = synth.make_workload("edges32d128", 33, prefix_lens=[3000, 300], nodes=[16, 5], dtype=F32, vocab=2056)
+    else:
+        w = synth.make_workload("edgesmixed", 34, prefix_lens=[2500, 40, 1200], nodes=[16, 3, 9], vocab=6000)
+        w.logits = synth.bf16_bits_to_f32(w.logits).astype(np.float32)
     d = _inputs(w, head_major)
     sep = _separate(w, d, T, 19, 2, head_major)
     st, k, v = _whole(w, d, T, 19, 2, head_major)
