@@ -5,8 +5,9 @@ and verification cost, and sizes the tree (how many tokens, how many branches) f
 size from those measurements (aiposthub.com analysis, section "EAGLE-4 是什麼？先看推測解碼為什麼能變快";
 arex-research.com release note, section "投机树多大，由实测成本决定", whose packaged schedule narrows
 the verification width from 16 to 4 once the batch reaches 20).  This module measures the
-verification half with this library's kernels: one whole verify step (tree attention, then the
-fused per-node argmax, acceptance and KV compaction; four launches on one stream) for every (batch, tree
+verification half with this library's kernels: one whole verify step (ev_verify_step: tree
+attention, its split merge together with the per-node argmax, then acceptance and KV compaction, on
+one stream) for every (batch, tree
 nodes, prefix length) of a grid, on synthetic inputs already in HBM, captured in a HIP graph and
 timed with device events around its replays (device time, no host launch overhead).  Draft tokens
 are random, so nearly every sequence accepts only its root and compaction moves little.

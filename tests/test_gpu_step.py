@@ -1,4 +1,4 @@
-"""The whole verification step (four launches on one stream) against the oracle on every workload,
+"""The whole verification step (ev_verify_step, one stream) against the oracle on every workload,
 in the launch configuration the benchmark times; and the sampled step (temperature > 0)."""
 import numpy as np
 import pytest
