@@ -1633,18 +1633,18 @@ __device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int
 }
 
 // The maximum of row 16t + threadIdx.x / (D / 8) of a unit over all its pieces (for units of
-// more pieces than one round loads), eight independent loads at a time.
+// more pieces than one round loads), sixteen independent loads at a time.
 template <int D>
 __device__ __forceinline__ float unit_row_max(const AttnArgs &a, int R, int w1, int npieces, int t) {
     const int r = 16 * t + static_cast<int>(threadIdx.x) / (D / 8);
     const int slot_floats = R * D + 2 * R;
     float M = -INFINITY;
-    for (int i0 = 0; i0 < npieces; i0 += 8) {
-        float mi[8];
+    for (int i0 = 0; i0 < npieces; i0 += 16) {
+        float mi[16];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) mi[k] = slot_of_piece(a.part, w1, i0 + k < npieces ? i0 + k : i0, slot_floats)[R * D + r];
+        for (int k = 0; k < 16; ++k) mi[k] = slot_of_piece(a.part, w1, i0 + k < npieces ? i0 + k : i0, slot_floats)[R * D + r];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) M = fmaxf(M, i0 + k < npieces ? mi[k] : -INFINITY);
+        for (int k = 0; k < 16; ++k) M = fmaxf(M, i0 + k < npieces ? mi[k] : -INFINITY);
     }
     return M;
 }
