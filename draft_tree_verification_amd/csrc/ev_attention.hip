@@ -1701,27 +1701,28 @@ __global__ __launch_bounds__(2 * D, 2) void tree_attention_merge_kernel(const At
     merge_blocks<D, F32OUT, 32>(a, R, RT, entries, static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
 }
 
-// The whole-step call's second launch at head_dim 128: the selection pass's row pieces (blocks
-// [0, sel_pieces), one piece each; sel_mode 1 argmax of bf16 logits, 2 of fp32 logits, 3 / 4 the
-// sampled draw) beside the merge of the split units (the kMergeBlocks blocks after them).  The
-// two read disjoint data and write disjoint outputs; one launch lets the selection stream while
-// the merge combines, instead of after it.  Merge rounds load at most 4 pieces (registers for a
-// full occupancy of the selection blocks).
+// The whole-step call's second launch at head_dim 128: the merge of the split units (the first
+// kMergeBlocks blocks, dispatched first: some take two items in a row) beside the selection
+// pass's row pieces (the blocks after them, one piece each; sel_mode 1 argmax of bf16 logits, 2
+// of fp32 logits, 3 / 4 the sampled draw).  The two read disjoint data and write disjoint
+// outputs; one launch lets the selection stream while the merge combines, instead of after it.
+// Merge rounds load at most 4 pieces (registers for a full occupancy of the selection blocks).
 template <bool F32OUT>
 __global__ __launch_bounds__(256, 8) void tree_attention_merge_select_kernel(const AttnArgs a, const ev::sel::ArgmaxArgs s,
                                                                           int sel_pieces, int sel_mode, int R, int RT,
                                                                           int entries) {
     const int b = static_cast<int>(blockIdx.x);
-    if (b < sel_pieces) {
+    if (b >= kMergeBlocks) {
+        const int pc = b - kMergeBlocks;
         switch (sel_mode) {
-            case 1: ev::sel::argmax_piece<false>(s, b); break;
-            case 2: ev::sel::argmax_piece<true>(s, b); break;
-            case 3: ev::sel::sample_piece<false>(s, b); break;
-            default: ev::sel::sample_piece<true>(s, b); break;
+            case 1: ev::sel::argmax_piece<false>(s, pc); break;
+            case 2: ev::sel::argmax_piece<true>(s, pc); break;
+            case 3: ev::sel::sample_piece<false>(s, pc); break;
+            default: ev::sel::sample_piece<true>(s, pc); break;
         }
         return;
     }
-    merge_blocks<128, F32OUT, 4>(a, R, RT, entries, b - sel_pieces, kMergeBlocks);
+    merge_blocks<128, F32OUT, 4>(a, R, RT, entries, b, kMergeBlocks);
 }
 
 // ---------------------------------------------------------------------------------------------
