@@ -185,14 +185,16 @@ def _prototypes(text):
 
 
 def test_header_signatures_match_documented_block():
-    """include/ev.h declares exactly the prototypes that the design doc lists (its deviations from the
-    survey's boundary sketch are documented beside that block)."""
+    """include/ev.h declares exactly the prototypes of the design notes' signature block, the
+    boundary as documented (beside that block, with each difference from the boundary first
+    sketched and the reason for it)."""
     with open(os.path.join(ROOT, "include", "ev.h")) as f:
         header = _prototypes(f.read())
-    with open(os.path.join(ROOT, "DESIGN.md")) as f:
+    notes = os.path.join(ROOT, "DESIGN.md")
+    with open(notes) as f:
         design = f.read()
     m = re.search(r"\*\*Signatures\.\*\*.*?```c\n(.*?)```", design, flags=re.S)
-    assert m, "DESIGN.md has no signature block"
+    assert m, "the design notes have no signature block"
     documented = sorted(line.strip() for line in m.group(1).splitlines() if line.strip())
     assert header == documented
     assert len(header) == len(ev.EXPORTS)
