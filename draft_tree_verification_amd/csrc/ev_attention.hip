@@ -1573,6 +1573,11 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel_ks(const At
 // pieces: M = max_i m_i, O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i, in piece order
 // (deterministic), 16 rows x D/8 threads with one float4 of O each.
 constexpr int kMergeBlocks = 512;
+// Summation order of a unit's pieces in every merge: consecutive chunks of kMergeChunk pieces,
+// each summed in piece order from zero, and the chunk sums added in chunk order to a total that
+// starts at zero.  Units of at most kMergeChunk pieces are one chunk (a plain sum in piece order);
+// larger units may then be merged chunk-parallel (merge_item_split) with the same bits.
+constexpr int kMergeChunk = 8;
 
 template <int D, int BATCH, bool F32OUT>
 __device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int4 e, int t, int half, bool given,
@@ -1587,10 +1592,11 @@ __device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int
     const int slot_floats = R * D + 2 * R;
     // The maximum over all the unit's pieces comes first: from the loads of the one round when a
     // round holds every piece, else (given) from a pass over the pieces' maxima before the call.
-    // The sums then run in piece order under that one scale, so the result has the same bits for
-    // any round size.
-    float M = given ? Mg : -INFINITY, l = 0.f;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // The sums then run in the chunked piece order (kMergeChunk) under that one scale, so the
+    // result has the same bits for any round size.  (A chunk sum is never -0: it starts at +0.)
+    static_assert(BATCH < kMergeChunk ? kMergeChunk % BATCH == 0 : BATCH % kMergeChunk == 0, "chunk-aligned rounds");
+    float M = given ? Mg : -INFINITY, l = 0.f, lc = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, cacc = {0.f, 0.f, 0.f, 0.f};
     for (int i0 = 0; i0 < npieces; i0 += BATCH) {
         const float *slot[BATCH];
 #pragma unroll
@@ -1614,10 +1620,24 @@ __device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
             const float f = i0 + k < npieces ? __builtin_amdgcn_exp2f(mi[k] - mu) : 0.f;
-            acc += f * x[k];
-            l += f * li[k];
+            cacc += f * x[k];
+            lc += f * li[k];
+            if (BATCH >= kMergeChunk && k % kMergeChunk == kMergeChunk - 1) {
+                acc += cacc;
+                l += lc;
+                cacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                lc = 0.f;
+            }
+        }
+        if (BATCH < kMergeChunk && (i0 + BATCH) % kMergeChunk == 0) {
+            acc += cacc;
+            l += lc;
+            cacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            lc = 0.f;
         }
     }
+    acc += cacc;  // the last, partial chunk (adds +0 when there is none)
+    l += lc;
     const int row = rg * R + r;
     if (row >= n * G) return;                  // rows past the unit's nodes
     const int node = row / G, h = g * G + row % G;
@@ -1630,6 +1650,142 @@ __device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int
             u32x2_t{ev::pack_bf16x2(val[0], val[1]), ev::pack_bf16x2(val[2], val[3])};
     }
     if (a.lse && half == 0 && c == 0) a.lse[orow] = (M + __log2f(l)) * kLn2;
+}
+
+// One merge item of a unit of more than kMergeChunk pieces, chunk-parallel: rows 16t..16t+15 and
+// columns 16e..16e+15 of the unit's output, on a block of 256 threads.  Wave w sums chunks w,
+// w + 4, ... (thread: row lane / 4, four columns); the block adds the chunk sums in chunk order
+// through LDS, four chunks per round.  Same bits as merge_item (the same scale, the same chunk
+// sums, the same order of their addition), in one or two round trips for units of up to
+// 4 * kMergeChunk pieces instead of a pass over the maxima and a round per four pieces.
+template <bool F32OUT>
+__device__ __forceinline__ void merge_item_split(const AttnArgs &a, int R, int w1, int4 e, int t, int col) {
+    constexpr int D = 128;
+    constexpr int CH = kMergeChunk;
+    __shared__ f32x4_t s_acc[kWaves][64];
+    __shared__ float s_l[kWaves][16], s_m[kWaves][16];
+    const int tid = threadIdx.x, j = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: piece addresses in scalar registers
+    const int rr = j >> 2, c = j & 3;
+    const int npieces = e.x, ns0 = e.y, n = e.z, ui = e.w;
+    const int nch = (npieces + CH - 1) / CH;
+    const int r = 16 * t + rr;
+    const int d0 = 16 * col + 4 * c;
+    const int slot_floats = R * D + 2 * R;
+    auto piece = [&](int p) { return slot_of_piece(a.part, w1, p < npieces ? p : npieces - 1, slot_floats); };
+    // the maximum of row r over every piece (this wave's chunks, then the four waves' maxima)
+    auto exchange_max = [&](float mw) {
+        if (c == 0) s_m[wave][rr] = mw;
+        __syncthreads();
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][rr]);
+        return M;
+    };
+    // the chunk sums of one round (chunks c0 .. c0 + 3) in chunk order onto wave 0's total
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+    auto add_round = [&](int c0, bool mine, const f32x4_t &cacc, float lc) {
+        if (mine) {
+            s_acc[wave][j] = cacc;
+            if (c == 0) s_l[wave][rr] = lc;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const int nw = min(kWaves, nch - c0);
+            for (int w = 0; w < nw; ++w) {
+                acc += s_acc[w][j];
+                l += s_l[w][rr];
+            }
+        }
+        __syncthreads();
+    };
+    float M;
+    if (nch <= kWaves) {
+        // each wave holds at most one chunk: all its loads in one round trip
+        const bool mine = wave < nch;
+        f32x4_t x[CH];
+        float mi[CH], li[CH];
+        float mw = -INFINITY;
+        if (mine) {
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                const float *sl = piece(wave * CH + k);
+                x[k] = *reinterpret_cast<const f32x4_t *>(sl + r * D + d0);
+                mi[k] = sl[R * D + r];
+                li[k] = sl[R * D + R + r];
+            }
+#pragma unroll
+            for (int k = 0; k < CH; ++k) mw = fmaxf(mw, wave * CH + k < npieces ? mi[k] : -INFINITY);
+        }
+        M = exchange_max(mw);
+        const float mu = M == -INFINITY ? 0.f : M;
+        f32x4_t cacc = {0.f, 0.f, 0.f, 0.f};
+        float lc = 0.f;
+        if (mine) {
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                const float f = wave * CH + k < npieces ? __builtin_amdgcn_exp2f(mi[k] - mu) : 0.f;
+                cacc += f * x[k];
+                lc += f * li[k];
+            }
+        }
+        add_round(0, mine, cacc, lc);
+    } else {
+        float mw = -INFINITY;
+        for (int ch = wave; ch < nch; ch += kWaves) {
+            float m8[CH];
+#pragma unroll
+            for (int k = 0; k < CH; ++k) m8[k] = piece(ch * CH + k)[R * D + r];
+#pragma unroll
+            for (int k = 0; k < CH; ++k) mw = fmaxf(mw, ch * CH + k < npieces ? m8[k] : -INFINITY);
+        }
+        M = exchange_max(mw);
+        const float mu = M == -INFINITY ? 0.f : M;
+        for (int c0 = 0; c0 < nch; c0 += kWaves) {
+            const int ch = c0 + wave;
+            const bool mine = ch < nch;
+            f32x4_t cacc = {0.f, 0.f, 0.f, 0.f};
+            float lc = 0.f;
+            if (mine) {
+                // the chunk in two halves (fewer registers; the sum still runs in piece order)
+#pragma unroll
+                for (int h0 = 0; h0 < CH; h0 += CH / 2) {
+                    f32x4_t x[CH / 2];
+                    float mi[CH / 2], li[CH / 2];
+#pragma unroll
+                    for (int k = 0; k < CH / 2; ++k) {
+                        const float *sl = piece(ch * CH + h0 + k);
+                        x[k] = *reinterpret_cast<const f32x4_t *>(sl + r * D + d0);
+                        mi[k] = sl[R * D + r];
+                        li[k] = sl[R * D + R + r];
+                    }
+#pragma unroll
+                    for (int k = 0; k < CH / 2; ++k) {
+                        const float f = ch * CH + h0 + k < npieces ? __builtin_amdgcn_exp2f(mi[k] - mu) : 0.f;
+                        cacc += f * x[k];
+                        lc += f * li[k];
+                    }
+                }
+            }
+            add_round(c0, mine, cacc, lc);
+        }
+    }
+    if (wave != 0) return;
+    const int rg = ui / a.hkv, g = ui % a.hkv;
+    const int G = a.group;
+    const int row = rg * R + r;
+    if (row >= n * G) return;  // rows past the unit's nodes
+    const int node = row / G, h = g * G + row % G;
+    const size_t orow = static_cast<size_t>(ns0 + node) * a.hq + h;
+    const f32x4_t val = acc * (1.f / l);
+    if constexpr (F32OUT) {
+        *reinterpret_cast<f32x4_t *>(static_cast<float *>(a.out) + orow * D + d0) = val;
+    } else {
+        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(a.out) + orow * D + d0) =
+            u32x2_t{ev::pack_bf16x2(val[0], val[1]), ev::pack_bf16x2(val[2], val[3])};
+    }
+    if (a.lse && col == 0 && c == 0) a.lse[orow] = (M + __log2f(l)) * kLn2;
 }
 
 // The maximum of row 16t + threadIdx.x / (D / 8) of a unit over all its pieces (for units of
@@ -1650,20 +1806,27 @@ __device__ __forceinline__ float unit_row_max(const AttnArgs &a, int R, int w1, 
 }
 
 // The merge items of blocks mb, mb + nb, mb + 2 nb, ...  MAXB (4 or 32) caps the pieces loaded
-// in one round (fewer registers; a unit of more pieces takes several rounds).
-template <int D, bool F32OUT, int MAXB>
+// in one round (fewer registers; a unit of more pieces takes several rounds).  SPLIT (head_dim
+// 128, 256 threads): when some unit has more than kMergeChunk pieces, every unit is merged in
+// items of 16 rows x 16 columns by merge_item_split instead.
+template <int D, bool F32OUT, int MAXB, bool SPLIT>
 __device__ __forceinline__ void merge_blocks(const AttnArgs &a, int R, int RT, int entries, int mb, int nb) {
     constexpr int NT = 2 * D;
+    static_assert(!SPLIT || D == 128, "chunk-parallel items: head_dim 128, 256 threads");
     __shared__ int s_idx[kMaxGrid];
     __shared__ int4 s_ent[kMaxGrid];
     __shared__ int s_cnt[NT / 64 + 1];
+    __shared__ int s_maxk;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) s_maxk = 0;
+    __syncthreads();
     // compact the table's split units (same order in every block)
     int base = 0;
     for (int e0 = 0; e0 < entries; e0 += NT) {
         const int e = e0 + tid;
         const int4 v = e < entries ? a.table[e] : int4{0, 0, 0, 0};
         const bool act = v.x > 0;
+        if (SPLIT && act) atomicMax(&s_maxk, v.x);
         const uint64_t bal = __ballot(act);
         const int before = __popcll(bal & ((1ull << lane) - 1));
         if (lane == 0) s_cnt[wave] = __popcll(bal);
@@ -1678,6 +1841,18 @@ __device__ __forceinline__ void merge_blocks(const AttnArgs &a, int R, int RT, i
         for (int w = 0; w < NT / 64; ++w) tot += s_cnt[w];
         base += tot;
         __syncthreads();
+    }
+    if (SPLIT && s_maxk > kMergeChunk) {  // (read after the compaction's last barrier)
+        const int sitems = base * RT * (D / 16);
+        for (int it = mb; it < sitems; it += nb) {
+            const int u = it / (RT * (D / 16)), t = (it / (D / 16)) % RT, col = it % (D / 16);
+            // (the item's unit is uniform: its table entry goes to scalar registers)
+            const int4 eu = s_ent[u];
+            const int4 es = int4{__builtin_amdgcn_readfirstlane(eu.x), __builtin_amdgcn_readfirstlane(eu.y),
+                                 __builtin_amdgcn_readfirstlane(eu.z), __builtin_amdgcn_readfirstlane(eu.w)};
+            merge_item_split<F32OUT>(a, R, __builtin_amdgcn_readfirstlane(s_idx[u]), es, t, col);
+        }
+        return;
     }
     const int items = base * RT * 2;
     for (int it = mb; it < items; it += nb) {
@@ -1698,7 +1873,7 @@ __device__ __forceinline__ void merge_blocks(const AttnArgs &a, int R, int RT, i
 
 template <int D, bool F32OUT>
 __global__ __launch_bounds__(2 * D, 2) void tree_attention_merge_kernel(const AttnArgs a, int R, int RT, int entries) {
-    merge_blocks<D, F32OUT, 32>(a, R, RT, entries, static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+    merge_blocks<D, F32OUT, 32, D == 128>(a, R, RT, entries, static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
 }
 
 // The whole-step call's second launch at head_dim 128: the merge of the split units (the first
@@ -1722,7 +1897,7 @@ __global__ __launch_bounds__(256, 8) void tree_attention_merge_select_kernel(con
         }
         return;
     }
-    merge_blocks<128, F32OUT, 4>(a, R, RT, entries, b, kMergeBlocks);
+    merge_blocks<128, F32OUT, 4, true>(a, R, RT, entries, b, kMergeBlocks);
 }
 
 // ---------------------------------------------------------------------------------------------
