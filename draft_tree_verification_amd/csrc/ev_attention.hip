@@ -1652,9 +1652,10 @@ __device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int
     if (a.lse && half == 0 && c == 0) a.lse[orow] = (M + __log2f(l)) * kLn2;
 }
 
-// One merge item of a unit of more than kMergeChunk pieces, chunk-parallel: rows 16t..16t+15 and
-// columns 16e..16e+15 of the unit's output, on a block of 256 threads.  Wave w sums chunks w,
-// w + 4, ... (thread: row lane / 4, four columns); the block adds the chunk sums in chunk order
+// One merge item of a unit of more than kMergeChunk pieces, chunk-parallel: 8 rows and 32 columns
+// (one 128-byte line of every fp32 row) of the unit's output, on a block of 256 threads; item col
+// (0..7) of row tile t holds rows 16t + 8 (col / 4) .. + 7 and columns 32 (col % 4) .. + 31.  Wave
+// w sums chunks w, w + 4, ... (thread: row lane / 8, four columns); the block adds the chunk sums in chunk order
 // through LDS, four chunks per round.  Same bits as merge_item (the same scale, the same chunk
 // sums, the same order of their addition), in one or two round trips for units of up to
 // 4 * kMergeChunk pieces instead of a pass over the maxima and a round per four pieces.
@@ -1663,14 +1664,14 @@ __device__ __forceinline__ void merge_item_split(const AttnArgs &a, int R, int w
     constexpr int D = 128;
     constexpr int CH = kMergeChunk;
     __shared__ f32x4_t s_acc[kWaves][64];
-    __shared__ float s_l[kWaves][16], s_m[kWaves][16];
+    __shared__ float s_l[kWaves][8], s_m[kWaves][8];
     const int tid = threadIdx.x, j = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: piece addresses in scalar registers
-    const int rr = j >> 2, c = j & 3;
+    const int rr = j >> 3, c = j & 7;
     const int npieces = e.x, ns0 = e.y, n = e.z, ui = e.w;
     const int nch = (npieces + CH - 1) / CH;
-    const int r = 16 * t + rr;
-    const int d0 = 16 * col + 4 * c;
+    const int r = 16 * t + 8 * (col >> 2) + rr;
+    const int d0 = 32 * (col & 3) + 4 * c;
     const int slot_floats = R * D + 2 * R;
     auto piece = [&](int p) { return slot_of_piece(a.part, w1, p < npieces ? p : npieces - 1, slot_floats); };
     // the maximum of row r over every piece (this wave's chunks, then the four waves' maxima)
@@ -1785,7 +1786,7 @@ __device__ __forceinline__ void merge_item_split(const AttnArgs &a, int R, int w
         *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(a.out) + orow * D + d0) =
             u32x2_t{ev::pack_bf16x2(val[0], val[1]), ev::pack_bf16x2(val[2], val[3])};
     }
-    if (a.lse && col == 0 && c == 0) a.lse[orow] = (M + __log2f(l)) * kLn2;
+    if (a.lse && (col & 3) == 0 && c == 0) a.lse[orow] = (M + __log2f(l)) * kLn2;
 }
 
 // The maximum of row 16t + threadIdx.x / (D / 8) of a unit over all its pieces (for units of
@@ -1808,7 +1809,7 @@ __device__ __forceinline__ float unit_row_max(const AttnArgs &a, int R, int w1, 
 // The merge items of blocks mb, mb + nb, mb + 2 nb, ...  MAXB (4 or 32) caps the pieces loaded
 // in one round (fewer registers; a unit of more pieces takes several rounds).  SPLIT (head_dim
 // 128, 256 threads): when some unit has more than kMergeChunk pieces, every unit is merged in
-// items of 16 rows x 16 columns by merge_item_split instead.
+// items of 8 rows x 32 columns by merge_item_split instead.
 template <int D, bool F32OUT, int MAXB, bool SPLIT>
 __device__ __forceinline__ void merge_blocks(const AttnArgs &a, int R, int RT, int entries, int mb, int nb) {
     constexpr int NT = 2 * D;
