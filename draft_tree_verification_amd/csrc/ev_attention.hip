@@ -1872,9 +1872,11 @@ __device__ __forceinline__ void merge_blocks(const AttnArgs &a, int R, int RT, i
     }
 }
 
-template <int D, bool F32OUT>
+// SPLIT: the form with chunk-parallel items, launched for batches of few units (each then split
+// into many pieces); both forms give the same bits, the plain one is faster where no unit needs it.
+template <int D, bool F32OUT, bool SPLIT>
 __global__ __launch_bounds__(2 * D, 2) void tree_attention_merge_kernel(const AttnArgs a, int R, int RT, int entries) {
-    merge_blocks<D, F32OUT, 32, D == 128>(a, R, RT, entries, static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+    merge_blocks<D, F32OUT, 32, SPLIT>(a, R, RT, entries, static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
 }
 
 // The whole-step call's second launch at head_dim 128: the merge of the split units (the first
@@ -1883,7 +1885,7 @@ __global__ __launch_bounds__(2 * D, 2) void tree_attention_merge_kernel(const At
 // of fp32 logits, 3 / 4 the sampled draw).  The two read disjoint data and write disjoint
 // outputs; one launch lets the selection stream while the merge combines, instead of after it.
 // Merge rounds load at most 4 pieces (registers for a full occupancy of the selection blocks).
-template <bool F32OUT>
+template <bool F32OUT, bool SPLIT>
 __global__ __launch_bounds__(256, 8) void tree_attention_merge_select_kernel(const AttnArgs a, const ev::sel::ArgmaxArgs s,
                                                                           int sel_pieces, int sel_mode, int R, int RT,
                                                                           int entries) {
@@ -1898,7 +1900,7 @@ __global__ __launch_bounds__(256, 8) void tree_attention_merge_select_kernel(con
         }
         return;
     }
-    merge_blocks<128, F32OUT, 4, true>(a, R, RT, entries, b, kMergeBlocks);
+    merge_blocks<128, F32OUT, 4, SPLIT>(a, R, RT, entries, b, kMergeBlocks);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -2104,6 +2106,11 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
     args.part = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + plan.table_bytes);
     args.err_flag = err_flag;
     hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, args);
+    // Merge launches with chunk-parallel items (head_dim 128) when the batch has so few units that
+    // each is cut into many pieces: at most grid / kMergeChunk units.  (Both forms give the same
+    // bits; the choice only picks the faster code for the batch's shape.)
+    const bool split_items = head_dim == 128 &&
+                             static_cast<int64_t>(batch) * num_kv_heads * plan.RG * kMergeChunk <= grid;
     // whole-step calls: the selection pass shares the merge launch when there is one at head_dim
     // 128, and is launched after the attention otherwise
     const bool sel = job && job->rows > 0;
@@ -2128,19 +2135,27 @@ ev_status launch_attention(const void *q, const void *k_cache, const void *v_cac
         const int mode = (sampled ? 3 : 1) + (job->dtype == EV_F32 ? 1 : 0);
         const dim3 fgrid(static_cast<unsigned>(pieces + kMergeBlocks));
         const int g32 = static_cast<int>(grid);
-        if (f32) hipLaunchKernelGGL((tree_attention_merge_select_kernel<true>), fgrid, dim3(256), 0, stream, args, sa, pieces, mode, plan.R, plan.RT, g32);
-        else hipLaunchKernelGGL((tree_attention_merge_select_kernel<false>), fgrid, dim3(256), 0, stream, args, sa, pieces, mode, plan.R, plan.RT, g32);
+        if (split_items) {
+            if (f32) hipLaunchKernelGGL((tree_attention_merge_select_kernel<true, true>), fgrid, dim3(256), 0, stream, args, sa, pieces, mode, plan.R, plan.RT, g32);
+            else hipLaunchKernelGGL((tree_attention_merge_select_kernel<false, true>), fgrid, dim3(256), 0, stream, args, sa, pieces, mode, plan.R, plan.RT, g32);
+        } else {
+            if (f32) hipLaunchKernelGGL((tree_attention_merge_select_kernel<true, false>), fgrid, dim3(256), 0, stream, args, sa, pieces, mode, plan.R, plan.RT, g32);
+            else hipLaunchKernelGGL((tree_attention_merge_select_kernel<false, false>), fgrid, dim3(256), 0, stream, args, sa, pieces, mode, plan.R, plan.RT, g32);
+        }
         return ev::launch_status();
     }
     if (grid > 1) {  // units split over workgroups: combine their pieces
         const dim3 mgrid(static_cast<unsigned>(kMergeBlocks));
         const int g32 = static_cast<int>(grid);
         if (head_dim == 64) {
-            if (f32) hipLaunchKernelGGL((tree_attention_merge_kernel<64, true>), mgrid, dim3(128), 0, stream, args, plan.R, plan.RT, g32);
-            else hipLaunchKernelGGL((tree_attention_merge_kernel<64, false>), mgrid, dim3(128), 0, stream, args, plan.R, plan.RT, g32);
+            if (f32) hipLaunchKernelGGL((tree_attention_merge_kernel<64, true, false>), mgrid, dim3(128), 0, stream, args, plan.R, plan.RT, g32);
+            else hipLaunchKernelGGL((tree_attention_merge_kernel<64, false, false>), mgrid, dim3(128), 0, stream, args, plan.R, plan.RT, g32);
+        } else if (split_items) {
+            if (f32) hipLaunchKernelGGL((tree_attention_merge_kernel<128, true, true>), mgrid, dim3(256), 0, stream, args, plan.R, plan.RT, g32);
+            else hipLaunchKernelGGL((tree_attention_merge_kernel<128, false, true>), mgrid, dim3(256), 0, stream, args, plan.R, plan.RT, g32);
         } else {
-            if (f32) hipLaunchKernelGGL((tree_attention_merge_kernel<128, true>), mgrid, dim3(256), 0, stream, args, plan.R, plan.RT, g32);
-            else hipLaunchKernelGGL((tree_attention_merge_kernel<128, false>), mgrid, dim3(256), 0, stream, args, plan.R, plan.RT, g32);
+            if (f32) hipLaunchKernelGGL((tree_attention_merge_kernel<128, true, false>), mgrid, dim3(256), 0, stream, args, plan.R, plan.RT, g32);
+            else hipLaunchKernelGGL((tree_attention_merge_kernel<128, false, false>), mgrid, dim3(256), 0, stream, args, plan.R, plan.RT, g32);
         }
     }
     if (sel) {
