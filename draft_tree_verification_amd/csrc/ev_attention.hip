@@ -1570,8 +1570,8 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attention_kernel_ks(const At
 // A resident grid: every block compacts the table's split units (their entries, in LDS, so no
 // item re-reads the table), then the blocks stride
 // over the work items (unit, row tile, half of the d columns).  An item combines the unit's
-// pieces: M = max_i m_i, O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i, in piece order
-// (deterministic), 16 rows x D/8 threads with one float4 of O each.
+// pieces: M = max_i m_i, O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i, summed in the fixed
+// chunked piece order below (deterministic), 16 rows x D/8 threads with one float4 of O each.
 constexpr int kMergeBlocks = 512;
 // Summation order of a unit's pieces in every merge: consecutive chunks of kMergeChunk pieces,
 // each summed in piece order from zero, and the chunk sums added in chunk order to a total that
@@ -1655,8 +1655,8 @@ __device__ __forceinline__ void merge_item(const AttnArgs &a, int R, int w1, int
 // One merge item of a unit of more than kMergeChunk pieces, chunk-parallel: 8 rows and 32 columns
 // (one 128-byte line of every fp32 row) of the unit's output, on a block of 256 threads; item col
 // (0..7) of row tile t holds rows 16t + 8 (col / 4) .. + 7 and columns 32 (col % 4) .. + 31.  Wave
-// w sums chunks w, w + 4, ... (thread: row lane / 8, four columns); the block adds the chunk sums in chunk order
-// through LDS, four chunks per round.  Same bits as merge_item (the same scale, the same chunk
+// w sums chunks w, w + 4, ... (thread: row lane / 8, four columns); the block adds the chunk
+// sums in chunk order through LDS, four chunks per round.  Same bits as merge_item (the same scale, the same chunk
 // sums, the same order of their addition), in one or two round trips for units of up to
 // 4 * kMergeChunk pieces instead of a pass over the maxima and a round per four pieces.
 template <bool F32OUT>
@@ -1819,8 +1819,10 @@ __device__ __forceinline__ void merge_blocks(const AttnArgs &a, int R, int RT, i
     __shared__ int s_cnt[NT / 64 + 1];
     __shared__ int s_maxk;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) s_maxk = 0;
-    __syncthreads();
+    if constexpr (SPLIT) {
+        if (tid == 0) s_maxk = 0;
+        __syncthreads();
+    }
     // compact the table's split units (same order in every block)
     int base = 0;
     for (int e0 = 0; e0 < entries; e0 += NT) {
