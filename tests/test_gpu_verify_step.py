@@ -100,14 +100,16 @@ def test_repeated_calls_on_one_workspace():
                                                ("fp32 d128", 0.0, False), ("fp32 d128", 0.9, True),
                                                ("bf16 kv fp32 logits", 0.0, False),
                                                ("bf16 kv fp32 logits", 0.9, False),
-                                               ("65 pieces", 0.0, False), ("33 pieces", 0.7, True)])
+                                               ("65 pieces", 0.0, False), ("33 pieces", 0.7, True),
+                                               ("one long among short", 0.0, False)])
 def test_whole_step_edge_shapes(case, T, head_major):
     """Shapes the workloads do not reach: an empty prefix, single-node and 64-node trees, unused
     slots between sequences, fp32 Q/K/V and logits at head_dim 64 with 4 q heads per KV head and
     at head_dim 128 (split units: the merge-plus-selection launch with fp32 outputs), bf16 K/V
     with fp32 logits (that launch's fp32 argmax and draw), a vocabulary that is not a multiple of
     the load width, units split into 33 and 65 pieces (the chunk-parallel merge over several
-    rounds, a partial last chunk).  The whole step equals the separate
+    rounds, a partial last chunk), and one long sequence among short ones (the plain merge form
+    with units of 24 pieces: chunk sums inside rounds of 32 and across rounds of 4).  The whole step equals the separate
     calls bit for bit; at T = 0 its tokens, acceptance, new lengths and compacted caches equal
     the oracle's, and its attention is within 2e-2 absolute + 1e-2 relative of the oracle's."""
     from draft_tree_verification_amd import synth
@@ -126,6 +128,9 @@ def test_whole_step_edge_shapes(case, T, head_major):
                                 vocab=3000)
     elif case == "33 pieces":  # 4 units split 33 ways: 5 chunks, two rounds
         w = synth.make_workload("pieces33", 36, prefix_lens=[4096], nodes=[16], num_q_heads=20, num_kv_heads=4,
+                                vocab=3000)
+    elif case == "one long among short":  # 72 units (plain merge form), the long sequence's split 24 ways
+        w = synth.make_workload("longshort", 37, prefix_lens=[64] * 4 + [16384] + [64] * 4, nodes=[16] * 9,
                                 vocab=3000)
     else:
         w = synth.make_workload("edgesmixed", 34, prefix_lens=[2500, 40, 1200], nodes=[16, 3, 9], vocab=6000)
